@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse paged prefill hot path on one MI355X.
+
+One step = plan + attention (per-page partial O / LSE) + LSE combine over one
+synthetic layer.  Inputs (several rotated sets, so that repeated steps do not
+reuse cached Q/KV) are resident in HBM before timing starts.  Prints one JSON
+line with whole-step throughput, per-kernel times, the roofline of the
+dominant kernel (measured with HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload_stats(p):
+    """Algorithmic work of one layer, from the selections (host numpy).
+
+    visible[t, g, j]: keys of slot j of (token t, KV head g) the causal /
+    tail rules leave visible (0 = empty slot)."""
+    pos = p.q_pos.numpy().astype(np.int64)
+    seq = p.q_seq.numpy()
+    sl = p.seq_lens.numpy().astype(np.int64)
+    valid_row = pos >= 0
+    last = np.where(valid_row, np.minimum(pos, sl[np.clip(seq, 0, len(sl) - 1)] - 1), -1)
+    si = p.sel_idx.numpy().astype(np.int64)
+    sm = p.sel_mask.numpy()
+    start = si * p.unit_tokens
+    vis = np.clip(last[:, None, None] - start + 1, 0, p.unit_tokens)
+    vis = np.where((sm != 0) & (si >= 0), vis, 0)
+    G = p.Hq // p.Hkv
+    n_vis = int(vis.sum()) * G                      # (row, key) pairs
+    nonempty = int((vis > 0).sum()) * G              # (row, split) partials written
+    return dict(n_visible=n_vis, nonempty=nonempty,
+                flops=4.0 * p.d_qk * n_vis if p.d_qk == p.d_v else 2.0 * (p.d_qk + p.d_v) * n_vis)
+
+
+def tensor_bytes(t):
+    return t.numel() * t.element_size()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=3, help="rotated input sets")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle leg")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the method shards without exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_paged_table_amd import synth
+    from block_sparse_paged_table_amd.runner import DeviceProblem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = args.config
+    log(f"generating {args.sets} input sets of config {cfg} ({synth.CONFIG_NAMES[cfg]})")
+    probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i) for i in range(args.sets)]
+    p0 = probs[0]
+    st = workload_stats(p0)
+    # one partial buffer / output shared by all sets (the biggest allocations)
+    dps = [DeviceProblem(probs[0])]
+    for p in probs[1:]:
+        dps.append(DeviceProblem(p, partial_o=dps[0].partial_o, partial_lse=dps[0].partial_lse))
+    for dp in dps[1:]:
+        dp.out, dp.lse = dps[0].out, dps[0].lse
+    torch.cuda.synchronize()
+    log("inputs resident; warmup")
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        dps[i % len(dps)].run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        dp = dps[i % len(dps)]
+        e = ev[i]
+        e[0].record(stream)
+        dp.plan()
+        e[1].record(stream)
+        dp.attend()
+        e[2].record(stream)
+        dp.combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    ms_per_step = wall * 1e3 / K
+    log(f"plan {plan_ms:.3f} ms, attention {attn_ms:.3f} ms, combine {comb_ms:.3f} ms, "
+        f"step(events) {step_ms:.3f} ms, step(wall) {ms_per_step:.3f} ms")
+
+    # algorithmic bytes per launch
+    p, dp = p0, dps[0]
+    S, rows, dv = p.num_splits, p.num_rows, p.d_v
+    out_b = dp.out.element_size()
+    kv_bytes = sum(tensor_bytes(t) for t in (dp.k, dp.v) if t is not None)
+    kv_bytes += sum(tensor_bytes(t) for t in (dp.k_sf, dp.v_sf) if t is not None)
+    attn_bytes = 4 * dv * st["nonempty"] + 4 * st["nonempty"] + tensor_bytes(dp.q) + kv_bytes
+    comb_bytes = 4 * dv * st["nonempty"] + 4 * rows * S + out_b * rows * dv + 4 * rows
+    attn_tflops = st["flops"] / (attn_ms * 1e-3) / 1e12
+    attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+    comb_gbs = comb_bytes / (comb_ms * 1e-3) / 1e9
+    mfma_dtype = {"e4m3": "fp8", "bf16": "bf16", "f16": "f16", "f32": "f32"}[p.q_dtype]
+    dominant = "attention" if attn_ms >= comb_ms else "combine"
+    if dominant == "attention":
+        roof = dict(kernel="k1_page_attend", bound="hbm", achieved=round(attn_gbs, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4),
+                    traffic=None, alg_bytes=attn_bytes)
+    else:
+        roof = dict(kernel="combine_kernel", bound="hbm", achieved=round(comb_gbs, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(comb_gbs / HBM_PEAK_GBS, 4),
+                    traffic=None, alg_bytes=comb_bytes)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        n = min(args.cpu_sample, p.total_q)
+        toks = np.linspace(0, p.total_q - 1, n).astype(np.int32)
+        keep = oracle.make_keep(p)
+        sub = workload_stats_subset(p, toks)
+        log(f"CPU oracle on {n} tokens")
+        t = time.perf_counter()
+        oracle.prefill_rows(p, toks, want_partials=True, want_single_pass=False, keep=keep)
+        dt = time.perf_counter() - t
+        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        cpu = dict(value=round(sub / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                   sample=f"{n} of {p.total_q} query tokens (evenly spaced), all heads and slots; "
+                          f"{dt:.2f} s, FP64 C oracle, OpenMP")
+
+    res = {
+        "metric": "sparse-prefill attn TFLOP/s over selected tokens + combine HBM GB/s, 1 GPU",
+        "value": round(st["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": mfma_dtype, "data": "synthetic",
+        "config": {"workload": p.name, "description": p.description, "total_q": p.total_q,
+                   "Hq": p.Hq, "Hkv": p.Hkv, "head_dim": p.d_qk, "page_size": p.page_size,
+                   "slots": p.num_slots, "input_sets": len(dps)},
+        "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4),
+                       "combine": round(comb_ms, 4)},
+        "attention": {"tflops": round(attn_tflops, 2),
+                      "mfma_frac": round(attn_tflops / MFMA_PEAK_TFLOPS[mfma_dtype], 4),
+                      "hbm_gbs": round(attn_gbs, 1), "alg_bytes": attn_bytes,
+                      "flops": st["flops"], "visible_keys": st["n_visible"]},
+        "combine": {"gbs": round(comb_gbs, 1), "hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+                    "alg_bytes": comb_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def workload_stats_subset(p, toks):
+    import dataclasses
+    import torch
+    sub = dataclasses.replace(p, q=p.q[toks], q_seq=p.q_seq[toks], q_pos=p.q_pos[toks],
+                              sel_idx=p.sel_idx[toks], sel_mask=p.sel_mask[toks])
+    return workload_stats(sub)["flops"]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,292 @@
+// C ABI of libmsa: host-side validation, workspace sizing and kernel
+// launches.  Nothing here allocates device memory or waits on the device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+using namespace msa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+msa_status fail(msa_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+msa_status ok() {
+  g_err[0] = '\0';
+  return MSA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int esize(int dt) {
+  switch (dt) {
+    case MSA_F32: return 4;
+    case MSA_BF16: return 2;
+    case MSA_F16: return 2;
+    case MSA_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+constexpr int kPageRouteRowsPerUnit = 1024;  // (token, head) rows per work unit
+
+// Route of a descriptor (page selections), or -1.
+int page_route(const msa_prefill_desc *d) {
+  if (d->q_dtype == MSA_F32 && d->kv_dtype == MSA_F32) return kRouteF32;
+  if (d->q_dtype == MSA_BF16 && d->kv_dtype == MSA_BF16) return kRouteBF16;
+  if (d->q_dtype == MSA_F16 && d->kv_dtype == MSA_F16) return kRouteF16;
+  if (d->q_dtype == MSA_E4M3 && d->kv_dtype == MSA_NVFP4) return kRouteQ8KV4;
+  return -1;
+}
+
+// Host checks shared by every prefill entry point.  On success fills the
+// resolved arguments (without workspace pointers).
+msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
+  if (!d) return fail(MSA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size != sizeof(msa_prefill_desc))
+    return fail(MSA_ERR_INVALID_ARG, "struct_size %u != %zu (ABI mismatch)", d->struct_size,
+                sizeof(msa_prefill_desc));
+  if (d->num_seqs < 1 || d->total_q < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(MSA_ERR_INVALID_ARG, "bad sizes: num_seqs %d total_q %d Hq %d Hkv %d", d->num_seqs,
+                d->total_q, d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(MSA_ERR_INVALID_ARG, "num_q_heads %d not a multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_slots < 1 || d->slots_per_split < 1 || d->num_slots % d->slots_per_split)
+    return fail(MSA_ERR_INVALID_ARG, "num_slots %d must be a positive multiple of slots_per_split %d",
+                d->num_slots, d->slots_per_split);
+  if (d->page_size < 1 || d->unit_tokens < 1 || d->max_pages < 1 || d->num_phys_pages < 1)
+    return fail(MSA_ERR_INVALID_ARG, "bad page geometry");
+  if (d->page_table_stride < d->max_pages)
+    return fail(MSA_ERR_INVALID_ARG, "page_table_stride %lld < max_pages %d",
+                (long long)d->page_table_stride, d->max_pages);
+  if (!(d->sm_scale >= 0.0f) || !std::isfinite(d->sm_scale) || !std::isfinite(d->q_scale) ||
+      !std::isfinite(d->k_scale) || !std::isfinite(d->v_scale))
+    return fail(MSA_ERR_INVALID_ARG, "scales must be finite (sm_scale >= 0)");
+  if (d->head_dim_qk < 1 || d->head_dim_v < 1)
+    return fail(MSA_ERR_INVALID_ARG, "bad head dims");
+  const void *need[] = {d->q, d->q_seq, d->q_pos, d->seq_lens, d->k_cache, d->v_cache,
+                        d->page_table, d->sel_idx, d->sel_mask, d->partial_o, d->partial_lse};
+  const char *names[] = {"q", "q_seq", "q_pos", "seq_lens", "k_cache", "v_cache",
+                         "page_table", "sel_idx", "sel_mask", "partial_o", "partial_lse"};
+  for (int i = 0; i < 11; ++i)
+    if (!need[i]) return fail(MSA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+  if (d->sel_stride_tok < d->num_slots || d->sel_stride_head < 0)
+    return fail(MSA_ERR_INVALID_ARG, "selection strides too small");
+  if ((int64_t)d->total_q * d->num_kv_heads * d->num_slots >= (1ll << 31) ||
+      (int64_t)d->total_q * d->num_q_heads >= (1ll << 31) || d->total_q >= (1 << 23))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit plan indices");
+
+  // ---- route selection: page selections only in this build
+  if (d->unit_tokens != d->page_size)
+    return fail(MSA_ERR_UNSUPPORTED, "microblock selections (unit_tokens %d < page_size %d) "
+                "are not supported by this build", d->unit_tokens, d->page_size);
+  const int route = page_route(d);
+  if (route < 0)
+    return fail(MSA_ERR_UNSUPPORTED, "dtype pair q %d / kv %d unsupported", d->q_dtype, d->kv_dtype);
+  if (d->page_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "page route is built for page_size 128 (got %d)", d->page_size);
+  if (d->head_dim_qk != d->head_dim_v)
+    return fail(MSA_ERR_UNSUPPORTED, "page route needs head_dim_qk == head_dim_v");
+  const int D = d->head_dim_qk;
+  if (!((D == 64 || D == 128) && (route != kRouteQ8KV4 || D == 128)))
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim %d unsupported for this dtype", D);
+  if (d->slots_per_split != 1)
+    return fail(MSA_ERR_UNSUPPORTED, "page route writes one partial per slot (slots_per_split 1)");
+  if (d->num_slots > 255)
+    return fail(MSA_ERR_UNSUPPORTED, "at most 255 slots");
+
+  // ---- alignment of vector accesses
+  const int qb = esize(d->q_dtype);
+  if (!aligned(d->q, 16) || (d->q_stride_tok * qb) % 16 || (d->q_stride_head * qb) % 16 ||
+      d->q_stride_head < 0 || d->q_stride_tok < 0)
+    return fail(MSA_ERR_INVALID_ARG, "q must be 16-byte aligned with 16-byte aligned strides");
+  if (!aligned(d->k_cache, 16) || !aligned(d->v_cache, 16) || d->kv_stride_page_bytes % 16 ||
+      d->kv_stride_tok_bytes % 16 || d->kv_stride_head_bytes % 16)
+    return fail(MSA_ERR_INVALID_ARG, "k/v cache and strides must be 16-byte aligned");
+  if (route == kRouteQ8KV4) {
+    if (!d->k_sf || !d->v_sf) return fail(MSA_ERR_INVALID_ARG, "NVFP4 scales are NULL");
+    if (!aligned(d->k_sf, 8) || !aligned(d->v_sf, 8) || d->sf_stride_page_bytes % 8 ||
+        d->sf_stride_tok_bytes % 8 || d->sf_stride_head_bytes % 8)
+      return fail(MSA_ERR_INVALID_ARG, "NVFP4 scale arrays and strides must be 8-byte aligned");
+  }
+  if (!aligned(d->partial_o, 16) || d->po_row_stride % 4 || d->po_split_stride % 4 ||
+      d->po_row_stride < d->head_dim_v)
+    return fail(MSA_ERR_INVALID_ARG, "partial_o must be 16-byte aligned, row stride >= head_dim_v");
+  if (!aligned(d->partial_lse, 4)) return fail(MSA_ERR_INVALID_ARG, "partial_lse misaligned");
+
+  PageArgs &r = *a;
+  memset(&r, 0, sizeof(r));
+  r.num_seqs = d->num_seqs;
+  r.total_q = d->total_q;
+  r.Hq = d->num_q_heads;
+  r.Hkv = d->num_kv_heads;
+  r.G = d->num_q_heads / d->num_kv_heads;
+  r.D = D;
+  r.page_size = d->page_size;
+  r.num_slots = d->num_slots;
+  r.max_pages = d->max_pages;
+  r.num_phys_pages = d->num_phys_pages;
+  r.chunk = (kPageRouteRowsPerUnit + r.G - 1) / r.G;
+  r.route = route;
+  const float sm = d->sm_scale > 0.0f ? d->sm_scale : 1.0f / std::sqrt((float)d->head_dim_qk);
+  r.scale_log2 = (float)((double)sm * d->q_scale * d->k_scale * 1.4426950408889634);
+  r.v_scale = d->v_scale;
+  r.q = d->q;
+  r.q_stride_tok = d->q_stride_tok;
+  r.q_stride_head = d->q_stride_head;
+  r.q_seq = d->q_seq;
+  r.q_pos = d->q_pos;
+  r.seq_lens = d->seq_lens;
+  r.k_cache = (const uint8_t *)d->k_cache;
+  r.v_cache = (const uint8_t *)d->v_cache;
+  r.kv_stride_page = d->kv_stride_page_bytes;
+  r.kv_stride_tok = d->kv_stride_tok_bytes;
+  r.kv_stride_head = d->kv_stride_head_bytes;
+  r.k_sf = d->k_sf;
+  r.v_sf = d->v_sf;
+  r.sf_stride_page = d->sf_stride_page_bytes;
+  r.sf_stride_tok = d->sf_stride_tok_bytes;
+  r.sf_stride_head = d->sf_stride_head_bytes;
+  r.page_table = d->page_table;
+  r.pt_stride = d->page_table_stride;
+  r.sel_idx = d->sel_idx;
+  r.sel_mask = d->sel_mask;
+  r.sel_stride_tok = d->sel_stride_tok;
+  r.sel_stride_head = d->sel_stride_head;
+  r.partial_o = d->partial_o;
+  r.po_split_stride = d->po_split_stride;
+  r.po_row_stride = d->po_row_stride;
+  r.partial_lse = d->partial_lse;
+  r.pl_split_stride = d->pl_split_stride;
+  const int64_t L = (int64_t)d->num_seqs * d->max_pages * d->num_kv_heads;
+  const int64_t NS = (int64_t)d->total_q * d->num_kv_heads * d->num_slots;
+  if (L >= (1ll << 31)) return fail(MSA_ERR_UNSUPPORTED, "too many page lists");
+  r.lay = page_layout(L, NS);
+  // every unit holds >= 1 entry: units <= entries/chunk + non-empty lists
+  r.max_units = NS / r.chunk + (L < NS ? L : NS);
+  return MSA_OK;
+}
+
+msa_status bind_workspace(PageArgs *a, const msa_prefill_desc *d, void *ws, size_t bytes) {
+  if (bytes < a->lay.total)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", bytes, a->lay.total);
+  if (!ws) return fail(MSA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a->ws = (uint8_t *)ws;
+  a->err_flags = d->err_flags ? d->err_flags : (uint32_t *)(a->ws + a->lay.meta) + 1;
+  return MSA_OK;
+}
+
+msa_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_prefill_workspace_bytes(const msa_prefill_desc *d, size_t *bytes) {
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  PageArgs a;
+  msa_status s = check_desc(d, &a);
+  if (s != MSA_OK) return s;
+  *bytes = a.lay.total;
+  return ok();
+}
+
+msa_status msa_prefill_plan(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
+  PageArgs a;
+  msa_status s = check_desc(d, &a);
+  if (s != MSA_OK) return s;
+  if ((s = bind_workspace(&a, d, ws, ws_bytes)) != MSA_OK) return s;
+  return hip_status(launch_page_plan(a, (hipStream_t)stream), "plan launch");
+}
+
+msa_status msa_prefill_attend(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
+  PageArgs a;
+  msa_status s = check_desc(d, &a);
+  if (s != MSA_OK) return s;
+  if ((s = bind_workspace(&a, d, ws, ws_bytes)) != MSA_OK) return s;
+  return hip_status(launch_page_attend(a, (hipStream_t)stream), "attention launch");
+}
+
+msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
+  msa_status s = msa_prefill_plan(d, ws, ws_bytes, stream);
+  if (s != MSA_OK) return s;
+  return msa_prefill_attend(d, ws, ws_bytes, stream);
+}
+
+msa_status msa_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
+                       int64_t pl_split, int32_t num_splits, int64_t num_rows, int32_t dv, void *out,
+                       int32_t out_dtype, int64_t out_row, float *lse, void *stream) {
+  if (num_rows < 0 || num_splits < 1 || dv < 4 || dv > 1024 || dv % 4)
+    return fail(MSA_ERR_INVALID_ARG, "bad sizes: splits %d rows %lld head_dim_v %d", num_splits,
+                (long long)num_rows, dv);
+  if (num_rows == 0) return ok();
+  if (!po || !pl || !out) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  if (out_dtype != MSA_F32 && out_dtype != MSA_BF16 && out_dtype != MSA_F16)
+    return fail(MSA_ERR_INVALID_ARG, "out_dtype must be F32, BF16 or F16");
+  const int ob = esize(out_dtype);
+  if (!aligned(po, 16) || po_row % 4 || po_split % 4 || po_row < dv)
+    return fail(MSA_ERR_INVALID_ARG, "partial_o must be 16-byte aligned with row stride >= head_dim_v");
+  if (!aligned(out, 4 * ob) || (out_row * ob) % (4 * ob) || out_row < dv)
+    return fail(MSA_ERR_INVALID_ARG, "out must be aligned to 4 elements with row stride >= head_dim_v");
+  if (!aligned(pl, 4) || (lse && !aligned(lse, 4)) || pl_split < 0)
+    return fail(MSA_ERR_INVALID_ARG, "lse buffers misaligned");
+  return hip_status(launch_combine(po, po_split, po_row, pl, pl_split, num_splits, num_rows, dv, out,
+                                   out_dtype, out_row, lse, (hipStream_t)stream),
+                    "combine launch");
+}
+
+msa_status msa_nvfp4_dequant_e4m3(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
+                                  int64_t n, void *stream) {
+  if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (!codes || !scales || !out) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  return hip_status(launch_nvfp4_dequant(codes, scales, out, n, (hipStream_t)stream), "dequant launch");
+}
+
+int msa_device_supported(int device) {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 yes, 2 no
+  if (device < 0 || device >= 64) return 0;
+  int c = cache[device].load();
+  if (c) return c == 1;
+  hipDeviceProp_t prop;
+  int yes = 0;
+  if (hipGetDeviceProperties(&prop, device) == hipSuccess)
+    yes = strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.sharedMemPerBlock >= 65536;
+  cache[device].store(yes ? 1 : 2);
+  return yes;
+}
+
+const char *msa_status_str(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char *msa_last_error(void) { return g_err; }
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+}  // extern "C"

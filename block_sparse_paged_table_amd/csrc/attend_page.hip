@@ -1,0 +1,482 @@
+// Attention step of the page-selection route (MiniMax-AI/MSA PR 21, section
+// "K1"), written for gfx950.
+//
+// One workgroup owns one work unit: a chunk of the queries that selected one
+// (request, logical page, KV head).  It loads that physical page once --
+// K as the QK operand type, V transposed to [d][key] as FP16 (or FP32) --
+// into LDS, then its four waves stream 16-row tiles of (query token, query
+// head) rows through:
+//
+//   S^T = K . Q^T        MFMA, FP32 accumulate (K rows = A operand from LDS,
+//                        Q rows = B operand straight from HBM/L2)
+//   mask                 only where a row can see part of the page: the key
+//                        offset must not pass the row's visible limit; a
+//                        wave-uniform ballot skips the select when every row
+//                        of the tile sees the whole page (section "K1",
+//                        "Softmax" bullet)
+//   softmax              row max / sum over 128 keys in registers
+//   O^T = V^T . P^T      MFMA; P in FP16 (BF16 P would miss 1e-3), FP32 acc
+//   epilogue             partial_o = O / l * v_scale (FP32), lse = m + ln l
+//
+// Computing S^T rather than S leaves each lane holding one query row's
+// scores in exactly the register layout the B operand of O^T = V^T P^T
+// needs (the key order inside a 32-key block is chosen to make that true),
+// and leaves each lane holding one output row for the epilogue, so no
+// cross-lane shuffles are needed except the 4-lane row reductions.
+//
+// Routes (Q / KV storage -> MFMA types):
+//   F32   : f32 / f32    -> QK 16x16x4 f32, PV 16x16x4 f32
+//   BF16  : bf16 / bf16  -> QK 16x16x32 bf16, PV 16x16x32 f16 with V scaled by
+//           a power of two per page so every BF16 value is exact in FP16
+//   F16   : f16 / f16    -> QK and PV 16x16x32 f16
+//   Q8KV4 : e4m3 / nvfp4 -> NVFP4 dequantised once per page to E4M3 (exact
+//           product, one rounding; section "Build the prefill for SM107"),
+//           QK 16x16x32 fp8, V E4M3 -> FP16 (exact), PV 16x16x32 f16
+#include "launch.h"
+
+namespace msa {
+namespace {
+
+constexpr int PAGE = 128;
+constexpr int NT = PAGE / 16;  // key tiles of 16 keys
+constexpr int THREADS = 256;
+constexpr int NWAVES = THREADS / kWave;
+
+template <int ROUTE> struct RouteInfo;
+template <> struct RouteInfo<kRouteF32> { static constexpr int QB = 4; static constexpr bool F16PV = false; };
+template <> struct RouteInfo<kRouteBF16> { static constexpr int QB = 2; static constexpr bool F16PV = true; };
+template <> struct RouteInfo<kRouteF16> { static constexpr int QB = 2; static constexpr bool F16PV = true; };
+template <> struct RouteInfo<kRouteQ8KV4> { static constexpr int QB = 1; static constexpr bool F16PV = true; };
+
+// Key (in-page offset) carried by A-operand row m of key tile t.  For FP16
+// PV the keys of tiles 2b and 2b+1 interleave so that the four S^T registers
+// of a lane in both tiles are 8 consecutive keys of 32-key block b.
+template <int ROUTE> __device__ __forceinline__ int key_of(int t, int m) {
+  if constexpr (ROUTE == kRouteF32) return t * 16 + m;
+  else return (t >> 1) * 32 + (m >> 2) * 8 + (t & 1) * 4 + (m & 3);
+}
+template <int ROUTE> __device__ __forceinline__ int row_of_key(int k) {
+  if constexpr (ROUTE == kRouteF32) return k & 15;
+  else return (k & 3) | (((k >> 3) & 3) << 2);
+}
+
+template <int ROUTE, int D> struct Geom {
+  static constexpr int QB = RouteInfo<ROUTE>::QB;
+  static constexpr int RB = D * QB;          // bytes of one K row in LDS
+  static constexpr int CPR = RB / 16;        // 16-byte chunks per K row
+  static constexpr int LANE_CH = CPR / 4;    // chunks of the row one lane holds
+  static constexpr int SWZ_SHIFT = CPR >= 16 ? 0 : (CPR == 8 ? 1 : 2);
+  static constexpr int K_BYTES = PAGE * RB;
+  static constexpr int VROW_F32 = D * 4 + 16;  // padded V row (FP32 route)
+  static constexpr int V_BYTES = RouteInfo<ROUTE>::F16PV ? D * PAGE * 2 : PAGE * VROW_F32;
+  static constexpr int LDS = K_BYTES + V_BYTES + 64;
+};
+
+// Byte offset of 16-byte chunk c of K row `key`: XOR swizzle so that the 16
+// rows one MFMA reads land in distinct LDS banks.
+template <int ROUTE, int D> __device__ __forceinline__ int k_off(int key, int c) {
+  using Gm = Geom<ROUTE, D>;
+  const int sw = row_of_key<ROUTE>(key) >> Gm::SWZ_SHIFT;
+  return key * Gm::RB + ((c ^ sw) << 4);
+}
+// Byte offset of the 16-byte chunk holding keys [8c, 8c+8) of V^T row dv.
+__device__ __forceinline__ int vt_off(int dv, int c) { return dv * (PAGE * 2) + ((c ^ (dv & 15)) << 4); }
+
+template <typename T> __device__ __forceinline__ T ld(const void *p) { return *(const T *)p; }
+
+// ------------------------------------------------------------ page loading
+
+// F32 / BF16 / F16: K rows copied as-is (swizzled); V transposed to FP16
+// (or kept [key][d] in FP32).  Returns the factor folded into v_scale.
+template <int ROUTE, int D>
+__device__ __forceinline__ float load_page_float(const PageArgs &a, int phys, int g, uint8_t *sK,
+                                                 uint8_t *sV, float *sRed) {
+  using Gm = Geom<ROUTE, D>;
+  const int tid = threadIdx.x;
+  const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
+  const uint8_t *vb = a.v_cache + (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
+  // K
+  constexpr int KCH = PAGE * Gm::CPR / THREADS;
+  u32x4 kreg[KCH];
+#pragma unroll
+  for (int it = 0; it < KCH; ++it) {
+    const int q = it * THREADS + tid, key = q / Gm::CPR, c = q % Gm::CPR;
+    kreg[it] = ld<u32x4>(kb + key * a.kv_stride_tok + c * 16);
+  }
+#pragma unroll
+  for (int it = 0; it < KCH; ++it) {
+    const int q = it * THREADS + tid, key = q / Gm::CPR, c = q % Gm::CPR;
+    *(u32x4 *)(sK + k_off<ROUTE, D>(key, c)) = kreg[it];
+  }
+  if constexpr (ROUTE == kRouteF32) {
+    constexpr int VCH = PAGE * D / 4 / THREADS;  // 16-byte chunks per thread
+#pragma unroll
+    for (int it = 0; it < VCH; ++it) {
+      const int q = it * THREADS + tid, key = q / (D / 4), c = q % (D / 4);
+      *(u32x4 *)(sV + key * Gm::VROW_F32 + c * 16) = ld<u32x4>(vb + key * a.kv_stride_tok + c * 16);
+    }
+    return 1.0f;
+  } else {
+    // thread -> key pair kp, d block db of D/4 elements
+    const int kp = tid & 63, db = tid >> 6;
+    constexpr int DB = D / 4;
+    constexpr int NCH = DB * 2 / 16;  // 16-byte chunks per key
+    u32x4 v0[NCH], v1[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v0[c] = ld<u32x4>(vb + (2 * kp) * a.kv_stride_tok + db * DB * 2 + c * 16);
+      v1[c] = ld<u32x4>(vb + (2 * kp + 1) * a.kv_stride_tok + db * DB * 2 + c * 16);
+    }
+    float scale = 1.0f, vfac = 1.0f;
+    if constexpr (ROUTE == kRouteBF16) {
+      // power-of-two scale so that max|v| * scale lies in [2^14, 2^15):
+      // every BF16 value (8-bit significand) is then exact in FP16 unless it
+      // is below 2^-14 of the page maximum.
+      uint32_t mx = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a0 = v0[c][w] & 0x7fff7fffu, a1 = v1[c][w] & 0x7fff7fffu;
+          mx = max(mx, max(max(a0 & 0xffffu, a0 >> 16), max(a1 & 0xffffu, a1 >> 16)));
+        }
+      // wave max then block max (bf16 bit patterns of |v| order like values)
+      for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+      if ((tid & 63) == 0) ((uint32_t *)sRed)[tid >> 6] = mx;
+      __syncthreads();
+      mx = ((uint32_t *)sRed)[0];
+#pragma unroll
+      for (int w = 1; w < NWAVES; ++w) mx = max(mx, ((uint32_t *)sRed)[w]);
+      const float vmax = bf16_bits_to_f32(mx);
+      int e = 0;
+      if (vmax > 0.0f && vmax < INFINITY) {
+        int x;
+        (void)frexpf(vmax, &x);
+        e = min(100, max(-100, 15 - x));
+      }
+      scale = __uint_as_float((uint32_t)(127 + e) << 23);
+      vfac = __uint_as_float((uint32_t)(127 - e) << 23);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int dv = db * DB + c * 8 + w * 2 + hh;
+          const uint32_t b0 = hh ? (v0[c][w] >> 16) : (v0[c][w] & 0xffffu);
+          const uint32_t b1 = hh ? (v1[c][w] >> 16) : (v1[c][w] & 0xffffu);
+          uint32_t word;
+          if constexpr (ROUTE == kRouteBF16) {
+            word = pack_f16x2(bf16_bits_to_f32(b0) * scale, bf16_bits_to_f32(b1) * scale);
+          } else {
+            word = b0 | (b1 << 16);
+          }
+          *(uint32_t *)(sV + vt_off(dv, kp >> 2) + ((kp & 3) << 2)) = word;
+        }
+    return vfac;
+  }
+}
+
+// Q8KV4: NVFP4 K/V dequantised to E4M3 once per page.
+template <int D>
+__device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int g, uint8_t *sK,
+                                                uint8_t *sV) {
+  static_assert(D == 128, "Q8KV4 route is built for head_dim 128");
+  const int tid = threadIdx.x;
+  const int64_t kvo = (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
+  const int64_t sfo = (int64_t)phys * a.sf_stride_page + (int64_t)g * a.sf_stride_head;
+  {  // K: thread -> key tid/2, half tid%2 of the row (64 elements)
+    const int key = tid >> 1, half = tid & 1;
+    const uint8_t *cp = a.k_cache + kvo + key * a.kv_stride_tok + half * (D / 4);
+    const uint32_t sf = ld<uint32_t>(a.k_sf + sfo + key * a.sf_stride_tok + half * (D / 32));
+    const u32x4 c0 = ld<u32x4>(cp), c1 = ld<u32x4>(cp + 16);
+    const uint32_t words[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {  // 16 output bytes = 2 code words = one scale
+      const uint32_t scale = (sf >> (8 * ch)) & 0xffu;
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t cw = words[ch * 2 + (w >> 1)] >> (16 * (w & 1));
+        uint32_t o = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o |= nvfp4_to_e4m3((cw >> (4 * i)) & 15u, scale) << (8 * i);
+        out[w] = o;
+      }
+      *(u32x4 *)(sK + k_off<kRouteQ8KV4, D>(key, half * 4 + ch)) = out;
+    }
+  }
+  {  // V: thread -> key pair kp, d block db of 32 elements; written as V^T FP16
+    const int kp = tid & 63, db = tid >> 6;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key = 2 * kp + kk;
+      const uint8_t *cp = a.v_cache + kvo + key * a.kv_stride_tok + db * 16;
+      const u32x4 cw4 = ld<u32x4>(cp);
+      const uint32_t sf = ld<uint16_t>(a.v_sf + sfo + key * a.sf_stride_tok + db * 2);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t code = (cw4[e >> 3] >> (4 * (e & 7))) & 15u;
+        const uint32_t scale = (sf >> (8 * (e >> 4))) & 0xffu;
+        const _Float16 hv = (_Float16)e4m3_to_f32(nvfp4_to_e4m3(code, scale));
+        const int dv = db * 32 + e;
+        *(_Float16 *)(sV + vt_off(dv, kp >> 2) + ((kp & 3) << 2) + kk * 2) = hv;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ the kernel
+
+template <int ROUTE, int D>
+__global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2 : 1))
+    k1_page_attend(const PageArgs a) {
+  using Gm = Geom<ROUTE, D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Gm::LDS];
+  uint8_t *sK = smem;
+  uint8_t *sV = smem + Gm::K_BYTES;
+  float *sRed = (float *)(smem + Gm::K_BYTES + Gm::V_BYTES);
+
+  // ---- work unit (XCD-aware: consecutive units stay on one XCD's L2)
+  const int32_t *meta = (const int32_t *)(a.ws + a.lay.meta);
+  const int num_units = meta[0];
+  const int per_xcd = (num_units + 7) >> 3;
+  const int bid = blockIdx.x;
+  if ((bid >> 3) >= per_xcd) return;
+  const int unit = (bid & 7) * per_xcd + (bid >> 3);
+  if (unit >= num_units) return;
+  const int32_t *unit_off = (const int32_t *)(a.ws + a.lay.unit_off);
+  const int32_t *list_off = (const int32_t *)(a.ws + a.lay.list_off);
+  int lo = 0, hi = (int)a.lay.num_lists;  // unit_off[lo] <= unit < unit_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (unit_off[mid] <= unit) lo = mid; else hi = mid;
+  }
+  const int list = lo;
+  const int chunk_i = unit - unit_off[list];
+  const int e_begin = list_off[list] + chunk_i * a.chunk;
+  const int e_count = min(a.chunk, list_off[list + 1] - e_begin);
+  const int g = list % a.Hkv;
+  const int u = (list / a.Hkv) % a.max_pages;
+  const int b = list / (a.Hkv * a.max_pages);
+  const int phys = a.page_table[b * a.pt_stride + u];
+
+  // ---- page -> LDS
+  float vfac = 1.0f;
+  if constexpr (ROUTE == kRouteQ8KV4) load_page_nvfp4<D>(a, phys, g, sK, sV);
+  else vfac = load_page_float<ROUTE, D>(a, phys, g, sK, sV, sRed);
+  __syncthreads();
+  const float out_scale = a.v_scale * vfac;
+
+  const PlanEntry *entries = (const PlanEntry *)(a.ws + a.lay.entries) + e_begin;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int G = a.G;
+  const int rows_total = e_count * G;
+  const int n_tiles = (rows_total + 15) >> 4;
+  const uint8_t *qbase = (const uint8_t *)a.q;
+
+  // Row of this lane in a tile.  Rows past the end (ragged last tile, or the
+  // prefetch beyond the last tile) read entry 0 / head 0 -- always in bounds --
+  // and never store.
+  struct RowInfo {
+    int tok, slot, limit, h;
+    bool active;
+  };
+  auto row_of = [&](int tile) {
+    RowInfo ri;
+    const int rho = tile * 16 + n;
+    ri.active = rho < rows_total;
+    const int e = ri.active ? rho / G : 0;
+    const int hl = ri.active ? rho - e * G : 0;
+    const PlanEntry ent = entries[e];
+    ri.tok = ent.tok_slot >> 8;
+    ri.slot = ent.tok_slot & 255;
+    ri.limit = ri.active ? ent.limit : -1;
+    ri.h = g * G + hl;
+    return ri;
+  };
+  // Q operand: this lane's contiguous quarter of its row
+  auto load_q = [&](const RowInfo &ri, u32x4 *q) {
+    const uint8_t *qp = qbase + ((int64_t)ri.tok * a.q_stride_tok + (int64_t)ri.h * a.q_stride_head) * Gm::QB +
+                        grp * (Gm::RB / 4);
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) q[c] = ld<u32x4>(qp + c * 16);
+  };
+
+  RowInfo cur = row_of(wave);
+  u32x4 qreg[Gm::LANE_CH];
+  load_q(cur, qreg);
+
+  for (int tile = wave; tile < n_tiles; tile += NWAVES) {
+    // The page in LDS is loop-invariant; without this compiler-only fence the
+    // K/V fragment reads are hoisted out of the loop into (spilled) registers.
+    __asm__ volatile("" ::: "memory");
+    const RowInfo nxt = row_of(tile + NWAVES);  // software pipeline: next entry
+    const int tok = cur.tok, slot = cur.slot, limit = cur.limit, h = cur.h;
+    const bool active = cur.active;
+
+    // ---- S^T = K Q^T  (chunk-outer so each K fragment is used once, at once)
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 kr = *(const u32x4 *)(sK + k_off<ROUTE, D>(key_of<ROUTE>(t, n), grp * Gm::LANE_CH + c));
+        if constexpr (ROUTE == kRouteF32) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[t] = mfma_f32(__uint_as_float(kr[w]), __uint_as_float(qreg[c][w]), acc[t]);
+        } else if constexpr (ROUTE == kRouteBF16) {
+          acc[t] = mfma_bf16(kr, qreg[c], acc[t]);
+        } else if constexpr (ROUTE == kRouteF16) {
+          acc[t] = mfma_f16(kr, qreg[c], acc[t]);
+        } else {
+          acc[t] = mfma_fp8(u32x2{kr[0], kr[1]}, u32x2{qreg[c][0], qreg[c][1]}, acc[t]);
+          acc[t] = mfma_fp8(u32x2{kr[2], kr[3]}, u32x2{qreg[c][2], qreg[c][3]}, acc[t]);
+        }
+      }
+    }
+
+    // ---- issue the next tile's Q loads; they land during softmax/PV/epilogue
+    u32x4 qnext[Gm::LANE_CH];
+    load_q(nxt, qnext);
+
+    // ---- scale (log2 domain), mask, row max
+    const bool full = __all(limit >= PAGE - 1);
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[t][i] * a.scale_log2;
+        if (!full && key_of<ROUTE>(t, 4 * grp + i) > limit) x = -INFINITY;
+        acc[t][i] = x;
+        m = fmaxf(m, x);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (m == -INFINITY) m = 0.0f;  // inactive row: keep the arithmetic finite
+
+    // ---- P = exp2(S - m).  l (exact FP32 sum) gives the LSE; lp, the sum of
+    // the P values the PV product actually uses, normalises the output so
+    // that its weights sum to one.
+    float l = 0.0f, lp = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(acc[t][i] - m);
+        l += p;
+        if constexpr (RouteInfo<ROUTE>::F16PV) {
+          const float pr = (float)(_Float16)p;
+          acc[t][i] = pr;
+          lp += pr;
+        } else {
+          acc[t][i] = p;
+        }
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if constexpr (RouteInfo<ROUTE>::F16PV) {
+      lp += __shfl_xor(lp, 16);
+      lp += __shfl_xor(lp, 32);
+    } else {
+      lp = l;
+    }
+
+    // ---- O^T = V^T P^T
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (RouteInfo<ROUTE>::F16PV) {
+#pragma unroll
+      for (int kb = 0; kb < PAGE / 32; ++kb) {
+        u32x4 pf;
+        pf[0] = pack_f16x2(acc[2 * kb][0], acc[2 * kb][1]);
+        pf[1] = pack_f16x2(acc[2 * kb][2], acc[2 * kb][3]);
+        pf[2] = pack_f16x2(acc[2 * kb + 1][0], acc[2 * kb + 1][1]);
+        pf[3] = pack_f16x2(acc[2 * kb + 1][2], acc[2 * kb + 1][3]);
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+          const u32x4 vf = *(const u32x4 *)(sV + vt_off(mt * 16 + n, kb * 4 + grp));
+          o[mt] = mfma_f16(vf, pf, o[mt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t * 16 + 4 * grp + i;
+#pragma unroll
+          for (int mt = 0; mt < D / 16; ++mt) {
+            const float vv = *(const float *)(sV + key * Gm::VROW_F32 + (mt * 16 + n) * 4);
+            o[mt] = mfma_f32(vv, acc[t][i], o[mt]);
+          }
+        }
+    }
+
+    // ---- epilogue: this lane holds row n, columns 16*mt + 4*grp + [0,4)
+    if (active) {
+      const float inv = out_scale / lp;
+      const int64_t row = (int64_t)tok * a.Hq + h;
+      float *dst = a.partial_o + (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        f32x4 v = o[mt] * inv;
+        *(f32x4 *)(dst + mt * 16) = v;
+      }
+      if (grp == 0)
+        a.partial_lse[(int64_t)slot * a.pl_split_stride + row] =
+            (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    }
+    cur = nxt;
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) qreg[c] = qnext[c];
+  }
+}
+
+template <int ROUTE, int D>
+hipError_t launch_route(const PageArgs &a, hipStream_t s) {
+  const int64_t grid = (a.max_units + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  k1_page_attend<ROUTE, D><<<(unsigned)grid, THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_page_attend(const PageArgs &a, hipStream_t s) {
+  switch (a.route) {
+    case kRouteF32:
+      return a.D == 64 ? launch_route<kRouteF32, 64>(a, s) : launch_route<kRouteF32, 128>(a, s);
+    case kRouteBF16:
+      return a.D == 64 ? launch_route<kRouteBF16, 64>(a, s) : launch_route<kRouteBF16, 128>(a, s);
+    case kRouteF16:
+      return a.D == 64 ? launch_route<kRouteF16, 64>(a, s) : launch_route<kRouteF16, 128>(a, s);
+    case kRouteQ8KV4:
+      return launch_route<kRouteQ8KV4, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Standalone device dequantisation (same routine the attention uses).
+namespace {
+__global__ void nvfp4_dequant_kernel(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
+                                     int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)nvfp4_to_e4m3(codes[i] & 15u, scales[i]);
+}
+}  // namespace
+
+hipError_t launch_nvfp4_dequant(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
+                                int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  nvfp4_dequant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(codes, scales, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the
+// kernels.  Everything here is resolved and validated on the host first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace msa {
+
+enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3 };
+
+// Resolved arguments of the page-selection route.
+struct PageArgs {
+  int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, num_slots, max_pages, num_phys_pages;
+  int32_t chunk;              // entries per work unit
+  int32_t route;
+  float scale_log2;           // sm_scale * q_scale * k_scale * log2(e)
+  float v_scale;
+  const void *q;
+  int64_t q_stride_tok, q_stride_head;
+  const int32_t *q_seq, *q_pos, *seq_lens;
+  const uint8_t *k_cache, *v_cache;
+  int64_t kv_stride_page, kv_stride_tok, kv_stride_head;   // bytes
+  const uint8_t *k_sf, *v_sf;
+  int64_t sf_stride_page, sf_stride_tok, sf_stride_head;   // bytes
+  const int32_t *page_table;
+  int64_t pt_stride;
+  const int32_t *sel_idx;
+  const uint8_t *sel_mask;
+  int64_t sel_stride_tok, sel_stride_head;
+  float *partial_o;
+  int64_t po_split_stride, po_row_stride;
+  float *partial_lse;
+  int64_t pl_split_stride;
+  uint32_t *err_flags;        // never null here (points into the workspace if the caller passed none)
+  // workspace
+  uint8_t *ws;
+  PageLayout lay;
+  int64_t max_units;          // grid bound of the attention kernel
+};
+
+hipError_t launch_page_plan(const PageArgs &a, hipStream_t s);
+hipError_t launch_page_attend(const PageArgs &a, hipStream_t s);
+
+hipError_t launch_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
+                          int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
+                          int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s);
+
+hipError_t launch_nvfp4_dequant(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
+                                int64_t n, hipStream_t s);
+
+}  // namespace msa

@@ -235,11 +235,12 @@ def build_page_problem(
             keys = rng.random((total_q, n_sel_heads, max_pages))
             pages = np.arange(max_pages)[None, None, :]
             keys = np.where(pages < own[:, None, None], keys, np.inf)
-            order = np.argsort(keys, axis=-1, kind="stable")[:, :, :hist]
+            take = min(hist, max_pages)
+            order = np.argsort(keys, axis=-1, kind="stable")[:, :, :take]
             chosen_key = np.take_along_axis(keys, order, axis=-1)
             ok = np.isfinite(chosen_key)
-            sel_idx[:, :, 1:1 + hist] = np.where(ok, order, -1)
-            sel_mask[:, :, 1:1 + hist] = ok.astype(np.uint8)
+            sel_idx[:, :, 1:1 + take] = np.where(ok, order, -1)
+            sel_mask[:, :, 1:1 + take] = ok.astype(np.uint8)
     elif select == "all":
         assert K >= max_pages, "select='all' needs a slot per page"
         for p in range(max_pages):

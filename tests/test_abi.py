@@ -1,0 +1,107 @@
+"""C ABI contract tests that need no GPU: the library loads, exports every
+entry point include/msa.h declares, and rejects bad arguments on the host
+before anything is enqueued (no device call is made by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_paged_table_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.library()
+    declared = _declared()
+    assert {"msa_sparse_prefill", "msa_combine", "msa_prefill_plan", "msa_prefill_attend",
+            "msa_prefill_workspace_bytes"} <= declared
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert msa.msa_abi_version() == 1
+
+
+def _desc(**over):
+    d = dict(num_seqs=1, total_q=16, num_q_heads=4, num_kv_heads=1, head_dim_qk=64,
+             head_dim_v=64, page_size=128, unit_tokens=128, num_slots=3, slots_per_split=1,
+             sm_scale=0.0, q_scale=1.0, k_scale=1.0, v_scale=1.0,
+             q=FAKE, q_dtype=msa.MSA_F32, q_stride_tok=256, q_stride_head=64,
+             q_seq=FAKE, q_pos=FAKE, seq_lens=FAKE, k_cache=FAKE, v_cache=FAKE,
+             kv_dtype=msa.MSA_F32, kv_stride_page_bytes=128 * 256, kv_stride_tok_bytes=256,
+             kv_stride_head_bytes=256, page_table=FAKE, page_table_stride=4, max_pages=4,
+             num_phys_pages=4, sel_idx=FAKE, sel_mask=FAKE, sel_stride_tok=3, sel_stride_head=3,
+             partial_o=FAKE, po_split_stride=64 * 64, po_row_stride=64, partial_lse=FAKE,
+             pl_split_stride=64)
+    d.update(over)
+    return msa.PrefillDesc(**d)
+
+
+def test_workspace_query_accepts_valid_descriptor():
+    assert msa.msa_prefill_workspace_bytes(_desc()) > 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), msa.MsaError),
+    (dict(num_q_heads=5, num_kv_heads=2), msa.MsaError),
+    (dict(q_dtype=msa.MSA_BF16), msa.MsaError),              # mixed dtype pair
+    (dict(page_size=64, unit_tokens=64), msa.MsaError),     # page size without a kernel
+    (dict(q=FAKE + 4), msa.MsaError),                       # misaligned q
+    (dict(kv_stride_tok_bytes=260), msa.MsaError),          # misaligned stride
+    (dict(slots_per_split=2, num_slots=4), msa.MsaError),
+    (dict(num_slots=4, slots_per_split=3), msa.MsaError),
+    (dict(page_table_stride=2), msa.MsaError),
+    (dict(po_row_stride=32), msa.MsaError),
+    (dict(q_dtype=msa.MSA_E4M3, kv_dtype=msa.MSA_NVFP4, head_dim_qk=128, head_dim_v=128,
+          q_stride_tok=512, q_stride_head=128), msa.MsaError),  # NVFP4 without scales
+])
+def test_host_validation_rejects(over, status):
+    with pytest.raises(status) as ei:
+        msa.msa_prefill_workspace_bytes(_desc(**over))
+    assert ei.value.status in (1, 2)
+    assert msa.library().msa_last_error().decode()
+
+
+def test_struct_size_mismatch_rejected():
+    d = _desc()
+    d.struct_size = 8
+    with pytest.raises(msa.MsaError) as ei:
+        msa.msa_prefill_workspace_bytes(d)
+    assert ei.value.status == 1
+
+
+def test_workspace_too_small_rejected_before_launch():
+    lib = msa.library()
+    d = _desc()
+    need = msa.msa_prefill_workspace_bytes(d)
+    st = lib.msa_sparse_prefill(ctypes.byref(d), FAKE, need - 1, None)
+    assert st == 3  # MSA_ERR_WORKSPACE_TOO_SMALL
+    st = lib.msa_prefill_plan(ctypes.byref(d), FAKE + 8, need, None)
+    assert st == 1  # misaligned workspace
+
+
+def test_combine_validation():
+    lib = msa.library()
+    # zero rows is a no-op success; bad sizes and dtypes are rejected
+    assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 4, 0, 128, FAKE, msa.MSA_BF16, 128, None, None) == 0
+    assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 0, 8, 128, FAKE, msa.MSA_BF16, 128, None, None) == 1
+    assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 4, 8, 126, FAKE, msa.MSA_BF16, 128, None, None) == 1
+    assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 4, 8, 128, FAKE, 7, 128, None, None) == 1
+    assert lib.msa_combine(FAKE + 4, 0, 128, FAKE, 0, 4, 8, 128, FAKE, 0, 128, None, None) == 1
+
+
+def test_status_strings():
+    lib = msa.library()
+    assert lib.msa_status_str(0) == b"MSA_OK"
+    assert lib.msa_status_str(3) == b"MSA_ERR_WORKSPACE_TOO_SMALL"

@@ -1,0 +1,227 @@
+"""GPU parity of the page-selection route (plan + attention + combine)
+against the FP64 oracle, through the C ABI.
+
+Small problems are compared on every row; the full-size workloads (the
+shapes bench.py times, in the same launch configuration) on sampled tokens
+that the oracle computes one by one, plus the exact empty-slot pattern over
+all rows.  Tolerances are defined in tests/parity.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_paged_table_amd import synth
+from block_sparse_paged_table_amd.runner import DeviceProblem
+import oracle
+from parity import check_combined, check_partials, gpu_rows
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _run(p, **kw):
+    dp = DeviceProblem(p, **kw)
+    dp.run()
+    torch.cuda.synchronize()
+    return dp
+
+
+def _full_parity(p, out_dtype=None, **kw):
+    dp = _run(p, out_dtype=out_dtype, **kw)
+    ref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    r1 = check_partials(p, po, pl, ref)
+    r2 = check_combined(p, out, lse, ref, dp.out_dtype)
+    assert dp.err_flags() == ref["err"]
+    return dp, r1, r2
+
+
+def _small(seed, **kw):
+    args = dict(name="small", seed=seed, ctx_lens=[0, 300], chunk_lens=[700, 450],
+                page_size=128, Hq=16, Hkv=1, d=128, num_slots=8, q_dtype="bf16",
+                kv_dtype="bf16", out_dtype="f32", pad_rows=5, shuffle_slots=True)
+    args.update(kw)
+    return synth.build_page_problem(**args)
+
+
+def test_tiny_fp32_config_all_rows():
+    p = synth.make_config(0)
+    _full_parity(p)
+    _full_parity(p, out_dtype="f32")
+
+
+@pytest.mark.parametrize("qd,kd,d", [("bf16", "bf16", 128), ("f16", "f16", 128),
+                                     ("bf16", "bf16", 64), ("f16", "f16", 64),
+                                     ("f32", "f32", 128), ("e4m3", "nvfp4", 128)])
+def test_small_all_rows(qd, kd, d):
+    p = _small(11, q_dtype=qd, kv_dtype=kd, d=d, Hq=8, Hkv=2)
+    _full_parity(p)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 2), (6, 1), (8, 1), (32, 2), (48, 3)])
+def test_head_groupings(Hq, Hkv):
+    p = _small(12, Hq=Hq, Hkv=Hkv, d=64, ctx_lens=[129], chunk_lens=[400], num_slots=4)
+    _full_parity(p)
+
+
+def test_fp32_output_and_bf16_output_agree():
+    p = _small(13, out_dtype="bf16")
+    dp16 = _run(p)
+    dp32 = _run(p, out_dtype="f32")
+    assert torch.equal(dp16.out, dp32.out.to(torch.bfloat16))
+    ref = oracle.prefill_rows(p)
+    _, _, out, lse = gpu_rows(dp16, np.arange(p.total_q))
+    check_combined(p, out, lse, ref, "bf16")
+
+
+def test_strided_partial_buffer():
+    p = _small(14)
+    dp = _run(p, po_row_pad=32)
+    ref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, ref)
+    check_combined(p, out, lse, ref, "f32")
+
+
+def test_shared_selection_stride_zero():
+    p = _small(15, Hq=8, Hkv=2, share_sel_across_heads=True)
+    dp = DeviceProblem(p)
+    dp.sel_idx = dp.sel_idx[:, :1].expand(-1, p.Hkv, -1)
+    dp.sel_mask = dp.sel_mask[:, :1].expand(-1, p.Hkv, -1)
+    dp.desc = dp.make_desc()
+    assert dp.desc.sel_stride_head == 0
+    dp.run()
+    torch.cuda.synchronize()
+    ref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, ref)
+    check_combined(p, out, lse, ref, "f32")
+
+
+def test_error_flags_and_invalid_rows():
+    p = _small(16, num_slots=6, Hq=4, Hkv=1, d=64)
+    si, sm = p.sel_idx.numpy().copy(), p.sel_mask.numpy().copy()
+    qs = p.q_seq.numpy().copy()
+    si[3, 0, 2], sm[3, 0, 2] = p.max_pages + 3, 1        # unit beyond the table row
+    si[9, 0, 1], sm[9, 0, 1] = -2, 1                     # negative unit
+    src = int(np.nonzero(sm[400, 0])[0][0])              # a used slot of token 400
+    dst = 5 if src != 5 else 4
+    si[400, 0, dst], sm[400, 0, dst] = si[400, 0, src], 1  # duplicate of that slot
+    sm[17] = 0                                           # no selection at all
+    qs[20] = 9                                           # request that does not exist
+    pt = p.page_table.numpy().copy()
+    pt[1, 2] = p.num_phys_pages + 11                     # table entry beyond the cache
+    p = dataclasses.replace(p, sel_idx=torch.from_numpy(si), sel_mask=torch.from_numpy(sm),
+                            q_seq=torch.from_numpy(qs), page_table=torch.from_numpy(pt))
+    dp, _, _ = _full_parity(p)
+    assert dp.err_flags() == 1 | 2 | 4 | 8
+
+
+def test_physical_permutation_bitwise_invariant():
+    p = _small(17, extra_phys_pages=5)
+    perm = np.random.default_rng(3).permutation(p.num_phys_pages)
+    k2, v2 = torch.empty_like(p.k_cache), torch.empty_like(p.v_cache)
+    k2[perm], v2[perm] = p.k_cache, p.v_cache
+    pt = p.page_table.numpy()
+    pt2 = np.where(pt >= 0, perm[np.maximum(pt, 0)], -1).astype(np.int32)
+    p2 = dataclasses.replace(p, k_cache=k2, v_cache=v2, page_table=torch.from_numpy(pt2))
+    a, b = _run(p), _run(p2)
+    assert torch.equal(a.partial_lse, b.partial_lse)
+    fin = torch.isfinite(a.partial_lse)
+    assert torch.equal(a.partial_o[fin], b.partial_o[fin])
+    assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+
+
+@pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("e4m3", "nvfp4")])
+def test_three_runs_bitwise_identical(qd, kd):
+    p = _small(18, q_dtype=qd, kv_dtype=kd, Hq=16, Hkv=2)
+    dp = DeviceProblem(p)
+    snaps = []
+    for _ in range(3):
+        dp.partial_o.fill_(0)
+        dp.run()
+        torch.cuda.synchronize()
+        snaps.append((dp.partial_o.clone(), dp.partial_lse.clone(), dp.out.clone()))
+    for s in snaps[1:]:
+        assert all(torch.equal(x, y) for x, y in zip(snaps[0], s))
+
+
+def test_onehot_selection_probe_bitexact():
+    """Index probe: K[t, 0] = 128 * (t mod page) and Q[., 0] = 16 give logit
+    gaps so large that every partial is exactly the value row of the last
+    visible key of its page; V encodes (logical page, offset).  Pins the
+    page-table gather, slot -> slab placement and the causal diagonal bit
+    for bit."""
+    p = _small(19, q_dtype="bf16", kv_dtype="bf16", Hq=4, Hkv=1, d=64, ctx_lens=[77, 0],
+               chunk_lens=[500, 333], num_slots=5, pad_rows=0)
+    P, page, Hkv, d = p.k_cache.shape
+    k = torch.zeros((P, page, Hkv, d), dtype=torch.float32)
+    k[:, :, :, 0] = 128.0 * torch.arange(page, dtype=torch.float32)[None, :, None]
+    v = torch.zeros((P, page, Hkv, d), dtype=torch.float32)
+    inv = {}
+    pt = p.page_table.numpy()
+    for b in range(p.num_seqs):
+        for lp in range(pt.shape[1]):
+            if pt[b, lp] >= 0:
+                inv[int(pt[b, lp])] = (b, lp)
+    for phys, (b, lp) in inv.items():
+        v[phys, :, :, 0] = float(b)
+        v[phys, :, :, 1] = float(lp)
+        v[phys, :, :, 2] = torch.arange(page, dtype=torch.float32)[:, None]
+    q = torch.zeros(p.q.shape, dtype=torch.float32)
+    q[:, :, 0] = 16.0
+    p = dataclasses.replace(p, k_cache=k.to(torch.bfloat16), v_cache=v.to(torch.bfloat16),
+                            q=q.to(torch.bfloat16), sm_scale=1.0)
+    dp = _run(p)
+    po = dp.partial_o.cpu().numpy()
+    pl = dp.partial_lse.cpu().numpy()
+    si, sm = p.sel_idx.numpy(), p.sel_mask.numpy()
+    qpos, qseq, sl = p.q_pos.numpy(), p.q_seq.numpy(), p.seq_lens.numpy()
+    checked = 0
+    for t in range(p.total_q):
+        for j in range(p.num_slots):
+            rows = t * p.Hq + np.arange(p.Hq)
+            if sm[t, 0, j] == 0:
+                assert np.all(np.isneginf(pl[j, rows]))
+                continue
+            u = int(si[t, 0, j])
+            last = min(u * page + page - 1, int(qpos[t]), int(sl[qseq[t]]) - 1)
+            expect = np.zeros(d, np.float32)
+            expect[0], expect[1], expect[2] = qseq[t], u, last - u * page
+            assert np.array_equal(po[j, rows], np.broadcast_to(expect, (p.Hq, d))), (t, j)
+            checked += 1
+    assert checked > 1000
+
+
+# ---------------------------------------------------------------- full sizes
+
+def _sample_tokens(p, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    T = p.total_q
+    fixed = [0, 1, 127, 128, 129, T // 2, T - 2, T - 1]
+    picks = set(t for t in fixed if 0 <= t < T)
+    picks |= set(int(x) for x in rng.choice(T, size=min(n, T), replace=False))
+    return np.array(sorted(picks))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_full_size_config_sampled(cfg):
+    p = synth.make_config(cfg)
+    dp = _run(p)
+    keep = oracle.make_keep(p)
+    # exact empty-slot pattern over every row
+    ne = oracle.slot_nonempty(p, keep=keep)                   # [T, Hkv, K]
+    G = p.Hq // p.Hkv
+    ne_rows = np.repeat(ne, G, axis=1).reshape(p.total_q * p.Hq, p.num_slots).T  # [K, rows]
+    gpu_empty = torch.isneginf(dp.partial_lse).cpu().numpy()
+    assert np.array_equal(gpu_empty, ne_rows == 0)
+    assert dp.err_flags() == 0
+    toks = _sample_tokens(p)
+    ref = oracle.prefill_rows(p, toks, keep=keep)
+    po, pl, out, lse = gpu_rows(dp, toks)
+    check_partials(p, po, pl, ref)
+    check_combined(p, out, lse, ref, dp.out_dtype)
