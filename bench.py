@@ -66,7 +66,20 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle leg")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times), to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the method shards without exchange; see the design notes)", file=sys.stderr)

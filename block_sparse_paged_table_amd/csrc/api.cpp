@@ -2,6 +2,7 @@
 // launches.  Nothing here allocates device memory or waits on the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -73,9 +74,10 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
   if (d->page_table_stride < d->max_pages)
     return fail(MSA_ERR_INVALID_ARG, "page_table_stride %lld < max_pages %d",
                 (long long)d->page_table_stride, d->max_pages);
-  if (!(d->sm_scale >= 0.0f) || !std::isfinite(d->sm_scale) || !std::isfinite(d->q_scale) ||
-      !std::isfinite(d->k_scale) || !std::isfinite(d->v_scale))
-    return fail(MSA_ERR_INVALID_ARG, "scales must be finite (sm_scale >= 0)");
+  if (!(d->sm_scale >= 0.0f) || !std::isfinite(d->sm_scale) || !(d->q_scale > 0.0f) ||
+      !std::isfinite(d->q_scale) || !(d->k_scale > 0.0f) || !std::isfinite(d->k_scale) ||
+      !std::isfinite(d->v_scale))
+    return fail(MSA_ERR_INVALID_ARG, "scales must be finite, sm_scale >= 0, q_scale and k_scale > 0");
   if (d->head_dim_qk < 1 || d->head_dim_v < 1)
     return fail(MSA_ERR_INVALID_ARG, "bad head dims");
   const void *need[] = {d->q, d->q_seq, d->q_pos, d->seq_lens, d->k_cache, d->v_cache,
@@ -140,7 +142,7 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
   r.num_slots = d->num_slots;
   r.max_pages = d->max_pages;
   r.num_phys_pages = d->num_phys_pages;
-  r.chunk = (kPageRouteRowsPerUnit + r.G - 1) / r.G;
+  r.chunk = std::min(kMaxChunk, (kPageRouteRowsPerUnit + r.G - 1) / r.G);
   r.route = route;
   const float sm = d->sm_scale > 0.0f ? d->sm_scale : 1.0f / std::sqrt((float)d->head_dim_qk);
   r.scale_log2 = (float)((double)sm * d->q_scale * d->k_scale * 1.4426950408889634);

@@ -32,6 +32,9 @@
 //   Q8KV4 : e4m3 / nvfp4 -> NVFP4 dequantised once per page to E4M3 (exact
 //           product, one rounding; section "Build the prefill for SM107"),
 //           QK 16x16x32 fp8, V E4M3 -> FP16 (exact), PV 16x16x32 f16
+#include <type_traits>
+#include <utility>
+
 #include "launch.h"
 
 namespace msa {
@@ -69,7 +72,9 @@ template <int ROUTE, int D> struct Geom {
   static constexpr int K_BYTES = PAGE * RB;
   static constexpr int VROW_F32 = D * 4 + 16;  // padded V row (FP32 route)
   static constexpr int V_BYTES = RouteInfo<ROUTE>::F16PV ? D * PAGE * 2 : PAGE * VROW_F32;
-  static constexpr int LDS = K_BYTES + V_BYTES + 64;
+  static constexpr int QPF = ROUTE == kRouteF32 ? 1 : (LANE_CH <= 2 ? 3 : 2);  // Q prefetch depth (tiles)
+  static constexpr int ENT_BYTES = kMaxChunk * (int)sizeof(PlanEntry);  // the unit's entries
+  static constexpr int LDS = K_BYTES + V_BYTES + 64 + ENT_BYTES;
 };
 
 // Byte offset of 16-byte chunk c of K row `key`: XOR swizzle so that the 16
@@ -83,6 +88,12 @@ template <int ROUTE, int D> __device__ __forceinline__ int k_off(int key, int c)
 __device__ __forceinline__ int vt_off(int dv, int c) { return dv * (PAGE * 2) + ((c ^ (dv & 15)) << 4); }
 
 template <typename T> __device__ __forceinline__ T ld(const void *p) { return *(const T *)p; }
+
+// f(integral_constant<J>) for J = 0 .. N-1, unrolled at compile time.
+template <typename F, int... Js>
+__device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int, Js...>) {
+  (f(std::integral_constant<int, Js>{}), ...);
+}
 
 // ------------------------------------------------------------ page loading
 
@@ -178,7 +189,9 @@ __device__ __forceinline__ float load_page_float(const PageArgs &a, int phys, in
   }
 }
 
-// Q8KV4: NVFP4 K/V dequantised to E4M3 once per page.
+// Q8KV4: NVFP4 K/V dequantised to E4M3 once per page, through per-block
+// magnitude tables (see nvfp4_mag_table): K stays E4M3 for the FP8 QK
+// product, V becomes FP16 (exact) and is stored transposed for PV.
 template <int D>
 __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int g, uint8_t *sK,
                                                 uint8_t *sV) {
@@ -186,44 +199,70 @@ __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int
   const int tid = threadIdx.x;
   const int64_t kvo = (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
   const int64_t sfo = (int64_t)phys * a.sf_stride_page + (int64_t)g * a.sf_stride_head;
-  {  // K: thread -> key tid/2, half tid%2 of the row (64 elements)
+  // V first: its loads are issued before K's conversion work.
+  const int kp = tid & 63, db = tid >> 6;  // key pair, block of 32 dims
+  u32x4 vcw[2];
+  uint32_t vsf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int key = 2 * kp + kk;
+    vcw[kk] = ld<u32x4>(a.v_cache + kvo + key * a.kv_stride_tok + db * 16);
+    vsf[kk] = ld<uint16_t>(a.v_sf + sfo + key * a.sf_stride_tok + db * 2);
+  }
+  {  // K: thread -> key tid/2, half tid%2 of the row (64 elements = 4 blocks)
     const int key = tid >> 1, half = tid & 1;
     const uint8_t *cp = a.k_cache + kvo + key * a.kv_stride_tok + half * (D / 4);
     const uint32_t sf = ld<uint32_t>(a.k_sf + sfo + key * a.sf_stride_tok + half * (D / 32));
     const u32x4 c0 = ld<u32x4>(cp), c1 = ld<u32x4>(cp + 16);
     const uint32_t words[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {  // 16 output bytes = 2 code words = one scale
+    for (int ch = 0; ch < 4; ++ch) {  // one block: 16 codes -> 16 output bytes
       const uint32_t scale = (sf >> (8 * ch)) & 0xffu;
+      const u32x2 tab = nvfp4_mag_table(scale);
+      const uint32_t flip = (scale & 0x80u) ? 0x80808080u : 0u;
       u32x4 out;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t cw = words[ch * 2 + (w >> 1)] >> (16 * (w & 1));
-        uint32_t o = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o |= nvfp4_to_e4m3((cw >> (4 * i)) & 15u, scale) << (8 * i);
-        out[w] = o;
-      }
+      for (int w = 0; w < 4; ++w)
+        out[w] = nvfp4_lookup4(words[ch * 2 + (w >> 1)] >> (16 * (w & 1)), tab, flip);
       *(u32x4 *)(sK + k_off<kRouteQ8KV4, D>(key, half * 4 + ch)) = out;
     }
   }
-  {  // V: thread -> key pair kp, d block db of 32 elements; written as V^T FP16
-    const int kp = tid & 63, db = tid >> 6;
+  // V: per key, FP16 pairs (dims 2i, 2i+1) of the 32 dims of block db
+  uint32_t hw[2][16];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int key = 2 * kp + kk;
-      const uint8_t *cp = a.v_cache + kvo + key * a.kv_stride_tok + db * 16;
-      const u32x4 cw4 = ld<u32x4>(cp);
-      const uint32_t sf = ld<uint16_t>(a.v_sf + sfo + key * a.sf_stride_tok + db * 2);
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const uint32_t code = (cw4[e >> 3] >> (4 * (e & 7))) & 15u;
-        const uint32_t scale = (sf >> (8 * (e >> 4))) & 0xffu;
-        const _Float16 hv = (_Float16)e4m3_to_f32(nvfp4_to_e4m3(code, scale));
-        const int dv = db * 32 + e;
-        *(_Float16 *)(sV + vt_off(dv, kp >> 2) + ((kp & 3) << 2) + kk * 2) = hv;
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t scale = (vsf[kk] >> (8 * b)) & 0xffu;
+      const u32x2 tab = nvfp4_mag_table(scale);
+      // FP16 magnitude table, split into its low and high bytes
+      uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        const uint32_t f = e4m3_mag_to_f16_bits((tab[c >> 2] >> (8 * (c & 3))) & 0xffu);
+        lo[c >> 2] |= (f & 0xffu) << (8 * (c & 3));
+        hi[c >> 2] |= (f >> 8) << (8 * (c & 3));
+      }
+      const uint32_t flip = (scale & 0x80u) ? 0x80008000u : 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // 4 codes -> two FP16 pairs
+        const uint32_t sp = spread_nibbles((vcw[kk][b * 2 + (q >> 1)] >> (16 * (q & 1))) & 0xffffu);
+        const uint32_t sel = sp & 0x07070707u, sg = sp & 0x08080808u;
+        const uint32_t L = __builtin_amdgcn_perm(lo[1], lo[0], sel);
+        const uint32_t H = __builtin_amdgcn_perm(hi[1], hi[0], sel);
+        const uint32_t p01 = __builtin_amdgcn_perm(H, L, 0x05010400u) | ((sg & 0x8u) << 12) | ((sg & 0x800u) << 20);
+        const uint32_t p23 = __builtin_amdgcn_perm(H, L, 0x07030602u) | ((sg & 0x80000u) >> 4) | ((sg & 0x8000000u) << 4);
+        hw[kk][b * 8 + q * 2] = p01 ^ flip;
+        hw[kk][b * 8 + q * 2 + 1] = p23 ^ flip;
       }
     }
+  // V^T rows dv, dv+1 get the (key 2kp, key 2kp+1) pairs
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int dv = db * 32 + 2 * i;
+    const int col = ((kp & 3) << 2);
+    *(uint32_t *)(sV + vt_off(dv, kp >> 2) + col) = __builtin_amdgcn_perm(hw[1][i], hw[0][i], 0x05040100u);
+    *(uint32_t *)(sV + vt_off(dv + 1, kp >> 2) + col) = __builtin_amdgcn_perm(hw[1][i], hw[0][i], 0x07060302u);
   }
 }
 
@@ -237,6 +276,7 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
   uint8_t *sK = smem;
   uint8_t *sV = smem + Gm::K_BYTES;
   float *sRed = (float *)(smem + Gm::K_BYTES + Gm::V_BYTES);
+  PlanEntry *sEnt = (PlanEntry *)(smem + Gm::K_BYTES + Gm::V_BYTES + 64);
 
   // ---- work unit (XCD-aware: consecutive units stay on one XCD's L2)
   const int32_t *meta = (const int32_t *)(a.ws + a.lay.meta);
@@ -262,6 +302,13 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
   const int b = list / (a.Hkv * a.max_pages);
   const int phys = a.page_table[b * a.pt_stride + u];
 
+  // ---- the unit's entries -> LDS (so the tile loop issues no dependent
+  // global loads behind its own stores: vmcnt counts loads and stores alike)
+  {
+    const PlanEntry *ge = (const PlanEntry *)(a.ws + a.lay.entries) + e_begin;
+    for (int i = threadIdx.x; i < e_count; i += THREADS) sEnt[i] = ge[i];
+  }
+
   // ---- page -> LDS
   float vfac = 1.0f;
   if constexpr (ROUTE == kRouteQ8KV4) load_page_nvfp4<D>(a, phys, g, sK, sV);
@@ -269,8 +316,10 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
   __syncthreads();
   const float out_scale = a.v_scale * vfac;
 
-  const PlanEntry *entries = (const PlanEntry *)(a.ws + a.lay.entries) + e_begin;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const PlanEntry *entries = sEnt;
+  float *dump = (float *)(a.ws + a.lay.dump);  // scratch row for masked-off stores
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int n = lane & 15, grp = lane >> 4;
   const int G = a.G;
   const int rows_total = e_count * G;
@@ -305,18 +354,38 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
     for (int c = 0; c < Gm::LANE_CH; ++c) q[c] = ld<u32x4>(qp + c * 16);
   };
 
-  RowInfo cur = row_of(wave);
-  u32x4 qreg[Gm::LANE_CH];
-  load_q(cur, qreg);
+  // ---- software pipeline: the Q fragments of the next QPF tiles are in
+  // flight while a tile is computed.  Each prefetch in the prologue is
+  // followed by one tile's worth of (scratch) stores so that the memory-op
+  // pattern at loop entry matches the back-edge: the compiler's wait before
+  // a tile's MFMAs then covers its own Q loads only, never the partial-output
+  // stores still in flight.
+  constexpr int PF = Gm::QPF;
+  constexpr int MT = D / 16;
+  RowInfo ri[PF];
+  u32x4 qb[PF][Gm::LANE_CH];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    ri[f] = row_of(wave + f * NWAVES);
+    load_q(ri[f], qb[f]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) *(f32x4 *)(dump + grp * 4 + mt * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+    dump[D + lane] = 0.0f;
+  }
+  const float sc = a.scale_log2;  // > 0 (validated on the host)
 
-  for (int tile = wave; tile < n_tiles; tile += NWAVES) {
+  // One tile; J (compile-time) names the prefetch buffer holding its Q.
+  // The loop below is unrolled PF times so each buffer is consumed by its
+  // QK and refilled in place -- rotating buffers through register moves
+  // would wait on loads still in flight.
+  auto step = [&](auto J_, const int tile) {
+#pragma clang fp contract(off)
+    constexpr int J = decltype(J_)::value;
     // The page in LDS is loop-invariant; without this compiler-only fence the
     // K/V fragment reads are hoisted out of the loop into (spilled) registers.
     __asm__ volatile("" ::: "memory");
-    const RowInfo nxt = row_of(tile + NWAVES);  // software pipeline: next entry
-    const int tok = cur.tok, slot = cur.slot, limit = cur.limit, h = cur.h;
-    const bool active = cur.active;
-
+    const int tok = ri[J].tok, slot = ri[J].slot, limit = ri[J].limit, h = ri[J].h;
+    const bool active = ri[J].active;
     // ---- S^T = K Q^T  (chunk-outer so each K fragment is used once, at once)
     f32x4 acc[NT];
 #pragma unroll
@@ -326,58 +395,69 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const u32x4 kr = *(const u32x4 *)(sK + k_off<ROUTE, D>(key_of<ROUTE>(t, n), grp * Gm::LANE_CH + c));
+        const u32x4 qr = qb[J][c];
         if constexpr (ROUTE == kRouteF32) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) acc[t] = mfma_f32(__uint_as_float(kr[w]), __uint_as_float(qreg[c][w]), acc[t]);
+          for (int w = 0; w < 4; ++w) acc[t] = mfma_f32(__uint_as_float(kr[w]), __uint_as_float(qr[w]), acc[t]);
         } else if constexpr (ROUTE == kRouteBF16) {
-          acc[t] = mfma_bf16(kr, qreg[c], acc[t]);
+          acc[t] = mfma_bf16(kr, qr, acc[t]);
         } else if constexpr (ROUTE == kRouteF16) {
-          acc[t] = mfma_f16(kr, qreg[c], acc[t]);
+          acc[t] = mfma_f16(kr, qr, acc[t]);
         } else {
-          acc[t] = mfma_fp8(u32x2{kr[0], kr[1]}, u32x2{qreg[c][0], qreg[c][1]}, acc[t]);
-          acc[t] = mfma_fp8(u32x2{kr[2], kr[3]}, u32x2{qreg[c][2], qreg[c][3]}, acc[t]);
+          acc[t] = mfma_fp8(u32x2{kr[0], kr[1]}, u32x2{qr[0], qr[1]}, acc[t]);
+          acc[t] = mfma_fp8(u32x2{kr[2], kr[3]}, u32x2{qr[2], qr[3]}, acc[t]);
         }
       }
     }
 
-    // ---- issue the next tile's Q loads; they land during softmax/PV/epilogue
-    u32x4 qnext[Gm::LANE_CH];
-    load_q(nxt, qnext);
+    // ---- prefetch tile + PF * NWAVES (inactive, in-bounds rows past the end)
+    ri[J] = row_of(tile + PF * NWAVES);
+    load_q(ri[J], qb[J]);
 
-    // ---- scale (log2 domain), mask, row max
-    const bool full = __all(limit >= PAGE - 1);
+    // ---- causal mask, only for tiles where some row sees part of the page
+    // (a wave-uniform branch; history pages and most own-page tiles skip it)
+    if (!__all(limit >= PAGE - 1)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key_of<ROUTE>(t, 4 * grp + i) > limit) acc[t][i] = -INFINITY;
+    }
+    // ---- scores in log2 units and their row max.  Scaling before the max
+    // keeps the largest key's weight exactly 1 (a single visible key then
+    // reproduces its value row bit for bit) -- provided the product is
+    // rounded before the subtraction, hence no FMA contraction in this step.
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = acc[t][i] * a.scale_log2;
-        if (!full && key_of<ROUTE>(t, 4 * grp + i) > limit) x = -INFINITY;
-        acc[t][i] = x;
-        m = fmaxf(m, x);
-      }
+      for (int i = 0; i < 4; ++i) acc[t][i] *= sc;
+      m = fmaxf(m, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
+    }
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
-    if (m == -INFINITY) m = 0.0f;  // inactive row: keep the arithmetic finite
+    const float msc = (m == -INFINITY) ? 0.0f : m;  // inactive row: stay finite
 
     // ---- P = exp2(S - m).  l (exact FP32 sum) gives the LSE; lp, the sum of
-    // the P values the PV product actually uses, normalises the output so
-    // that its weights sum to one.
+    // the P values PV actually uses, normalises the output so that its
+    // weights sum to one.
     float l = 0.0f, lp = 0.0f;
+    uint32_t pk[NT * 2];  // FP16 pairs of P (16-bit PV routes)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(acc[t][i] - m);
+        const float p = __builtin_amdgcn_exp2f(acc[t][i] - msc);
+        acc[t][i] = p;
         l += p;
-        if constexpr (RouteInfo<ROUTE>::F16PV) {
-          const float pr = (float)(_Float16)p;
-          acc[t][i] = pr;
-          lp += pr;
-        } else {
-          acc[t][i] = p;
-        }
       }
+      if constexpr (RouteInfo<ROUTE>::F16PV) {
+        pk[2 * t] = pack_f16x2(acc[t][0], acc[t][1]);
+        pk[2 * t + 1] = pack_f16x2(acc[t][2], acc[t][3]);
+        lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2 * t]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
+        lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2 * t + 1]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
+      }
+    }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if constexpr (RouteInfo<ROUTE>::F16PV) {
@@ -388,19 +468,15 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
     }
 
     // ---- O^T = V^T P^T
-    f32x4 o[D / 16];
+    f32x4 o[MT];
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (RouteInfo<ROUTE>::F16PV) {
 #pragma unroll
       for (int kb = 0; kb < PAGE / 32; ++kb) {
-        u32x4 pf;
-        pf[0] = pack_f16x2(acc[2 * kb][0], acc[2 * kb][1]);
-        pf[1] = pack_f16x2(acc[2 * kb][2], acc[2 * kb][3]);
-        pf[2] = pack_f16x2(acc[2 * kb + 1][0], acc[2 * kb + 1][1]);
-        pf[3] = pack_f16x2(acc[2 * kb + 1][2], acc[2 * kb + 1][3]);
+        const u32x4 pf = {pk[4 * kb], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
           const u32x4 vf = *(const u32x4 *)(sV + vt_off(mt * 16 + n, kb * 4 + grp));
           o[mt] = mfma_f16(vf, pf, o[mt]);
         }
@@ -412,30 +488,40 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
         for (int i = 0; i < 4; ++i) {
           const int key = t * 16 + 4 * grp + i;
 #pragma unroll
-          for (int mt = 0; mt < D / 16; ++mt) {
+          for (int mt = 0; mt < MT; ++mt) {
             const float vv = *(const float *)(sV + key * Gm::VROW_F32 + (mt * 16 + n) * 4);
             o[mt] = mfma_f32(vv, acc[t][i], o[mt]);
           }
         }
     }
 
-    // ---- epilogue: this lane holds row n, columns 16*mt + 4*grp + [0,4)
-    if (active) {
-      const float inv = out_scale / lp;
-      const int64_t row = (int64_t)tok * a.Hq + h;
-      float *dst = a.partial_o + (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4;
+    // ---- epilogue: this lane holds row n, columns 16*mt + 4*grp + [0,4).
+    // The stores are unconditional -- rows without a destination (ragged
+    // last tile; the LSE of lanes other than the row's first) write to a
+    // scratch row of the workspace -- so the compiler can count the stores
+    // in flight across the loop back-edge.
+    const float inv = out_scale / lp;  // IEEE division (v_rcp_f32 is not exact even at 1.0)
+    const int64_t row = (int64_t)tok * a.Hq + h;
+    float *dst = active ? a.partial_o + (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4
+                        : dump + grp * 4;
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) {
-        f32x4 v = o[mt] * inv;
-        *(f32x4 *)(dst + mt * 16) = v;
-      }
-      if (grp == 0)
-        a.partial_lse[(int64_t)slot * a.pl_split_stride + row] =
-            (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    for (int mt = 0; mt < MT; ++mt) *(f32x4 *)(dst + mt * 16) = o[mt] * inv;
+    float *ldst = (active && grp == 0) ? a.partial_lse + (int64_t)slot * a.pl_split_stride + row
+                                       : dump + D + lane;
+    *ldst = (msc + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+  };
+
+  if (wave < n_tiles) {
+    for (int tile = wave;;) {
+      bool done = false;  // wave-uniform
+      for_each_index([&](auto J) {
+        if (!done) {
+          step(J, tile);
+          done = (tile += NWAVES) >= n_tiles;
+        }
+      }, std::make_integer_sequence<int, PF>{});
+      if (done) break;
     }
-    cur = nxt;
-#pragma unroll
-    for (int c = 0; c < Gm::LANE_CH; ++c) qreg[c] = qnext[c];
   }
 }
 

@@ -82,11 +82,58 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
-// NVFP4 element: E2M1 code x E4M3 scale, rounded once to E4M3.  The float
-// product is exact (at most 6 significant bits), so the single rounding is
-// the conversion.
+// |x| -> E4M3 magnitude code without branches: round to nearest even at the
+// 3-bit mantissa (normal range, |x| >= 2^-6) or on the 2^-9 grid (subnormal
+// range), saturating at 448 (0x7E).  `ax` must be finite and >= 0.
+__device__ __forceinline__ uint32_t e4m3_mag_rne(float ax) {
+  const uint32_t a = __float_as_uint(ax);
+  const uint32_t cn = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t cs = (uint32_t)__builtin_rintf(ax * 512.0f);
+  return min(a < 0x3c800000u ? cs : cn, 0x7eu);
+}
+
+// NVFP4 dequantisation (MiniMax-AI/MSA PR 21, section "Build the prefill for
+// SM107"): an element is its E2M1 code times its block's E4M3 scale, rounded
+// once to E4M3 (the float product is exact: at most 6 significant bits).
+// Rounding is symmetric, so a block needs only the 8 magnitudes
+// |e2m1(c)| * |scale|, c = 0..7; an element's byte is its magnitude with the
+// sign bit XOR-ed from the code and the scale (an IEEE product's sign, which
+// also gives the sign of zero).
+//
+// nvfp4_mag_table: the 8 magnitude bytes, byte c of the 8-byte pair.
+__device__ __forceinline__ u32x2 nvfp4_mag_table(uint32_t scale) {
+  const float s = e4m3_to_f32(scale & 0x7fu);
+  const uint32_t m1 = e4m3_mag_rne(0.5f * s), m2 = e4m3_mag_rne(s), m3 = e4m3_mag_rne(1.5f * s);
+  const uint32_t m4 = e4m3_mag_rne(2.0f * s), m5 = e4m3_mag_rne(3.0f * s);
+  const uint32_t m6 = e4m3_mag_rne(4.0f * s), m7 = e4m3_mag_rne(6.0f * s);
+  return u32x2{(m1 << 8) | (m2 << 16) | (m3 << 24), m4 | (m5 << 8) | (m6 << 16) | (m7 << 24)};
+}
+
+// Spread 4 nibbles (bits 4i..4i+3) to the low nibbles of 4 bytes.
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
+  return (x & 0xfu) | ((x & 0xf0u) << 4) | ((x & 0xf00u) << 8) | ((x & 0xf000u) << 12);
+}
+
+// Four E4M3 bytes (byte i) of the four codes in the low 16 bits of `codes`
+// (element i in bits 4i..4i+3), all sharing one block scale.
+// `sign_flip` = 0x80808080 if the scale is negative, else 0.
+__device__ __forceinline__ uint32_t nvfp4_lookup4(uint32_t codes, u32x2 tab, uint32_t sign_flip) {
+  const uint32_t sp = spread_nibbles(codes & 0xffffu);
+  const uint32_t mags = __builtin_amdgcn_perm(tab[1], tab[0], sp & 0x07070707u);
+  return (mags | ((sp & 0x08080808u) << 4)) ^ sign_flip;
+}
+
+// E4M3 magnitude byte -> FP16 bits (exact: every E4M3 value is an FP16 value).
+__device__ __forceinline__ uint32_t e4m3_mag_to_f16_bits(uint32_t b) {
+  const uint32_t e = b >> 3, m = b & 7u;
+  const uint32_t normal = ((e + 8u) << 10) | (m << 7);
+  const uint32_t sub = __builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
+  return e ? normal : sub;
+}
+
+// Single-element form (standalone dequantisation entry point; same tables).
 __device__ __forceinline__ uint32_t nvfp4_to_e4m3(uint32_t code, uint32_t scale) {
-  return f32_to_e4m3(e2m1_to_f32(code) * e4m3_to_f32(scale));
+  return nvfp4_lookup4(code & 15u, nvfp4_mag_table(scale), (scale & 0x80u) ? 0x80808080u : 0u) & 0xffu;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -120,7 +167,7 @@ struct PlanEntry {
 struct PageLayout {
   int64_t num_lists;     // num_seqs * max_pages * Hkv
   int64_t num_sel;       // total_q * Hkv * num_slots
-  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, meta, total;
+  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, meta, dump, total;
 };
 
 __host__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -131,6 +178,7 @@ __host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel) {
   L.num_sel = num_sel;
   size_t off = 0;
   L.meta = off;      off = align_up(off + 64 * 4, 256);
+  L.dump = off;      off = align_up(off + 1024 * 4, 256);  // scratch for masked-off stores
   L.counts = off;    off = align_up(off + (size_t)num_lists * 4, 256);
   L.list_off = off;  off = align_up(off + (size_t)(num_lists + 1) * 4, 256);
   L.unit_off = off;  off = align_up(off + (size_t)(num_lists + 1) * 4, 256);

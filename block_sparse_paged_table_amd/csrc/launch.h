@@ -9,6 +9,8 @@
 
 namespace msa {
 
+constexpr int kMaxChunk = 256;  // entries per work unit (upper bound)
+
 enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3 };
 
 // Resolved arguments of the page-selection route.
