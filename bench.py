@@ -45,10 +45,15 @@ def workload_stats(p):
     sm = p.sel_mask.numpy()
     start = si * p.unit_tokens
     vis = np.clip(last[:, None, None] - start + 1, 0, p.unit_tokens)
+    if p.unit_tokens != p.page_size:  # microblocks: count the mask bits in the visible prefix
+        prefix = (1 << vis) - 1
+        bits = (sm.astype(np.int64) & prefix)
+        vis = sum((bits >> i) & 1 for i in range(p.unit_tokens))
     vis = np.where((sm != 0) & (si >= 0), vis, 0)
     G = p.Hq // p.Hkv
     n_vis = int(vis.sum()) * G                      # (row, key) pairs
-    nonempty = int((vis > 0).sum()) * G              # (row, split) partials written
+    per_split = vis.reshape(vis.shape[0], vis.shape[1], p.num_splits, p.slots_per_split).sum(-1)
+    nonempty = int((per_split > 0).sum()) * G        # (row, split) partials written
     return dict(n_visible=n_vis, nonempty=nonempty,
                 flops=4.0 * p.d_qk * n_vis if p.d_qk == p.d_v else 2.0 * (p.d_qk + p.d_v) * n_vis)
 
@@ -96,6 +101,9 @@ def main():
     probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i) for i in range(args.sets)]
     p0 = probs[0]
     st = workload_stats(p0)
+    for p in probs[1:]:  # rotated sets share the output buffers: same geometry only
+        assert (p.total_q, p.num_rows, p.num_splits, p.d_v) == \
+            (p0.total_q, p0.num_rows, p0.num_splits, p0.d_v), "input sets differ in shape"
     # one partial buffer / output shared by all sets (the biggest allocations)
     dps = [DeviceProblem(probs[0])]
     for p in probs[1:]:

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "grouped.h"
 #include "launch.h"
 
 using namespace msa;
@@ -53,9 +54,77 @@ int page_route(const msa_prefill_desc *d) {
   return -1;
 }
 
+// Grouped microblock route (4-token units with per-row bit masks, one split).
+msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
+  if (d->unit_tokens != 4 || d->page_size % 4)
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route needs unit_tokens 4 and page_size %% 4 == 0");
+  if (d->slots_per_split != d->num_slots)
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route writes one split (slots_per_split == num_slots)");
+  if (d->num_slots > 512) return fail(MSA_ERR_UNSUPPORTED, "microblock route: at most 512 slots");
+  if (d->q_dtype != MSA_F16 || d->kv_dtype != MSA_F16)
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route is built for FP16 Q and KV");
+  if (d->head_dim_qk != d->head_dim_v || (d->head_dim_qk != 128 && d->head_dim_qk != 256))
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route needs head_dim 128 or 256 (qk == v)");
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G > 8) return fail(MSA_ERR_UNSUPPORTED, "microblock route: at most 8 query heads per KV head");
+  if (d->num_seqs >= (1 << 16) || (int64_t)d->max_pages * d->page_size / 4 >= (1ll << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route: too many requests or units");
+  if (!aligned(d->q, 16) || (d->q_stride_tok * 2) % 16 || (d->q_stride_head * 2) % 16 ||
+      d->q_stride_head < 0 || d->q_stride_tok < 0)
+    return fail(MSA_ERR_INVALID_ARG, "q must be 16-byte aligned with 16-byte aligned strides");
+  if (!aligned(d->k_cache, 16) || !aligned(d->v_cache, 16) || d->kv_stride_page_bytes % 16 ||
+      d->kv_stride_tok_bytes % 16 || d->kv_stride_head_bytes % 16)
+    return fail(MSA_ERR_INVALID_ARG, "k/v cache and strides must be 16-byte aligned");
+  if (!aligned(d->partial_o, 16) || d->po_row_stride % 4 || d->po_row_stride < d->head_dim_v)
+    return fail(MSA_ERR_INVALID_ARG, "partial_o must be 16-byte aligned, row stride >= head_dim_v");
+  if (!aligned(d->partial_lse, 4)) return fail(MSA_ERR_INVALID_ARG, "partial_lse misaligned");
+  GroupArgs &r = *a;
+  memset(&r, 0, sizeof(r));
+  r.num_seqs = d->num_seqs;
+  r.total_q = d->total_q;
+  r.Hq = d->num_q_heads;
+  r.Hkv = d->num_kv_heads;
+  r.G = G;
+  r.D = d->head_dim_qk;
+  r.page_size = d->page_size;
+  r.unit_tokens = d->unit_tokens;
+  r.num_slots = d->num_slots;
+  r.max_pages = d->max_pages;
+  r.num_phys_pages = d->num_phys_pages;
+  r.num_groups = (d->total_q + kGroupTokens - 1) / kGroupTokens;
+  r.list_cap = kGroupTokens * d->num_slots;
+  r.sort_n = kGPlanThreads;
+  while (r.sort_n < r.list_cap) r.sort_n <<= 1;
+  const float sm = d->sm_scale > 0.0f ? d->sm_scale : 1.0f / std::sqrt((float)d->head_dim_qk);
+  r.scale_log2 = (float)((double)sm * d->q_scale * d->k_scale * 1.4426950408889634);
+  r.v_scale = d->v_scale;
+  r.q = d->q;
+  r.q_stride_tok = d->q_stride_tok;
+  r.q_stride_head = d->q_stride_head;
+  r.q_seq = d->q_seq;
+  r.q_pos = d->q_pos;
+  r.seq_lens = d->seq_lens;
+  r.k_cache = (const uint8_t *)d->k_cache;
+  r.v_cache = (const uint8_t *)d->v_cache;
+  r.kv_stride_page = d->kv_stride_page_bytes;
+  r.kv_stride_tok = d->kv_stride_tok_bytes;
+  r.kv_stride_head = d->kv_stride_head_bytes;
+  r.page_table = d->page_table;
+  r.pt_stride = d->page_table_stride;
+  r.sel_idx = d->sel_idx;
+  r.sel_mask = d->sel_mask;
+  r.sel_stride_tok = d->sel_stride_tok;
+  r.sel_stride_head = d->sel_stride_head;
+  r.partial_o = d->partial_o;
+  r.po_row_stride = d->po_row_stride;
+  r.partial_lse = d->partial_lse;
+  r.lay = group_layout((int64_t)r.num_groups * r.Hkv, r.list_cap);
+  return MSA_OK;
+}
+
 // Host checks shared by every prefill entry point.  On success fills the
-// resolved arguments (without workspace pointers).
-msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
+// resolved arguments of the route (without workspace pointers).
+msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, bool *grouped) {
   if (!d) return fail(MSA_ERR_INVALID_ARG, "descriptor is NULL");
   if (d->struct_size != sizeof(msa_prefill_desc))
     return fail(MSA_ERR_INVALID_ARG, "struct_size %u != %zu (ABI mismatch)", d->struct_size,
@@ -92,10 +161,12 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
       (int64_t)d->total_q * d->num_q_heads >= (1ll << 31) || d->total_q >= (1 << 23))
     return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit plan indices");
 
-  // ---- route selection: page selections only in this build
-  if (d->unit_tokens != d->page_size)
-    return fail(MSA_ERR_UNSUPPORTED, "microblock selections (unit_tokens %d < page_size %d) "
-                "are not supported by this build", d->unit_tokens, d->page_size);
+  // ---- microblock selections take the grouped route
+  if (d->unit_tokens != d->page_size) {
+    *grouped = true;
+    return resolve_grouped(d, ga);
+  }
+  *grouped = false;
   const int route = page_route(d);
   if (route < 0)
     return fail(MSA_ERR_UNSUPPORTED, "dtype pair q %d / kv %d unsupported", d->q_dtype, d->kv_dtype);
@@ -183,13 +254,32 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a) {
   return MSA_OK;
 }
 
-msa_status bind_workspace(PageArgs *a, const msa_prefill_desc *d, void *ws, size_t bytes) {
-  if (bytes < a->lay.total)
-    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", bytes, a->lay.total);
+// Validated arguments of one call, for whichever route the descriptor takes.
+struct Resolved {
+  bool grouped;
+  PageArgs pa;
+  GroupArgs ga;
+  size_t ws_bytes() const { return grouped ? ga.lay.total : pa.lay.total; }
+};
+
+msa_status resolve(const msa_prefill_desc *d, Resolved *r) {
+  return check_desc(d, &r->pa, &r->ga, &r->grouped);
+}
+
+msa_status bind_workspace(Resolved *r, const msa_prefill_desc *d, void *ws, size_t bytes) {
+  const size_t need = r->ws_bytes();
+  if (bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", bytes, need);
   if (!ws) return fail(MSA_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  a->ws = (uint8_t *)ws;
-  a->err_flags = d->err_flags ? d->err_flags : (uint32_t *)(a->ws + a->lay.meta) + 1;
+  uint8_t *w = (uint8_t *)ws;
+  if (r->grouped) {
+    r->ga.ws = w;
+    r->ga.err_flags = d->err_flags ? d->err_flags : (uint32_t *)(w + r->ga.lay.meta) + 1;
+  } else {
+    r->pa.ws = w;
+    r->pa.err_flags = d->err_flags ? d->err_flags : (uint32_t *)(w + r->pa.lay.meta) + 1;
+  }
   return MSA_OK;
 }
 
@@ -204,27 +294,29 @@ extern "C" {
 
 msa_status msa_prefill_workspace_bytes(const msa_prefill_desc *d, size_t *bytes) {
   if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
-  PageArgs a;
-  msa_status s = check_desc(d, &a);
+  Resolved r;
+  msa_status s = resolve(d, &r);
   if (s != MSA_OK) return s;
-  *bytes = a.lay.total;
+  *bytes = r.ws_bytes();
   return ok();
 }
 
 msa_status msa_prefill_plan(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
-  PageArgs a;
-  msa_status s = check_desc(d, &a);
+  Resolved r;
+  msa_status s = resolve(d, &r);
   if (s != MSA_OK) return s;
-  if ((s = bind_workspace(&a, d, ws, ws_bytes)) != MSA_OK) return s;
-  return hip_status(launch_page_plan(a, (hipStream_t)stream), "plan launch");
+  if ((s = bind_workspace(&r, d, ws, ws_bytes)) != MSA_OK) return s;
+  if (r.grouped) return hip_status(launch_grouped_plan(r.ga, (hipStream_t)stream), "plan launch");
+  return hip_status(launch_page_plan(r.pa, (hipStream_t)stream), "plan launch");
 }
 
 msa_status msa_prefill_attend(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
-  PageArgs a;
-  msa_status s = check_desc(d, &a);
+  Resolved r;
+  msa_status s = resolve(d, &r);
   if (s != MSA_OK) return s;
-  if ((s = bind_workspace(&a, d, ws, ws_bytes)) != MSA_OK) return s;
-  return hip_status(launch_page_attend(a, (hipStream_t)stream), "attention launch");
+  if ((s = bind_workspace(&r, d, ws, ws_bytes)) != MSA_OK) return s;
+  if (r.grouped) return hip_status(launch_grouped_attend(r.ga, (hipStream_t)stream), "attention launch");
+  return hip_status(launch_page_attend(r.pa, (hipStream_t)stream), "attention launch");
 }
 
 msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {

@@ -1,0 +1,58 @@
+// Internal interface of the grouped microblock route (planner + attention).
+#pragma once
+
+#include "common.h"
+
+namespace msa {
+
+constexpr int kGroupTokens = 8;        // adjacent query tokens per group
+constexpr int kGPlanThreads = 256;
+constexpr int kGUnitsPerBatch = 8;     // microblocks per attention batch (32 keys)
+
+// Workspace of the grouped route.  Per (KV head, group): the number of
+// distinct units and a list of up to list_cap entries
+// {K/V byte offset (lo, hi), mask32, active row tiles}.
+struct GroupLayout {
+  size_t meta, counts, stage, lists, total;
+};
+
+__host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap) {
+  GroupLayout L;
+  size_t off = 0;
+  L.meta = off;   off = align_up(off + 64 * 4, 256);
+  L.counts = off; off = align_up(off + (size_t)num_lists * 4, 256);
+  L.stage = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
+  L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
+  L.total = off;
+  return L;
+}
+
+struct GroupArgs {
+  int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, unit_tokens, num_slots, max_pages,
+      num_phys_pages;
+  int32_t num_groups;  // ceil(total_q / kGroupTokens)
+  int32_t sort_n;      // power of two >= kGroupTokens * num_slots and >= kGPlanThreads
+  int32_t list_cap;    // kGroupTokens * num_slots
+  float scale_log2, v_scale;
+  const void *q;
+  int64_t q_stride_tok, q_stride_head;
+  const int32_t *q_seq, *q_pos, *seq_lens;
+  const uint8_t *k_cache, *v_cache;
+  int64_t kv_stride_page, kv_stride_tok, kv_stride_head;  // bytes
+  const int32_t *page_table;
+  int64_t pt_stride;
+  const int32_t *sel_idx;
+  const uint8_t *sel_mask;
+  int64_t sel_stride_tok, sel_stride_head;
+  float *partial_o;
+  int64_t po_row_stride;
+  float *partial_lse;
+  uint32_t *err_flags;
+  uint8_t *ws;
+  GroupLayout lay;
+};
+
+hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s);
+hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s);
+
+}  // namespace msa

@@ -57,6 +57,12 @@ class DeviceProblem:
             partial_o = torch.empty((S, rows, dv + po_row_pad), dtype=torch.float32, device=dev)
         if partial_lse is None:
             partial_lse = torch.empty((S, rows), dtype=torch.float32, device=dev)
+        # caller-provided buffers must hold every (split, row) the kernels write
+        if (partial_o.dim() != 3 or partial_o.shape[0] < S or partial_o.shape[1] < rows
+                or partial_o.shape[2] < dv or partial_o.dtype != torch.float32):
+            raise ValueError(f"partial_o {tuple(partial_o.shape)} too small for {(S, rows, dv)}")
+        if partial_lse.dim() != 2 or partial_lse.shape[0] < S or partial_lse.shape[1] < rows:
+            raise ValueError(f"partial_lse {tuple(partial_lse.shape)} too small for {(S, rows)}")
         self.partial_o = partial_o
         self.partial_lse = partial_lse
         self.out_dtype = out_dtype or p.out_dtype

@@ -335,7 +335,9 @@ def make_config(idx: int, seed: Optional[int] = None) -> Problem:
     if idx == 3:
         return make_grouped_page4(seed=seed)
     if idx == 4:
-        rng = np.random.default_rng(seed)
+        # request shapes come from a fixed shape seed, so input sets drawn with
+        # other seeds (rotated data) keep the same geometry
+        rng = np.random.default_rng(1004)
         chunks = rng.choice([128, 256, 512, 1024, 2048, 4096], size=8)
         ctx = rng.integers(8192, 131072, size=8, endpoint=True)
         return build_page_problem(

@@ -105,3 +105,28 @@ def test_status_strings():
     lib = msa.library()
     assert lib.msa_status_str(0) == b"MSA_OK"
     assert lib.msa_status_str(3) == b"MSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_runner_rejects_undersized_partial_buffers():
+    """Caller-owned partial buffers are sized by the caller; the harness checks
+    them before any descriptor is built (the library only sees pointers)."""
+    import torch
+    from block_sparse_paged_table_amd import synth
+    from block_sparse_paged_table_amd.runner import DeviceProblem
+    p = synth.make_config(0)
+    small = torch.empty((p.num_splits, p.num_rows - 1, p.d_v), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        DeviceProblem(p, device="cpu", partial_o=small)
+    with pytest.raises(ValueError):
+        DeviceProblem(p, device="cpu", partial_lse=torch.empty((p.num_splits, 3)))
+
+
+def test_rotated_input_sets_share_geometry():
+    """Benchmark input sets drawn with other seeds differ in data only."""
+    import numpy as np
+    from block_sparse_paged_table_amd import synth
+    for cfg in (0, 4):
+        a, b = synth.make_config(cfg), synth.make_config(cfg, seed=1000 + cfg + 100)
+        assert (a.total_q, a.num_rows, a.max_pages) == (b.total_q, b.num_rows, b.max_pages)
+        assert np.array_equal(a.seq_lens.numpy(), b.seq_lens.numpy())
+        assert not np.array_equal(a.sel_idx.numpy(), b.sel_idx.numpy())

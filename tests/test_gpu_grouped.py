@@ -1,0 +1,111 @@
+"""GPU parity of the grouped microblock route (4-token units with exact
+per-row masks, 8-token groups, one split) against the FP64 oracle, through
+the C ABI.  Tolerances are defined in tests/parity.py."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_paged_table_amd import synth
+from block_sparse_paged_table_amd.runner import DeviceProblem
+import oracle
+from parity import check_combined, check_partials, gpu_rows
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _mb(seed, **kw):
+    args = dict(name="mb", seed=seed, ctx_len=200, chunk_len=45, pad_rows=3, Hq=6, Hkv=1, d=256,
+                num_slots=48, page_size=16, spare_pages=3)
+    args.update(kw)
+    return synth.build_microblock_problem(**args)
+
+
+def _parity(p, out_dtype=None):
+    dp = DeviceProblem(p, out_dtype=out_dtype)
+    dp.run()
+    torch.cuda.synchronize()
+    ref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, ref)
+    check_combined(p, out, lse, ref, dp.out_dtype)
+    assert dp.err_flags() == ref["err"]
+    return dp
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(6, 1, 256), (6, 1, 128), (1, 1, 128), (2, 1, 256),
+                                      (8, 1, 128), (12, 2, 256), (3, 3, 128)])
+def test_grouped_small_all_rows(Hq, Hkv, d):
+    _parity(_mb(31, Hq=Hq, Hkv=Hkv, d=d))
+
+
+def test_grouped_contiguous_cache_and_f32_output():
+    _parity(_mb(32, interleaved=False), out_dtype="f32")
+
+
+def test_grouped_ragged_group_and_early_rows():
+    # 37 tokens: the last group is partial; the chunk starts at position 0, so
+    # early rows see few units and some see nothing but their own
+    _parity(_mb(33, ctx_len=0, chunk_len=37, pad_rows=0, num_slots=16))
+
+
+def test_grouped_errors_and_duplicates():
+    p = _mb(34, num_slots=24)
+    si, sm = p.sel_idx.numpy().copy(), p.sel_mask.numpy().copy()
+    si[2, 0, 5], sm[2, 0, 5] = 10 ** 6, 0xF                   # unit beyond the table
+    si[7, 0, 9], sm[7, 0, 9] = si[7, 0, 1], 0x3                 # duplicate unit, other bits
+    sm[11] = 0                                                   # row with no selection
+    pt = p.page_table.numpy().copy()
+    pt[0, 3] = p.num_phys_pages + 4                              # bad physical page
+    p = dataclasses.replace(p, sel_idx=torch.from_numpy(si), sel_mask=torch.from_numpy(sm),
+                            page_table=torch.from_numpy(pt))
+    dp = _parity(p)
+    assert dp.err_flags() & (1 | 8)
+
+
+def test_grouped_three_runs_bitwise_identical():
+    p = _mb(35)
+    dp = DeviceProblem(p)
+    snaps = []
+    for _ in range(3):
+        dp.partial_o.fill_(0)
+        dp.run()
+        torch.cuda.synchronize()
+        snaps.append((dp.partial_o.clone(), dp.partial_lse.clone(), dp.out.clone()))
+    for s in snaps[1:]:
+        assert all(torch.equal(x, y) for x, y in zip(snaps[0], s))
+
+
+def test_grouped_all_invalid_group_bitwise_zero():
+    p = _mb(36, chunk_len=16, pad_rows=8, num_slots=12)
+    sm = p.sel_mask.numpy().copy()
+    sm[0:8] = 0                                  # a whole group selects nothing
+    p = dataclasses.replace(p, sel_mask=torch.from_numpy(sm))
+    dp = _parity(p)
+    out = dp.out[: 8 * p.Hq].float().cpu().numpy()
+    assert np.all(out == 0.0) and not np.signbit(out).any()
+    assert torch.all(torch.isneginf(dp.lse[: 8 * p.Hq]))
+
+
+def test_grouped_full_size_config_sampled():
+    p = synth.make_config(3)
+    dp = DeviceProblem(p)
+    dp.run()
+    torch.cuda.synchronize()
+    assert dp.err_flags() == 0
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([[0, 1, 7, 8, 4095, 8119, 8120, 8191],
+                                     rng.choice(p.total_q, 40, replace=False)]))
+    ref = oracle.prefill_rows(p, toks)
+    po, pl, out, lse = gpu_rows(dp, toks)
+    check_partials(p, po, pl, ref)
+    check_combined(p, out, lse, ref, dp.out_dtype)
+    # padding rows: +0 output and lse = -inf
+    pad = np.nonzero(p.q_pos.numpy() < 0)[0]
+    rows = (pad[:, None] * p.Hq + np.arange(p.Hq)[None]).ravel()
+    o = dp.out[torch.as_tensor(rows, device="cuda")].float().cpu().numpy()
+    assert np.all(o == 0.0) and not np.signbit(o).any()
