@@ -157,7 +157,8 @@ def main():
     mfma_dtype = {"e4m3": "fp8", "bf16": "bf16", "f16": "f16", "f32": "f32"}[p.q_dtype]
     dominant = "attention" if attn_ms >= comb_ms else "combine"
     if dominant == "attention":
-        roof = dict(kernel="k1_page_attend", bound="hbm", achieved=round(attn_gbs, 1),
+        kname = "k1_page_attend" if p.unit_tokens == p.page_size else "k_grouped_attend"
+        roof = dict(kernel=kname, bound="hbm", achieved=round(attn_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4),
                     traffic=None, alg_bytes=attn_bytes)
     else:
