@@ -62,6 +62,29 @@ def tensor_bytes(t):
     return t.numel() * t.element_size()
 
 
+KERNEL_SOURCES = {"k1_page_attend": "attend_page.hip", "combine_kernel": "combine.hip",
+                  "k_grouped_attend": "attend_grouped.hip"}
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel's sources
+    changed since the counters were taken (hash recorded beside the figure)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h", "launch.h"):
+        with open(os.path.join(ROOT, "block_sparse_paged_table_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "traffic:" and parts[1] == kernel:
+            return int(parts[2]) if parts[3] == h.hexdigest() else None
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,7 +92,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle leg")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens for the CPU oracle leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), to "
@@ -160,11 +183,11 @@ def main():
         kname = "k1_page_attend" if p.unit_tokens == p.page_size else "k_grouped_attend"
         roof = dict(kernel=kname, bound="hbm", achieved=round(attn_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4),
-                    traffic=None, alg_bytes=attn_bytes)
+                    traffic=recorded_traffic(kname, p.name), alg_bytes=attn_bytes)
     else:
         roof = dict(kernel="combine_kernel", bound="hbm", achieved=round(comb_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(comb_gbs / HBM_PEAK_GBS, 4),
-                    traffic=None, alg_bytes=comb_bytes)
+                    traffic=recorded_traffic("combine_kernel", p.name), alg_bytes=comb_bytes)
 
     cpu = None
     if not args.no_cpu:
@@ -200,7 +223,8 @@ def main():
                       "hbm_gbs": round(attn_gbs, 1), "alg_bytes": attn_bytes,
                       "flops": st["flops"], "visible_keys": st["n_visible"]},
         "combine": {"gbs": round(comb_gbs, 1), "hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
-                    "alg_bytes": comb_bytes},
+                    "alg_bytes": comb_bytes,
+                    "traffic": recorded_traffic("combine_kernel", p.name)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
