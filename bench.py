@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens for the CPU oracle leg")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--slice-tokens", type=int, default=0,
+                    help="order_slice_tokens of the descriptor (0 = chosen by the library)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -128,9 +130,10 @@ def main():
         assert (p.total_q, p.num_rows, p.num_splits, p.d_v) == \
             (p0.total_q, p0.num_rows, p0.num_splits, p0.d_v), "input sets differ in shape"
     # one partial buffer / output shared by all sets (the biggest allocations)
-    dps = [DeviceProblem(probs[0])]
+    dps = [DeviceProblem(probs[0], order_slice_tokens=args.slice_tokens)]
     for p in probs[1:]:
-        dps.append(DeviceProblem(p, partial_o=dps[0].partial_o, partial_lse=dps[0].partial_lse))
+        dps.append(DeviceProblem(p, partial_o=dps[0].partial_o, partial_lse=dps[0].partial_lse,
+                                 order_slice_tokens=args.slice_tokens))
     for dp in dps[1:]:
         dp.out, dp.lse = dps[0].out, dps[0].lse
     torch.cuda.synchronize()

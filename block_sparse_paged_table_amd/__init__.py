@@ -74,6 +74,7 @@ class PrefillDesc(ctypes.Structure):
         ("partial_o", _c_p), ("po_split_stride", _c_i64), ("po_row_stride", _c_i64),
         ("partial_lse", _c_p), ("pl_split_stride", _c_i64),
         ("err_flags", _c_p),
+        ("order_slice_tokens", ctypes.c_int32),
     ]
 
     def __init__(self, **kw):

@@ -247,10 +247,36 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
   r.pl_split_stride = d->pl_split_stride;
   const int64_t L = (int64_t)d->num_seqs * d->max_pages * d->num_kv_heads;
   const int64_t NS = (int64_t)d->total_q * d->num_kv_heads * d->num_slots;
-  if (L >= (1ll << 31)) return fail(MSA_ERR_UNSUPPORTED, "too many page lists");
-  r.lay = page_layout(L, NS);
+  if (L >= (1ll << 24)) return fail(MSA_ERR_UNSUPPORTED, "too many page lists");
+  if (d->order_slice_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "order_slice_tokens < 0");
+
+  // Ordering slices: the plan keeps one list per (slice, request, logical
+  // page, KV head), so units come out slice by slice and the workgroups an
+  // XCD runs at one time read the queries of one slice only.  Automatic
+  // size: none while all queries fit in 16 MiB (their re-reads then hit the
+  // caches anyway); else ~512 KiB of queries per slice, but enough tokens
+  // that an average page list of a slice still fills one unit.
+  const int64_t rows = (int64_t)d->total_q * d->num_kv_heads;  // (token, KV head) rows
+  int64_t st = d->order_slice_tokens;
+  if (st == 0) {
+    const int64_t q_tok_bytes = (int64_t)d->num_q_heads * D * qb;
+    if ((int64_t)d->total_q * q_tok_bytes <= (16ll << 20))
+      st = (int64_t)d->total_q + 1;
+    else
+      st = std::max<int64_t>((512 << 10) / q_tok_bytes, (int64_t)r.chunk * d->max_pages / d->num_slots);
+  }
+  const int64_t rows_cap = std::max<int64_t>(256, (rows + 255) / 256 * 256);
+  int64_t slice_rows = std::min(rows_cap, (std::max<int64_t>(1, st * d->num_kv_heads) + 255) / 256 * 256);
+  int64_t n_slices = std::max<int64_t>(1, (rows + slice_rows - 1) / slice_rows);
+  while (n_slices * L > (1ll << 24) && n_slices > 1) {  // bound the plan's list arrays
+    slice_rows *= 2;
+    n_slices = std::max<int64_t>(1, (rows + slice_rows - 1) / slice_rows);
+  }
+  r.slice_rows = (int32_t)slice_rows;
+  r.lists_per_slice = (int32_t)L;
+  r.lay = page_layout(n_slices * L, NS);
   // every unit holds >= 1 entry: units <= entries/chunk + non-empty lists
-  r.max_units = NS / r.chunk + (L < NS ? L : NS);
+  r.max_units = NS / r.chunk + std::min(n_slices * L, NS);
   return MSA_OK;
 }
 

@@ -165,10 +165,12 @@ struct PlanEntry {
 };
 
 struct PageLayout {
-  int64_t num_lists;     // num_seqs * max_pages * Hkv
+  int64_t num_lists;     // slices * num_seqs * max_pages * Hkv
   int64_t num_sel;       // total_q * Hkv * num_slots
-  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, meta, dump, total;
+  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, meta, dump, tiles, total;
 };
+
+constexpr int kScanTile = 4096;  // lists per block of the plan's scan
 
 __host__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -185,6 +187,7 @@ __host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel) {
   L.slot_list = off; off = align_up(off + (size_t)num_sel * 4, 256);
   L.slot_pos = off;  off = align_up(off + (size_t)num_sel * 4, 256);
   L.entries = off;   off = align_up(off + (size_t)num_sel * sizeof(PlanEntry), 256);
+  L.tiles = off;     off = align_up(off + (size_t)((num_lists + kScanTile - 1) / kScanTile + 1) * 8, 256);
   L.total = off;
   return L;
 }

@@ -17,6 +17,8 @@ enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3
 struct PageArgs {
   int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, num_slots, max_pages, num_phys_pages;
   int32_t chunk;              // entries per work unit
+  int32_t slice_rows;         // (token, KV head) rows per ordering slice, multiple of 256
+  int32_t lists_per_slice;    // num_seqs * max_pages * Hkv
   int32_t route;
   float scale_log2;           // sm_scale * q_scale * k_scale * log2(e)
   float v_scale;

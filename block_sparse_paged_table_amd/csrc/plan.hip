@@ -6,13 +6,17 @@
 //   plan_zero  : clear the per-list counters and the error word
 //   plan_count : per (token, KV head) -- validate every slot, write
 //                lse = -inf for each empty slot, and give every used slot its
-//                position inside its (request, logical page, KV head) list.
+//                position inside its (slice, request, logical page, KV head)
+//                list.  Slices are runs of slice_rows (token, KV head) rows;
+//                listing them outermost makes the work units come out slice
+//                by slice, so the units running together on one XCD re-read
+//                the queries of one slice only (they stay in its L2).
 //                A workgroup first counts into an LDS histogram, then claims
 //                its block of each list with one global atomic per list, so
 //                the global counters see one atomic per (workgroup, list)
 //                instead of one per selection.
-//   plan_scan  : one workgroup -- exclusive scans of list sizes and of work
-//                units (lists cut into chunks of `chunk` entries)
+//   plan_scan  : exclusive scans of list sizes and of work units (lists cut
+//                into chunks of `chunk` entries), tile by tile
 //   plan_fill  : scatter (token, slot, visible limit) entries to their
 //                positions (no atomics)
 //
@@ -55,8 +59,10 @@ __device__ __forceinline__ RowCtx row_ctx(const PageArgs &a, int r, uint32_t &er
 template <bool LDS_HIST>
 __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
   extern __shared__ int32_t hist[];
-  const int64_t L = a.lay.num_lists;
+  const int64_t L = a.lists_per_slice;
   const int tid = threadIdx.x;
+  // slice_rows is a multiple of the block size: one slice per workgroup
+  const int64_t lbase = ((int64_t)blockIdx.x * kPlanThreads) / a.slice_rows * L;
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
   if constexpr (LDS_HIST) {
     for (int64_t i = tid; i < L; i += kPlanThreads) hist[i] = 0;
@@ -94,9 +100,9 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
           }
         }
       }
-      slot_list[j] = list;
+      slot_list[j] = list >= 0 ? (int32_t)(lbase + list) : -1;
       if (list >= 0) {
-        slot_pos[j] = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[list], 1);
+        slot_pos[j] = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[lbase + list], 1);
       } else {
         float *pl = a.partial_lse + j * a.pl_split_stride + (int64_t)r * a.Hq + g * a.G;
         for (int h = 0; h < a.G; ++h) pl[h] = -INFINITY;
@@ -108,20 +114,25 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
     __syncthreads();
     for (int64_t i = tid; i < L; i += kPlanThreads) {
       const int32_t n = hist[i];
-      if (n) hist[i] = atomicAdd(&counts[i], n);  // this workgroup's block of list i
+      if (n) hist[i] = atomicAdd(&counts[lbase + i], n);  // this workgroup's block of list i
     }
     __syncthreads();
     if (live)
       for (int j = 0; j < K; ++j) {
         const int list = slot_list[j];
-        if (list >= 0) slot_pos[j] += hist[list];
+        if (list >= 0) slot_pos[j] += hist[list - lbase];
       }
   }
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = kScanTile / kScanThreads;  // lists per thread
 
-__global__ void __launch_bounds__(kScanThreads) plan_scan(const PageArgs a) {
+// Exclusive scans of list sizes (-> list_off, entry offsets) and of work
+// units per list (-> unit_off), in three steps: per tile of kScanTile lists,
+// over the tile totals, then tile offsets added back.  With a single tile
+// the first step writes the final values.
+__global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a) {
   __shared__ int32_t s_e[kScanThreads];
   __shared__ int32_t s_u[kScanThreads];
   const int t = threadIdx.x;
@@ -129,14 +140,14 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan(const PageArgs a) {
   const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
-  int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
-  const int64_t per = (L + kScanThreads - 1) / kScanThreads;
-  const int64_t i0 = min(L, (int64_t)t * per), i1 = min(L, i0 + per);
+  const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)t * kScanPer;
+  int32_t c[kScanPer];
   int32_t se = 0, su = 0;
-  for (int64_t i = i0; i < i1; ++i) {
-    const int32_t c = counts[i];
-    se += c;
-    su += (c + a.chunk - 1) / a.chunk;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) {
+    c[k] = i0 + k < L ? counts[i0 + k] : 0;
+    se += c[k];
+    su += (c[k] + a.chunk - 1) / a.chunk;
   }
   s_e[t] = se;
   s_u[t] = su;
@@ -150,19 +161,84 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan(const PageArgs a) {
     __syncthreads();
   }
   int32_t be = s_e[t] - se, bu = s_u[t] - su;
-  for (int64_t i = i0; i < i1; ++i) {
-    const int32_t c = counts[i];
-    list_off[i] = be;
-    unit_off[i] = bu;
-    be += c;
-    bu += (c + a.chunk - 1) / a.chunk;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) {
+    if (i0 + k < L) {
+      list_off[i0 + k] = be;
+      unit_off[i0 + k] = bu;
+    }
+    be += c[k];
+    bu += (c[k] + a.chunk - 1) / a.chunk;
   }
   if (t == kScanThreads - 1) {
-    list_off[L] = s_e[t];
-    unit_off[L] = s_u[t];
-    meta[0] = s_u[t];  // number of work units
-    meta[2] = s_e[t];  // number of entries
+    if (gridDim.x == 1) {
+      int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
+      list_off[L] = s_e[t];
+      unit_off[L] = s_u[t];
+      meta[0] = s_u[t];  // number of work units
+      meta[2] = s_e[t];  // number of entries
+    } else {
+      int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
+      tiles[2 * blockIdx.x] = s_e[t];
+      tiles[2 * blockIdx.x + 1] = s_u[t];
+    }
   }
+}
+
+__global__ void __launch_bounds__(kScanThreads) plan_scan_top(const PageArgs a, int nt) {
+  __shared__ int32_t s_e[kScanThreads];
+  __shared__ int32_t s_u[kScanThreads];
+  const int t = threadIdx.x;
+  int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
+  const int per = (nt + kScanThreads - 1) / kScanThreads;
+  const int j0 = min(nt, t * per), j1 = min(nt, j0 + per);
+  int32_t se = 0, su = 0;
+  for (int j = j0; j < j1; ++j) {
+    se += tiles[2 * j];
+    su += tiles[2 * j + 1];
+  }
+  s_e[t] = se;
+  s_u[t] = su;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int32_t ve = t >= off ? s_e[t - off] : 0;
+    const int32_t vu = t >= off ? s_u[t - off] : 0;
+    __syncthreads();
+    s_e[t] += ve;
+    s_u[t] += vu;
+    __syncthreads();
+  }
+  int32_t be = s_e[t] - se, bu = s_u[t] - su;
+  for (int j = j0; j < j1; ++j) {  // totals -> exclusive offsets, in place
+    const int32_t e = tiles[2 * j], u = tiles[2 * j + 1];
+    tiles[2 * j] = be;
+    tiles[2 * j + 1] = bu;
+    be += e;
+    bu += u;
+  }
+  if (t == kScanThreads - 1) {
+    const int64_t L = a.lay.num_lists;
+    int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
+    ((int32_t *)(a.ws + a.lay.list_off))[L] = s_e[t];
+    ((int32_t *)(a.ws + a.lay.unit_off))[L] = s_u[t];
+    meta[0] = s_u[t];
+    meta[2] = s_e[t];
+  }
+}
+
+__global__ void __launch_bounds__(kScanThreads) plan_scan_add(const PageArgs a) {
+  const int tile = blockIdx.x + 1;  // tile 0 has offset 0
+  const int32_t *tiles = (const int32_t *)(a.ws + a.lay.tiles);
+  const int32_t oe = tiles[2 * tile], ou = tiles[2 * tile + 1];
+  int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
+  int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
+  const int64_t L = a.lay.num_lists;
+  const int64_t i0 = (int64_t)tile * kScanTile;
+  for (int k = threadIdx.x; k < kScanTile; k += kScanThreads)
+    if (i0 + k < L) {
+      list_off[i0 + k] += oe;
+      unit_off[i0 + k] += ou;
+    }
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a) {
@@ -191,18 +267,23 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a) {
 
 hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
-  const int64_t L = a.lay.num_lists;
+  const int64_t L = a.lay.num_lists;  // all slices
   const int64_t zero_blocks = (L + 255) / 256 > 0 ? (L + 255) / 256 : 1;
   plan_zero<<<(unsigned)zero_blocks, 256, 0, s>>>(counts, L, a.err_flags);
   const int64_t rows = (int64_t)a.total_q * a.Hkv;
   const unsigned blocks = (unsigned)((rows + kPlanThreads - 1) / kPlanThreads);
   if (blocks) {
-    if (L <= kMaxLdsLists)
-      plan_count<true><<<blocks, kPlanThreads, (size_t)L * 4, s>>>(a);
+    if (a.lists_per_slice <= kMaxLdsLists)
+      plan_count<true><<<blocks, kPlanThreads, (size_t)a.lists_per_slice * 4, s>>>(a);
     else
       plan_count<false><<<blocks, kPlanThreads, 0, s>>>(a);
   }
-  plan_scan<<<1, kScanThreads, 0, s>>>(a);
+  const int nt = (int)((L + kScanTile - 1) / kScanTile);
+  plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
+  if (nt > 1) {
+    plan_scan_top<<<1, kScanThreads, 0, s>>>(a, nt);
+    plan_scan_add<<<nt - 1, kScanThreads, 0, s>>>(a);
+  }
   if (blocks) plan_fill<<<blocks, kPlanThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -27,8 +27,9 @@ class DeviceProblem:
 
     def __init__(self, p: Problem, device: str = "cuda", out_dtype: str = None,
                  partial_o: torch.Tensor = None, partial_lse: torch.Tensor = None,
-                 po_row_pad: int = 0):
+                 po_row_pad: int = 0, order_slice_tokens: int = 0):
         self.p = p
+        self.order_slice_tokens = order_slice_tokens
         dev = torch.device(device)
         self.device = dev
         self.q = p.q.to(dev)
@@ -94,7 +95,7 @@ class DeviceProblem:
             partial_o=self.partial_o.data_ptr(), po_split_stride=self.partial_o.stride(0),
             po_row_stride=self.partial_o.stride(1),
             partial_lse=self.partial_lse.data_ptr(), pl_split_stride=self.partial_lse.stride(0),
-            err_flags=self.err.data_ptr(),
+            err_flags=self.err.data_ptr(), order_slice_tokens=self.order_slice_tokens,
         )
         if self.k_sf is not None:
             sb = _bstrides(self.k_sf)

@@ -150,6 +150,13 @@ typedef struct msa_prefill_desc {
     float *partial_lse;
     int64_t pl_split_stride;
     uint32_t *err_flags;       /* nullable; set (not OR-ed) by the plan step */
+
+    /* Scheduling hint of the page route: work units are ordered by slices of
+     * about this many query tokens, so that the queries a slice re-reads (once
+     * per selected page) stay in one XCD's L2 while its units run.  0 picks a
+     * value from the problem's shape.  Results are bitwise independent of it:
+     * every (row, split) partial is computed on its own. */
+    int32_t order_slice_tokens;
 } msa_prefill_desc;
 
 /* Workspace needed by msa_prefill_plan/_attend for this problem (bytes).

@@ -73,6 +73,15 @@ def test_host_validation_rejects(over, status):
     assert msa.library().msa_last_error().decode()
 
 
+def test_ordering_slice_hint():
+    """order_slice_tokens only sizes the plan's list arrays; negative is rejected."""
+    base = msa.msa_prefill_workspace_bytes(_desc(total_q=4096))
+    many = msa.msa_prefill_workspace_bytes(_desc(total_q=4096, order_slice_tokens=1))
+    assert many > base
+    with pytest.raises(msa.MsaError):
+        msa.msa_prefill_workspace_bytes(_desc(order_slice_tokens=-1))
+
+
 def test_struct_size_mismatch_rejected():
     d = _desc()
     d.struct_size = 8

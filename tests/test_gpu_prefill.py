@@ -68,6 +68,26 @@ def test_head_groupings(Hq, Hkv):
     _full_parity(p)
 
 
+@pytest.mark.parametrize("Hq,Hkv,qd,kd", [(16, 2, "e4m3", "nvfp4"), (48, 3, "bf16", "bf16")])
+def test_ordering_slices_bitwise_identical(Hq, Hkv, qd, kd):
+    """The unit order (slices of the plan) changes scheduling only: every
+    written partial, the combined output and the LSE are bitwise equal for any
+    slice length, and match the oracle with many slices."""
+    # a long context makes many (slice, page, head) lists: the plan's scan
+    # then runs over several tiles
+    p = _small(21, Hq=Hq, Hkv=Hkv, q_dtype=qd, kv_dtype=kd, ctx_lens=[0, 20000, 1000],
+               chunk_lens=[700, 450, 600], num_slots=8)
+    _full_parity(p, order_slice_tokens=1)
+    ref = _run(p)
+    live = ref.partial_lse > -float("inf")
+    assert live.any() and not live.all()
+    for st in (1, 100, 300, 1 << 20):
+        dp = _run(p, order_slice_tokens=st)
+        assert torch.equal(dp.partial_lse, ref.partial_lse), st
+        assert torch.equal(dp.partial_o[live], ref.partial_o[live]), st
+        assert torch.equal(dp.out, ref.out) and torch.equal(dp.lse, ref.lse), st
+
+
 def test_fp32_output_and_bf16_output_agree():
     p = _small(13, out_dtype="bf16")
     dp16 = _run(p)
