@@ -250,9 +250,10 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
   if (L >= (1ll << 24)) return fail(MSA_ERR_UNSUPPORTED, "too many page lists");
   if (d->order_slice_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "order_slice_tokens < 0");
 
-  // Ordering slices: the plan keeps one list per (slice, request, logical
-  // page, KV head), so units come out slice by slice and the workgroups an
-  // XCD runs at one time read the queries of one slice only.  Automatic
+  // Ordering slices: the plan keeps one list per (slice, KV head, request,
+  // logical page), so units come out slice by slice (one KV head after the
+  // other) and the workgroups an XCD runs at one time read the queries of
+  // one slice and head group only.  Automatic
   // size: none while all queries fit in 16 MiB (their re-reads then hit the
   // caches anyway); else ~512 KiB of queries per slice, but enough tokens
   // that an average page list of a slice still fills one unit.

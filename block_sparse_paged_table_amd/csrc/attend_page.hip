@@ -293,14 +293,14 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
     const int mid = (lo + hi) >> 1;
     if (unit_off[mid] <= unit) lo = mid; else hi = mid;
   }
-  const int list = lo;  // (slice, request, logical page, KV head)
+  const int list = lo;  // (slice, KV head, request, logical page)
   const int chunk_i = unit - unit_off[list];
   const int e_begin = list_off[list] + chunk_i * a.chunk;
   const int e_count = min(a.chunk, list_off[list + 1] - e_begin);
   const int pl = list % a.lists_per_slice;
-  const int g = pl % a.Hkv;
-  const int u = (pl / a.Hkv) % a.max_pages;
-  const int b = pl / (a.Hkv * a.max_pages);
+  const int u = pl % a.max_pages;
+  const int b = (pl / a.max_pages) % a.num_seqs;
+  const int g = pl / (a.max_pages * a.num_seqs);
   const int phys = a.page_table[b * a.pt_stride + u];
 
   // ---- the unit's entries -> LDS (so the tile loop issues no dependent

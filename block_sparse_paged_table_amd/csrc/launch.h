@@ -18,7 +18,7 @@ struct PageArgs {
   int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, num_slots, max_pages, num_phys_pages;
   int32_t chunk;              // entries per work unit
   int32_t slice_rows;         // (token, KV head) rows per ordering slice, multiple of 256
-  int32_t lists_per_slice;    // num_seqs * max_pages * Hkv
+  int32_t lists_per_slice;    // Hkv * num_seqs * max_pages (KV head outermost)
   int32_t route;
   float scale_log2;           // sm_scale * q_scale * k_scale * log2(e)
   float v_scale;

@@ -6,7 +6,7 @@
 //   plan_zero  : clear the per-list counters and the error word
 //   plan_count : per (token, KV head) -- validate every slot, write
 //                lse = -inf for each empty slot, and give every used slot its
-//                position inside its (slice, request, logical page, KV head)
+//                position inside its (slice, KV head, request, logical page)
 //                list.  Slices are runs of slice_rows (token, KV head) rows;
 //                listing them outermost makes the work units come out slice
 //                by slice, so the units running together on one XCD re-read
@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
             if (pp < 0 || pp >= a.num_phys_pages)
               err |= MSA_ERRF_PHYS_RANGE;
             else
-              list = (c.b * a.max_pages + u) * a.Hkv + g;
+              list = (g * a.num_seqs + c.b) * a.max_pages + u;  // KV head outermost
           }
         }
       }
