@@ -170,6 +170,41 @@ def test_three_runs_bitwise_identical(qd, kd):
         assert all(torch.equal(x, y) for x, y in zip(snaps[0], s))
 
 
+@pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("e4m3", "nvfp4")])
+def test_graph_capture_replays_match_eager(qd, kd):
+    """plan + attention + combine captured in one HIP graph (kernels only, no
+    memset nodes); every replay, with eager work and clobbered outputs in
+    between, reproduces the eager results bit for bit."""
+    p = _small(22, q_dtype=qd, kv_dtype=kd, Hq=16, Hkv=2)
+    dp = DeviceProblem(p)
+    dp.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dp.partial_lse, dp.partial_o, dp.out, dp.lse)]
+    live = ref[0] > -float("inf")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dp.run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (dp.partial_o, dp.out, dp.lse, dp.partial_lse):
+            t.fill_(float(i + 1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.partial_lse, ref[0]), i
+        assert torch.equal(dp.partial_o[live], ref[1][live]), i
+        assert torch.equal(dp.out, ref[2]) and torch.equal(dp.lse, ref[3]), i
+        assert dp.err_flags() == 0
+        dp.run()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_onehot_selection_probe_bitexact():
     """Index probe: K[t, 0] = 128 * (t mod page) and Q[., 0] = 16 give logit
     gaps so large that every partial is exactly the value row of the last
