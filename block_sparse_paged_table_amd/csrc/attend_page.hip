@@ -234,15 +234,9 @@ __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const uint32_t scale = (vsf[kk] >> (8 * b)) & 0xffu;
-      const u32x2 tab = nvfp4_mag_table(scale);
       // FP16 magnitude table, split into its low and high bytes
-      uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-#pragma unroll
-      for (int c = 1; c < 8; ++c) {
-        const uint32_t f = e4m3_mag_to_f16_bits((tab[c >> 2] >> (8 * (c & 3))) & 0xffu);
-        lo[c >> 2] |= (f & 0xffu) << (8 * (c & 3));
-        hi[c >> 2] |= (f >> 8) << (8 * (c & 3));
-      }
+      uint32_t lo[2], hi[2];
+      nvfp4_f16_tables(nvfp4_mag_table(scale), lo, hi);
       const uint32_t flip = (scale & 0x80u) ? 0x80008000u : 0u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // 4 codes -> two FP16 pairs

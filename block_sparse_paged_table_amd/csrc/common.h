@@ -46,52 +46,6 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 // ---------------------------------------------------------------- formats
 
-// OCP E4M3 byte -> float (exact).  NaN codes are not special-cased.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (b & 0x80u) ? -v : v;
-}
-
-// E2M1 code (low 4 bits) -> float (exact): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const float v = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : (m ? 0.5f : 0.0f);
-  return (c & 8u) ? -v : v;
-}
-
-// float -> OCP E4M3 byte, round to nearest even, saturating to +-448; the
-// sign of zero is kept.  NaN -> 0x7F.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t a = bits & 0x7fffffffu;
-  uint32_t code;
-  if (a > 0x7f800000u) return 0x7fu;
-  if (a >= 0x43e80000u) {            // |x| >= 464: beyond the last rounding midpoint
-    code = 0x7eu;
-  } else if (a < 0x3c800000u) {      // |x| < 2^-6: subnormal grid of step 2^-9
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    const uint32_t e = (a >> 23) - 120u;   // biased E4M3 exponent, 1..15
-    const uint32_t mant = a & 0x7fffffu;
-    const uint32_t keep = mant >> 20, rem = mant & 0xfffffu;
-    const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
-    code = ((e << 3) | keep) + up;
-  }
-  return sign | code;
-}
-
-// |x| -> E4M3 magnitude code without branches: round to nearest even at the
-// 3-bit mantissa (normal range, |x| >= 2^-6) or on the 2^-9 grid (subnormal
-// range), saturating at 448 (0x7E).  `ax` must be finite and >= 0.
-__device__ __forceinline__ uint32_t e4m3_mag_rne(float ax) {
-  const uint32_t a = __float_as_uint(ax);
-  const uint32_t cn = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t cs = (uint32_t)__builtin_rintf(ax * 512.0f);
-  return min(a < 0x3c800000u ? cs : cn, 0x7eu);
-}
-
 // NVFP4 dequantisation (MiniMax-AI/MSA PR 21, section "Build the prefill for
 // SM107"): an element is its E2M1 code times its block's E4M3 scale, rounded
 // once to E4M3 (the float product is exact: at most 6 significant bits).
@@ -100,13 +54,33 @@ __device__ __forceinline__ uint32_t e4m3_mag_rne(float ax) {
 // sign bit XOR-ed from the code and the scale (an IEEE product's sign, which
 // also gives the sign of zero).
 //
-// nvfp4_mag_table: the 8 magnitude bytes, byte c of the 8-byte pair.
+// nvfp4_mag_table: the 8 magnitude bytes, byte c of the 8-byte pair.  The
+// products are exact in FP32; clamping them to 448 and converting with the
+// hardware's round-to-nearest-even FP8 conversion gives the saturating RNE
+// rounding (every product above 448 rounds to 448).
 __device__ __forceinline__ u32x2 nvfp4_mag_table(uint32_t scale) {
-  const float s = e4m3_to_f32(scale & 0x7fu);
-  const uint32_t m1 = e4m3_mag_rne(0.5f * s), m2 = e4m3_mag_rne(s), m3 = e4m3_mag_rne(1.5f * s);
-  const uint32_t m4 = e4m3_mag_rne(2.0f * s), m5 = e4m3_mag_rne(3.0f * s);
-  const uint32_t m6 = e4m3_mag_rne(4.0f * s), m7 = e4m3_mag_rne(6.0f * s);
-  return u32x2{(m1 << 8) | (m2 << 16) | (m3 << 24), m4 | (m5 << 8) | (m6 << 16) | (m7 << 24)};
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)(scale & 0x7fu), 0);
+  const float top = 448.0f;
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(0.0f, 0.5f * s, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(s, fminf(1.5f * s, top), w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(2.0f * s, top), fminf(3.0f * s, top), 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(4.0f * s, top), fminf(6.0f * s, top), w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+
+// The same 8 magnitudes as FP16 (exact: E4M3 values are FP16 values), split
+// into a table of their low bytes and one of their high bytes (byte c of
+// each pair), for byte-permute lookups.
+__device__ __forceinline__ void nvfp4_f16_tables(u32x2 tab, uint32_t lo[2], uint32_t hi[2]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)tab[w], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)tab[w], true);
+    const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f01[0], f01[1]));
+    const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f23[0], f23[1]));
+    lo[w] = __builtin_amdgcn_perm(h23, h01, 0x06040200u);
+    hi[w] = __builtin_amdgcn_perm(h23, h01, 0x07050301u);
+  }
 }
 
 // Spread 4 nibbles (bits 4i..4i+3) to the low nibbles of 4 bytes.
@@ -121,14 +95,6 @@ __device__ __forceinline__ uint32_t nvfp4_lookup4(uint32_t codes, u32x2 tab, uin
   const uint32_t sp = spread_nibbles(codes & 0xffffu);
   const uint32_t mags = __builtin_amdgcn_perm(tab[1], tab[0], sp & 0x07070707u);
   return (mags | ((sp & 0x08080808u) << 4)) ^ sign_flip;
-}
-
-// E4M3 magnitude byte -> FP16 bits (exact: every E4M3 value is an FP16 value).
-__device__ __forceinline__ uint32_t e4m3_mag_to_f16_bits(uint32_t b) {
-  const uint32_t e = b >> 3, m = b & 7u;
-  const uint32_t normal = ((e + 8u) << 10) | (m << 7);
-  const uint32_t sub = __builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
-  return e ? normal : sub;
 }
 
 // Single-element form (standalone dequantisation entry point; same tables).
