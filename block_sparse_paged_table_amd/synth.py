@@ -28,7 +28,7 @@ import torch
 
 # Storage dtypes understood by the library and the oracle.
 Q_DTYPES = ("f32", "bf16", "f16", "e4m3")
-KV_DTYPES = ("f32", "bf16", "f16", "nvfp4")
+KV_DTYPES = ("f32", "bf16", "f16", "e4m3", "nvfp4")
 TORCH_DTYPE = {
     "f32": torch.float32,
     "bf16": torch.bfloat16,
@@ -274,6 +274,9 @@ def build_page_problem(
     if kv_dtype == "nvfp4":
         k_cache, k_sf, k_scale = quantize_nvfp4(kf)
         v_cache, v_sf, v_scale = quantize_nvfp4(vf)
+    elif kv_dtype == "e4m3":
+        k_cache, k_scale = quantize_e4m3_tensor(torch.from_numpy(kf))
+        v_cache, v_scale = quantize_e4m3_tensor(torch.from_numpy(vf))
     else:
         k_cache = torch.from_numpy(kf).to(TORCH_DTYPE[kv_dtype])
         v_cache = torch.from_numpy(vf).to(TORCH_DTYPE[kv_dtype])

@@ -174,6 +174,10 @@ class _Keep:
             self.k_sf = np.ascontiguousarray(_as_np(p.k_sf), np.uint8)
             self.v_sf = np.ascontiguousarray(_as_np(p.v_sf), np.uint8)
             kv_fmt = FMT_NVFP4
+        elif p.kv_dtype == "e4m3":
+            self.k = np.ascontiguousarray(_as_np(p.k_cache), np.uint8)
+            self.v = np.ascontiguousarray(_as_np(p.v_cache), np.uint8)
+            kv_fmt = FMT_E4M3
         else:
             self.k = np.ascontiguousarray(_as_np(p.k_cache), np.float64)
             self.v = np.ascontiguousarray(_as_np(p.v_cache), np.float64)

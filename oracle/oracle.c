@@ -168,8 +168,8 @@ typedef struct {
     /* Q: F64 values or E4M3 bytes, [total_q][Hq][d_qk] */
     int q_fmt;
     const void *q;
-    /* KV: F64 [P][page][Hkv][d]; NVFP4 codes [P][page][Hkv][d/2] (element 2i
-     * in the low nibble) with E4M3 scales [P][page][Hkv][d/16] */
+    /* KV: F64 or E4M3 bytes [P][page][Hkv][d]; NVFP4 codes [P][page][Hkv][d/2]
+     * (element 2i in the low nibble) with E4M3 scales [P][page][Hkv][d/16] */
     int kv_fmt;
     const void *k, *v;
     const uint8_t *k_sf, *v_sf;
@@ -207,6 +207,8 @@ static double kv_value(const orc_problem *p, const double tab[16][256], int is_v
         uint8_t scale = sf[base * (dim / 16) + d / 16];
         return tab[code][scale];
     }
+    if (p->kv_fmt == ORC_FMT_E4M3)      /* per-tensor scaled FP8 cache */
+        return orc_e4m3_decode(((const uint8_t *)(is_v ? p->v : p->k))[base * dim + d]);
     return ((const double *)(is_v ? p->v : p->k))[base * dim + d];
 }
 

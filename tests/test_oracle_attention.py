@@ -54,7 +54,8 @@ def _assert_same_finite(a, b, tol=TOL):
 
 # ------------------------------------------------------------ dense equivalence
 
-@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("e4m3", "nvfp4")])
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("e4m3", "nvfp4"),
+                                    ("e4m3", "e4m3")])
 def test_dense_equivalence_sdpa(dtypes):
     qd, kd = dtypes
     p = synth.build_page_problem(
@@ -290,9 +291,10 @@ def _tiny_cases():
         name="mb2", seed=27, ctx_len=40, chunk_len=17, pad_rows=1, Hq=2, Hkv=2, d=16,
         num_slots=8, page_size=8, spare_pages=1)
     yield dataclasses.replace(mb, slots_per_split=2)
+    yield _small(seed=28, Hq=4, Hkv=2, d=32, q_dtype="e4m3", kv_dtype="e4m3", num_slots=4)
 
 
-@pytest.mark.parametrize("case", list(range(8)))
+@pytest.mark.parametrize("case", list(range(9)))
 def test_bruteforce_agrees(case):
     p = list(_tiny_cases())[case]
     a = oracle.prefill_rows(p)
