@@ -26,7 +26,7 @@ from typing import Optional
 __all__ = [
     "MSA_F32", "MSA_BF16", "MSA_F16", "MSA_E4M3", "MSA_NVFP4",
     "MSA_ERRF_SEL_RANGE", "MSA_ERRF_PHYS_RANGE", "MSA_ERRF_QSEQ_RANGE", "MSA_ERRF_DUPLICATE",
-    "MsaError", "PrefillDesc", "library", "library_path",
+    "MsaError", "PrefillDesc", "library", "library_path", "msa_combine_ex",
     "msa_prefill_workspace_bytes", "msa_prefill_plan", "msa_prefill_attend",
     "msa_sparse_prefill", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_device_supported",
     "msa_abi_version",
@@ -75,6 +75,7 @@ class PrefillDesc(ctypes.Structure):
         ("partial_lse", _c_p), ("pl_split_stride", _c_i64),
         ("err_flags", _c_p),
         ("order_slice_tokens", ctypes.c_int32),
+        ("partial_dtype", ctypes.c_int32),
     ]
 
     def __init__(self, **kw):
@@ -93,6 +94,8 @@ _SIGNATURES = [
     ("msa_sparse_prefill", ctypes.c_int, [ctypes.POINTER(PrefillDesc), _c_p, ctypes.c_size_t, _c_p]),
     ("msa_combine", ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i32,
                                    _c_p, _c_i32, _c_i64, _c_p, _c_p]),
+    ("msa_combine_ex", ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64,
+                                      _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     ("msa_nvfp4_dequant_e4m3", ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p]),
     ("msa_device_supported", ctypes.c_int, [ctypes.c_int]),
     ("msa_status_str", ctypes.c_char_p, [ctypes.c_int]),
@@ -170,25 +173,46 @@ def msa_sparse_prefill(desc: PrefillDesc, workspace, stream=None):
     _check(library().msa_sparse_prefill(ctypes.byref(desc), p, n, _stream(stream)))
 
 
+def _combine_args(partial_o, partial_lse, out, po_split_stride, po_row_stride, pl_split_stride,
+                  out_dtype, out_row_stride):
+    import torch
+    codes = {torch.float32: MSA_F32, torch.bfloat16: MSA_BF16, torch.float16: MSA_F16}
+    return (partial_o.stride(0) if po_split_stride is None else po_split_stride,
+            partial_o.stride(-2) if po_row_stride is None else po_row_stride,
+            partial_lse.stride(0) if pl_split_stride is None else pl_split_stride,
+            codes[out.dtype] if out_dtype is None else out_dtype,
+            out.stride(-2) if out_row_stride is None else out_row_stride,
+            codes.get(partial_o.dtype))
+
+
 def msa_combine(partial_o, partial_lse, num_splits: int, num_rows: int, head_dim_v: int, out,
                 lse=None, po_split_stride: Optional[int] = None, po_row_stride: Optional[int] = None,
                 pl_split_stride: Optional[int] = None, out_dtype: Optional[int] = None,
                 out_row_stride: Optional[int] = None, stream=None):
-    """LSE combine; strides default to those of [S, rows, d] / [S, rows] / [rows, d] tensors."""
-    import torch
-    if po_split_stride is None:
-        po_split_stride = partial_o.stride(0)
-    if po_row_stride is None:
-        po_row_stride = partial_o.stride(-2)
-    if pl_split_stride is None:
-        pl_split_stride = partial_lse.stride(0)
-    if out_dtype is None:
-        out_dtype = {torch.float32: MSA_F32, torch.bfloat16: MSA_BF16, torch.float16: MSA_F16}[out.dtype]
-    if out_row_stride is None:
-        out_row_stride = out.stride(-2)
-    _check(library().msa_combine(_ptr(partial_o), po_split_stride, po_row_stride, _ptr(partial_lse),
-                                 pl_split_stride, num_splits, num_rows, head_dim_v, _ptr(out),
-                                 out_dtype, out_row_stride, _ptr(lse), _stream(stream)))
+    """LSE combine of FP32 partials; strides default to those of [S, rows, d] /
+    [S, rows] / [rows, d] tensors."""
+    pss, prs, lss, odt, ors, _ = _combine_args(partial_o, partial_lse, out, po_split_stride,
+                                               po_row_stride, pl_split_stride, out_dtype,
+                                               out_row_stride)
+    _check(library().msa_combine(_ptr(partial_o), pss, prs, _ptr(partial_lse), lss, num_splits,
+                                 num_rows, head_dim_v, _ptr(out), odt, ors, _ptr(lse),
+                                 _stream(stream)))
+
+
+def msa_combine_ex(partial_o, partial_lse, num_splits: int, num_rows: int, head_dim_v: int, out,
+                   lse=None, partial_dtype: Optional[int] = None,
+                   po_split_stride: Optional[int] = None, po_row_stride: Optional[int] = None,
+                   pl_split_stride: Optional[int] = None, out_dtype: Optional[int] = None,
+                   out_row_stride: Optional[int] = None, stream=None):
+    """LSE combine of FP32, BF16 or FP16 partials (dtype taken from the tensor
+    unless given)."""
+    pss, prs, lss, odt, ors, pdt = _combine_args(partial_o, partial_lse, out, po_split_stride,
+                                                 po_row_stride, pl_split_stride, out_dtype,
+                                                 out_row_stride)
+    pdt = pdt if partial_dtype is None else partial_dtype
+    _check(library().msa_combine_ex(_ptr(partial_o), pdt, pss, prs, _ptr(partial_lse), lss,
+                                    num_splits, num_rows, head_dim_v, _ptr(out), odt, ors,
+                                    _ptr(lse), _stream(stream)))
 
 
 def msa_nvfp4_dequant_e4m3(codes, scales, out, stream=None):

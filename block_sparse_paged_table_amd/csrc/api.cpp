@@ -51,6 +51,7 @@ int page_route(const msa_prefill_desc *d) {
   if (d->q_dtype == MSA_BF16 && d->kv_dtype == MSA_BF16) return kRouteBF16;
   if (d->q_dtype == MSA_F16 && d->kv_dtype == MSA_F16) return kRouteF16;
   if (d->q_dtype == MSA_E4M3 && d->kv_dtype == MSA_NVFP4) return kRouteQ8KV4;
+  if (d->q_dtype == MSA_E4M3 && d->kv_dtype == MSA_E4M3) return kRouteQ8KV8;
   return -1;
 }
 
@@ -116,6 +117,7 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   r.sel_stride_tok = d->sel_stride_tok;
   r.sel_stride_head = d->sel_stride_head;
   r.partial_o = d->partial_o;
+  r.po_dtype = d->partial_dtype;
   r.po_row_stride = d->po_row_stride;
   r.partial_lse = d->partial_lse;
   r.lay = group_layout((int64_t)r.num_groups * r.Hkv, r.list_cap);
@@ -149,6 +151,8 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
     return fail(MSA_ERR_INVALID_ARG, "scales must be finite, sm_scale >= 0, q_scale and k_scale > 0");
   if (d->head_dim_qk < 1 || d->head_dim_v < 1)
     return fail(MSA_ERR_INVALID_ARG, "bad head dims");
+  if (d->partial_dtype != MSA_F32 && d->partial_dtype != MSA_BF16 && d->partial_dtype != MSA_F16)
+    return fail(MSA_ERR_INVALID_ARG, "partial_dtype must be F32, BF16 or F16");
   const void *need[] = {d->q, d->q_seq, d->q_pos, d->seq_lens, d->k_cache, d->v_cache,
                         d->page_table, d->sel_idx, d->sel_mask, d->partial_o, d->partial_lse};
   const char *names[] = {"q", "q_seq", "q_pos", "seq_lens", "k_cache", "v_cache",
@@ -179,6 +183,8 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
     return fail(MSA_ERR_UNSUPPORTED, "head_dim %d unsupported for this dtype", D);
   if (d->slots_per_split != 1)
     return fail(MSA_ERR_UNSUPPORTED, "page route writes one partial per slot (slots_per_split 1)");
+  if (route == kRouteF32 && d->partial_dtype != MSA_F32)
+    return fail(MSA_ERR_UNSUPPORTED, "FP32 queries take FP32 partials");
   if (d->num_slots > 255)
     return fail(MSA_ERR_UNSUPPORTED, "at most 255 slots");
 
@@ -241,6 +247,7 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
   r.sel_stride_tok = d->sel_stride_tok;
   r.sel_stride_head = d->sel_stride_head;
   r.partial_o = d->partial_o;
+  r.po_dtype = d->partial_dtype;
   r.po_split_stride = d->po_split_stride;
   r.po_row_stride = d->po_row_stride;
   r.partial_lse = d->partial_lse;
@@ -352,12 +359,15 @@ msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *ws, size_t ws_byt
   return msa_prefill_attend(d, ws, ws_bytes, stream);
 }
 
-msa_status msa_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
-                       int64_t pl_split, int32_t num_splits, int64_t num_rows, int32_t dv, void *out,
-                       int32_t out_dtype, int64_t out_row, float *lse, void *stream) {
+msa_status msa_combine_ex(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
+                          const float *pl, int64_t pl_split, int32_t num_splits, int64_t num_rows,
+                          int32_t dv, void *out, int32_t out_dtype, int64_t out_row, float *lse,
+                          void *stream) {
   if (num_rows < 0 || num_splits < 1 || dv < 4 || dv > 1024 || dv % 4)
     return fail(MSA_ERR_INVALID_ARG, "bad sizes: splits %d rows %lld head_dim_v %d", num_splits,
                 (long long)num_rows, dv);
+  if (po_dtype != MSA_F32 && po_dtype != MSA_BF16 && po_dtype != MSA_F16)
+    return fail(MSA_ERR_INVALID_ARG, "partial dtype must be F32, BF16 or F16");
   if (num_rows == 0) return ok();
   if (!po || !pl || !out) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
   if (out_dtype != MSA_F32 && out_dtype != MSA_BF16 && out_dtype != MSA_F16)
@@ -369,9 +379,16 @@ msa_status msa_combine(const float *po, int64_t po_split, int64_t po_row, const 
     return fail(MSA_ERR_INVALID_ARG, "out must be aligned to 4 elements with row stride >= head_dim_v");
   if (!aligned(pl, 4) || (lse && !aligned(lse, 4)) || pl_split < 0)
     return fail(MSA_ERR_INVALID_ARG, "lse buffers misaligned");
-  return hip_status(launch_combine(po, po_split, po_row, pl, pl_split, num_splits, num_rows, dv, out,
-                                   out_dtype, out_row, lse, (hipStream_t)stream),
+  return hip_status(launch_combine(po, po_dtype, po_split, po_row, pl, pl_split, num_splits, num_rows,
+                                   dv, out, out_dtype, out_row, lse, (hipStream_t)stream),
                     "combine launch");
+}
+
+msa_status msa_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
+                       int64_t pl_split, int32_t num_splits, int64_t num_rows, int32_t dv, void *out,
+                       int32_t out_dtype, int64_t out_row, float *lse, void *stream) {
+  return msa_combine_ex(po, MSA_F32, po_split, po_row, pl, pl_split, num_splits, num_rows, dv, out,
+                        out_dtype, out_row, lse, stream);
 }
 
 msa_status msa_nvfp4_dequant_e4m3(const uint8_t *codes, const uint8_t *scales, uint8_t *out,

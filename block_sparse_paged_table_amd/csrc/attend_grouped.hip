@@ -131,7 +131,8 @@ __device__ __forceinline__ void store_batch(uint8_t *st, const BatchRegs<D> &r) 
   }
 }
 
-template <int D>
+// PO: dtype of partial_o (MSA_F32, MSA_BF16 or MSA_F16).
+template <int D, int PO>
 __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
   using Gm = GGeom<D>;
   constexpr int MT = D / 16;
@@ -254,15 +255,15 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
   lp += __shfl_xor(lp, 16);
   lp += __shfl_xor(lp, 32);
   const int64_t row = (int64_t)tok * a.Hq + h;
-  float *dst = a.partial_o + row * a.po_row_stride + gl * 4;
+  const int64_t off = row * a.po_row_stride + gl * 4;
   if (l > 0.0f) {
     const float inv = a.v_scale / lp;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4 *)(dst + mt * 16) = o[mt] * inv;
+    for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, o[mt] * inv);
     if (gl == 0) a.partial_lse[row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   } else {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4 *)(dst + mt * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, f32x4{0.f, 0.f, 0.f, 0.f});
     if (gl == 0) a.partial_lse[row] = -INFINITY;
   }
 }
@@ -272,10 +273,14 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;
   dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv);
-  if (a.D == 256)
-    k_grouped_attend<256><<<grid, GT, 0, s>>>(a);
-  else
-    k_grouped_attend<128><<<grid, GT, 0, s>>>(a);
+  switch ((a.D == 256 ? 8 : 0) + a.po_dtype) {
+    case 8 + MSA_F32: k_grouped_attend<256, MSA_F32><<<grid, GT, 0, s>>>(a); break;
+    case 8 + MSA_BF16: k_grouped_attend<256, MSA_BF16><<<grid, GT, 0, s>>>(a); break;
+    case 8 + MSA_F16: k_grouped_attend<256, MSA_F16><<<grid, GT, 0, s>>>(a); break;
+    case MSA_BF16: k_grouped_attend<128, MSA_BF16><<<grid, GT, 0, s>>>(a); break;
+    case MSA_F16: k_grouped_attend<128, MSA_F16><<<grid, GT, 0, s>>>(a); break;
+    default: k_grouped_attend<128, MSA_F32><<<grid, GT, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 

@@ -32,6 +32,8 @@
 //   Q8KV4 : e4m3 / nvfp4 -> NVFP4 dequantised once per page to E4M3 (exact
 //           product, one rounding; section "Build the prefill for SM107"),
 //           QK 16x16x32 fp8, V E4M3 -> FP16 (exact), PV 16x16x32 f16
+//   Q8KV8 : e4m3 / e4m3  -> per-tensor scaled FP8 cache: K copied as is, QK
+//           16x16x32 fp8, V E4M3 -> FP16 (exact), PV 16x16x32 f16
 #include <type_traits>
 #include <utility>
 
@@ -50,6 +52,7 @@ template <> struct RouteInfo<kRouteF32> { static constexpr int QB = 4; static co
 template <> struct RouteInfo<kRouteBF16> { static constexpr int QB = 2; static constexpr bool F16PV = true; };
 template <> struct RouteInfo<kRouteF16> { static constexpr int QB = 2; static constexpr bool F16PV = true; };
 template <> struct RouteInfo<kRouteQ8KV4> { static constexpr int QB = 1; static constexpr bool F16PV = true; };
+template <> struct RouteInfo<kRouteQ8KV8> { static constexpr int QB = 1; static constexpr bool F16PV = true; };
 
 // Key (in-page offset) carried by A-operand row m of key tile t.  For FP16
 // PV the keys of tiles 2b and 2b+1 interleave so that the four S^T registers
@@ -189,6 +192,55 @@ __device__ __forceinline__ float load_page_float(const PageArgs &a, int phys, in
   }
 }
 
+// Q8KV8: K rows copied as E4M3 (swizzled); V converted E4M3 -> FP16 (exact)
+// and stored transposed for PV, key pairs packed as FP16x2 words.
+template <int D>
+__device__ __forceinline__ void load_page_fp8(const PageArgs &a, int phys, int g, uint8_t *sK,
+                                              uint8_t *sV) {
+  using Gm = Geom<kRouteQ8KV8, D>;
+  const int tid = threadIdx.x;
+  const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
+  const uint8_t *vb = a.v_cache + (int64_t)phys * a.kv_stride_page + (int64_t)g * a.kv_stride_head;
+  // thread -> key pair kp, block db of D/4 dims (V)
+  const int kp = tid & 63, db = tid >> 6;
+  constexpr int DB = D / 4;
+  constexpr int NCH = DB / 16;  // 16-byte chunks per key and block
+  u32x4 v0[NCH], v1[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    v0[c] = ld<u32x4>(vb + (2 * kp) * a.kv_stride_tok + db * DB + c * 16);
+    v1[c] = ld<u32x4>(vb + (2 * kp + 1) * a.kv_stride_tok + db * DB + c * 16);
+  }
+  constexpr int KCH = PAGE * Gm::CPR / THREADS;
+  u32x4 kreg[KCH];
+#pragma unroll
+  for (int it = 0; it < KCH; ++it) {
+    const int q = it * THREADS + tid, key = q / Gm::CPR, c = q % Gm::CPR;
+    kreg[it] = ld<u32x4>(kb + key * a.kv_stride_tok + c * 16);
+  }
+#pragma unroll
+  for (int it = 0; it < KCH; ++it) {
+    const int q = it * THREADS + tid, key = q / Gm::CPR, c = q % Gm::CPR;
+    *(u32x4 *)(sK + k_off<kRouteQ8KV8, D>(key, c)) = kreg[it];
+  }
+  const int col = (kp & 3) << 2;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const auto a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v0[c][w], false);
+      const auto a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v1[c][w], false);
+      const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v0[c][w], true);
+      const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v1[c][w], true);
+      const int dv = db * DB + c * 16 + w * 4;
+      const float f[4][2] = {{a0[0], a1[0]}, {a0[1], a1[1]}, {b0[0], b1[0]}, {b0[1], b1[1]}};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(uint32_t *)(sV + vt_off(dv + e, kp >> 2) + col) =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[e][0], f[e][1]));
+    }
+}
+
 // Q8KV4: NVFP4 K/V dequantised to E4M3 once per page, through per-block
 // magnitude tables (see nvfp4_mag_table): K stays E4M3 for the FP8 QK
 // product, V becomes FP16 (exact) and is stored transposed for PV.
@@ -262,7 +314,9 @@ __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int
 
 // ------------------------------------------------------------ the kernel
 
-template <int ROUTE, int D>
+// PO: dtype of partial_o (MSA_F32, or MSA_BF16 / MSA_F16 to halve the
+// partial bytes; the LSE stays FP32).
+template <int ROUTE, int D, int PO>
 __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2 : 1))
     k1_page_attend(const PageArgs a) {
   using Gm = Geom<ROUTE, D>;
@@ -307,6 +361,7 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
   // ---- page -> LDS
   float vfac = 1.0f;
   if constexpr (ROUTE == kRouteQ8KV4) load_page_nvfp4<D>(a, phys, g, sK, sV);
+  else if constexpr (ROUTE == kRouteQ8KV8) load_page_fp8<D>(a, phys, g, sK, sV);
   else vfac = load_page_float<ROUTE, D>(a, phys, g, sK, sV, sRed);
   __syncthreads();
   const float out_scale = a.v_scale * vfac;
@@ -497,10 +552,10 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
     // in flight across the loop back-edge.
     const float inv = out_scale / lp;  // IEEE division (v_rcp_f32 is not exact even at 1.0)
     const int64_t row = (int64_t)tok * a.Hq + h;
-    float *dst = active ? a.partial_o + (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4
-                        : dump + grp * 4;
+    void *dst = active ? a.partial_o : (void *)dump;
+    const int64_t po_off = active ? (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4 : grp * 4;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4 *)(dst + mt * 16) = o[mt] * inv;
+    for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(dst, po_off + mt * 16, o[mt] * inv);
     float *ldst = (active && grp == 0) ? a.partial_lse + (int64_t)slot * a.pl_split_stride + row
                                        : dump + D + lane;
     *ldst = (msc + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
@@ -524,7 +579,15 @@ template <int ROUTE, int D>
 hipError_t launch_route(const PageArgs &a, hipStream_t s) {
   const int64_t grid = (a.max_units + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-  k1_page_attend<ROUTE, D><<<(unsigned)grid, THREADS, 0, s>>>(a);
+  if constexpr (ROUTE == kRouteF32) {  // FP32 partials only (checked on the host)
+    k1_page_attend<ROUTE, D, MSA_F32><<<(unsigned)grid, THREADS, 0, s>>>(a);
+  } else {
+    switch (a.po_dtype) {
+      case MSA_BF16: k1_page_attend<ROUTE, D, MSA_BF16><<<(unsigned)grid, THREADS, 0, s>>>(a); break;
+      case MSA_F16: k1_page_attend<ROUTE, D, MSA_F16><<<(unsigned)grid, THREADS, 0, s>>>(a); break;
+      default: k1_page_attend<ROUTE, D, MSA_F32><<<(unsigned)grid, THREADS, 0, s>>>(a); break;
+    }
+  }
   return hipGetLastError();
 }
 
@@ -540,6 +603,8 @@ hipError_t launch_page_attend(const PageArgs &a, hipStream_t s) {
       return a.D == 64 ? launch_route<kRouteF16, 64>(a, s) : launch_route<kRouteF16, 128>(a, s);
     case kRouteQ8KV4:
       return launch_route<kRouteQ8KV4, 128>(a, s);
+    case kRouteQ8KV8:
+      return a.D == 64 ? launch_route<kRouteQ8KV8, 64>(a, s) : launch_route<kRouteQ8KV8, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,8 +1,8 @@
 // LSE combine (MiniMax-AI/MSA PR 21, section "Combine"), written for gfx950.
 //
 // All (token, head) rows of the batch form one flat list; the kernel is a
-// pure stream over the partial buffer, so its job is to keep enough 16-byte
-// loads in flight.  A thread owns four consecutive columns of one row; a
+// pure stream over the partial buffer, so its job is to keep enough loads in
+// flight.  Partials are FP32, or BF16 / FP16 widened exactly on load.  A thread owns four consecutive columns of one row; a
 // workgroup owns a run of consecutive rows, i.e. one contiguous block of
 // every split slab.  Per row:
 //   M = max_s lse_s                       (-inf for a row with no key at all)
@@ -21,8 +21,26 @@
 namespace msa {
 namespace {
 
-template <int CPT, int B, int OUT>
-__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ po, int64_t po_split,
+// Four consecutive partial elements of dtype IN at element offset `off`, as
+// FP32 (exact for every input dtype); streamed, so loaded non-temporally.
+template <int IN>
+__device__ __forceinline__ f32x4 load_partial4(const void *base, int64_t off) {
+  if constexpr (IN == MSA_F32) {
+    return __builtin_nontemporal_load((const f32x4 *)((const float *)base + off));
+  } else {
+    if constexpr (IN == MSA_F16) {
+      const f16x4 h = __builtin_nontemporal_load((const f16x4 *)((const uint16_t *)base + off));
+      return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+      const u32x2 w = __builtin_nontemporal_load((const u32x2 *)((const uint16_t *)base + off));
+      return f32x4{bf16_bits_to_f32(w[0] & 0xffffu), bf16_bits_to_f32(w[0] >> 16),
+                   bf16_bits_to_f32(w[1] & 0xffffu), bf16_bits_to_f32(w[1] >> 16)};
+    }
+  }
+}
+
+template <int CPT, int B, int OUT, int IN>
+__global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ po, int64_t po_split,
                                                       int64_t po_row, const float *__restrict__ pl,
                                                       int64_t pl_split, int S, int64_t rows, int dv,
                                                       void *__restrict__ out, int64_t out_row,
@@ -52,7 +70,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
   for (int k = 0; k < NV; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   float W = 0.0f;
   if (M != -INFINITY) {
-    const float *base = po + rr * po_row + cc * CPT;
+    const int64_t base = rr * po_row + cc * CPT;
 #pragma unroll 1
     for (int s0 = 0; s0 < S; s0 += B) {
       if (s0 > 0) {
@@ -66,7 +84,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
         if (l[i] != -INFINITY)
 #pragma unroll
           for (int k = 0; k < NV; ++k)
-            v[i][k] = __builtin_nontemporal_load((const f32x4 *)(base + (int64_t)(s0 + i) * po_split + 4 * k));
+            v[i][k] = load_partial4<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k);
 #pragma unroll
       for (int i = 0; i < B; ++i)
         if (l[i] != -INFINITY) {
@@ -99,8 +117,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
     lse_out[row] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(W) * 0.69314718055994530942f;
 }
 
-template <int CPT, int B>
-hipError_t launch_cb(const float *po, int64_t po_split, int64_t po_row, const float *pl,
+template <int CPT, int B, int IN>
+hipError_t launch_cb(const void *po, int64_t po_split, int64_t po_row, const float *pl,
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
                      int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
   const int tpr = dv / CPT;  // <= 256 (head_dim_v <= 1024)
@@ -109,26 +127,37 @@ hipError_t launch_cb(const float *po, int64_t po_split, int64_t po_row, const fl
   if (blocks == 0) return hipSuccess;
   switch (out_dtype) {
     case MSA_F32:
-      combine_kernel<CPT, B, MSA_F32><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F32, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
     case MSA_BF16:
-      combine_kernel<CPT, B, MSA_BF16><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_BF16, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
     default:
-      combine_kernel<CPT, B, MSA_F16><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F16, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
   }
   return hipGetLastError();
 }
 
+template <int IN>
+hipError_t launch_in(const void *po, int64_t po_split, int64_t po_row, const float *pl,
+                     int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
+                     int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+  if (S <= 4) return launch_cb<4, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+  if (S <= 8) return launch_cb<4, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+  return launch_cb<4, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+}
+
 }  // namespace
 
-hipError_t launch_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
-                          int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
-                          int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
-  if (S <= 4) return launch_cb<4, 4>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-  if (S <= 8) return launch_cb<4, 8>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-  return launch_cb<4, 16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+hipError_t launch_combine(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
+                          const float *pl, int64_t pl_split, int32_t S, int64_t rows, int32_t dv,
+                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+  switch (po_dtype) {
+    case MSA_BF16: return launch_in<MSA_BF16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+    case MSA_F16: return launch_in<MSA_F16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+    default: return launch_in<MSA_F32>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+  }
 }
 
 }  // namespace msa

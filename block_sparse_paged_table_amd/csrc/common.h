@@ -15,6 +15,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -119,6 +120,21 @@ __host__ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   f16x2 v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four consecutive partial-output elements at element offset `off` of a
+// buffer of dtype PO (MSA_F32, or MSA_BF16 / MSA_F16 rounded to nearest even).
+template <int PO>
+__device__ __forceinline__ void store_partial4(void *base, int64_t off, f32x4 v) {
+  if constexpr (PO == MSA_F32) {
+    *(f32x4 *)((float *)base + off) = v;
+  } else if constexpr (PO == MSA_F16) {
+    *(u32x2 *)((uint16_t *)base + off) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+  } else {
+    *(u32x2 *)((uint16_t *)base + off) =
+        u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+              f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+  }
 }
 
 // ---------------------------------------------------------------- plan layout

@@ -44,7 +44,8 @@ struct GroupArgs {
   const int32_t *sel_idx;
   const uint8_t *sel_mask;
   int64_t sel_stride_tok, sel_stride_head;
-  float *partial_o;
+  void *partial_o;             // po_dtype elements
+  int32_t po_dtype;            // MSA_F32, MSA_BF16 or MSA_F16
   int64_t po_row_stride;
   float *partial_lse;
   uint32_t *err_flags;

@@ -11,7 +11,7 @@ namespace msa {
 
 constexpr int kMaxChunk = 256;  // entries per work unit (upper bound)
 
-enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3 };
+enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3, kRouteQ8KV8 = 4 };
 
 // Resolved arguments of the page-selection route.
 struct PageArgs {
@@ -34,7 +34,8 @@ struct PageArgs {
   const int32_t *sel_idx;
   const uint8_t *sel_mask;
   int64_t sel_stride_tok, sel_stride_head;
-  float *partial_o;
+  void *partial_o;             // po_dtype elements
+  int32_t po_dtype;            // MSA_F32, MSA_BF16 or MSA_F16
   int64_t po_split_stride, po_row_stride;
   float *partial_lse;
   int64_t pl_split_stride;
@@ -48,9 +49,9 @@ struct PageArgs {
 hipError_t launch_page_plan(const PageArgs &a, hipStream_t s);
 hipError_t launch_page_attend(const PageArgs &a, hipStream_t s);
 
-hipError_t launch_combine(const float *po, int64_t po_split, int64_t po_row, const float *pl,
-                          int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
-                          int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s);
+hipError_t launch_combine(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
+                          const float *pl, int64_t pl_split, int32_t S, int64_t rows, int32_t dv,
+                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s);
 
 hipError_t launch_nvfp4_dequant(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
                                 int64_t n, hipStream_t s);

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (MSA_BF16, MSA_E4M3, MSA_F16, MSA_F32, MSA_NVFP4, PrefillDesc, msa_combine,
+from . import (MSA_BF16, MSA_E4M3, MSA_F16, MSA_F32, MSA_NVFP4, PrefillDesc, msa_combine_ex,
                msa_prefill_attend, msa_prefill_plan, msa_prefill_workspace_bytes,
                msa_sparse_prefill)
 from .synth import Problem
@@ -27,9 +27,10 @@ class DeviceProblem:
 
     def __init__(self, p: Problem, device: str = "cuda", out_dtype: str = None,
                  partial_o: torch.Tensor = None, partial_lse: torch.Tensor = None,
-                 po_row_pad: int = 0, order_slice_tokens: int = 0):
+                 po_row_pad: int = 0, order_slice_tokens: int = 0, partial_dtype: str = "f32"):
         self.p = p
         self.order_slice_tokens = order_slice_tokens
+        self.partial_dtype = partial_dtype
         dev = torch.device(device)
         self.device = dev
         self.q = p.q.to(dev)
@@ -55,12 +56,13 @@ class DeviceProblem:
         self.sel_mask = p.sel_mask.to(dev)
         S, rows, dv = p.num_splits, p.num_rows, p.d_v
         if partial_o is None:
-            partial_o = torch.empty((S, rows, dv + po_row_pad), dtype=torch.float32, device=dev)
+            partial_o = torch.empty((S, rows, dv + po_row_pad), dtype=OUT_TORCH[partial_dtype],
+                                    device=dev)
         if partial_lse is None:
             partial_lse = torch.empty((S, rows), dtype=torch.float32, device=dev)
         # caller-provided buffers must hold every (split, row) the kernels write
         if (partial_o.dim() != 3 or partial_o.shape[0] < S or partial_o.shape[1] < rows
-                or partial_o.shape[2] < dv or partial_o.dtype != torch.float32):
+                or partial_o.shape[2] < dv or partial_o.dtype != OUT_TORCH[partial_dtype]):
             raise ValueError(f"partial_o {tuple(partial_o.shape)} too small for {(S, rows, dv)}")
         if partial_lse.dim() != 2 or partial_lse.shape[0] < S or partial_lse.shape[1] < rows:
             raise ValueError(f"partial_lse {tuple(partial_lse.shape)} too small for {(S, rows)}")
@@ -96,6 +98,7 @@ class DeviceProblem:
             po_row_stride=self.partial_o.stride(1),
             partial_lse=self.partial_lse.data_ptr(), pl_split_stride=self.partial_lse.stride(0),
             err_flags=self.err.data_ptr(), order_slice_tokens=self.order_slice_tokens,
+            partial_dtype=DTYPE_CODE[self.partial_dtype],
         )
         if self.k_sf is not None:
             sb = _bstrides(self.k_sf)
@@ -116,9 +119,9 @@ class DeviceProblem:
 
     def combine(self, stream=None, lse: bool = True):
         p = self.p
-        msa_combine(self.partial_o, self.partial_lse, p.num_splits, p.num_rows, p.d_v, self.out,
-                    self.lse if lse else None, po_row_stride=self.partial_o.stride(1),
-                    stream=stream)
+        msa_combine_ex(self.partial_o, self.partial_lse, p.num_splits, p.num_rows, p.d_v, self.out,
+                       self.lse if lse else None, po_row_stride=self.partial_o.stride(1),
+                       stream=stream)
 
     def run(self, stream=None):
         self.prefill(stream)

@@ -112,7 +112,8 @@ typedef struct msa_prefill_desc {
     const void *k_cache;
     const void *v_cache;
     int32_t kv_dtype;          /* F32 (with Q F32), BF16 (with Q BF16),
-                                  F16 (with Q F16), NVFP4 (with Q E4M3) */
+                                  F16 (with Q F16), NVFP4 or E4M3 (with Q
+                                  E4M3; E4M3 = per-tensor scaled FP8 cache) */
     int64_t kv_stride_page_bytes;
     int64_t kv_stride_tok_bytes;
     int64_t kv_stride_head_bytes;
@@ -141,10 +142,11 @@ typedef struct msa_prefill_desc {
     int64_t sel_stride_tok;
     int64_t sel_stride_head;
 
-    /* outputs: partial_o[s*po_split_stride + row*po_row_stride + c] (FP32,
-     * c < head_dim_v) and partial_lse[s*pl_split_stride + row].  An empty
-     * split gets lse = -inf and an unspecified partial_o row. */
-    float *partial_o;
+    /* outputs: partial_o[s*po_split_stride + row*po_row_stride + c] (of
+     * partial_dtype, c < head_dim_v) and partial_lse[s*pl_split_stride + row]
+     * (FP32).  An empty split gets lse = -inf and an unspecified partial_o
+     * row.  partial_o must be 16-byte aligned, its strides multiples of 4. */
+    void *partial_o;
     int64_t po_split_stride;
     int64_t po_row_stride;
     float *partial_lse;
@@ -157,6 +159,11 @@ typedef struct msa_prefill_desc {
      * value from the problem's shape.  Results are bitwise independent of it:
      * every (row, split) partial is computed on its own. */
     int32_t order_slice_tokens;
+
+    /* dtype of partial_o: F32 (0, the default), or BF16 / F16 (rounded to
+     * nearest even) to halve the partial bytes; not for F32 queries.  FP16
+     * partials need |v_scale * v| < 65504. */
+    int32_t partial_dtype;
 } msa_prefill_desc;
 
 /* Workspace needed by msa_prefill_plan/_attend for this problem (bytes).
@@ -190,14 +197,24 @@ msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *workspace, size_t
  *   partial_lse [s*pl_split_stride + row]                    FP32
  *   out         [row*out_row_stride + c]  out_dtype F32, BF16 or F16 (RNE)
  *   lse         [row]                     FP32, nullable
- * partial_o, out and their strides must be 16-byte aligned and head_dim_v a
- * multiple of 4 (<= 512).
+ * partial_o must be 16-byte aligned with strides that are multiples of 4,
+ * out aligned to 4 elements with a row stride that is a multiple of 4, and
+ * head_dim_v a multiple of 4 (<= 1024).
  */
 msa_status msa_combine(const float *partial_o, int64_t po_split_stride, int64_t po_row_stride,
                        const float *partial_lse, int64_t pl_split_stride,
                        int32_t num_splits, int64_t num_rows, int32_t head_dim_v,
                        void *out, int32_t out_dtype, int64_t out_row_stride,
                        float *lse, void *stream);
+
+/* msa_combine for partial buffers of dtype partial_dtype (F32, BF16 or F16;
+ * the pages' K1 keeps BF16/FP16 partials -- MiniMax-AI/MSA PR 21, section
+ * "Combine").  Elements are widened to FP32 exactly; same layout rules. */
+msa_status msa_combine_ex(const void *partial_o, int32_t partial_dtype, int64_t po_split_stride,
+                          int64_t po_row_stride, const float *partial_lse, int64_t pl_split_stride,
+                          int32_t num_splits, int64_t num_rows, int32_t head_dim_v,
+                          void *out, int32_t out_dtype, int64_t out_row_stride,
+                          float *lse, void *stream);
 
 /* Exact NVFP4 dequantisation used by the attention kernel, as a standalone
  * device routine (MiniMax-AI/MSA PR 21, section "Build the prefill for

@@ -50,6 +50,11 @@ def _desc(**over):
 
 def test_workspace_query_accepts_valid_descriptor():
     assert msa.msa_prefill_workspace_bytes(_desc()) > 0
+    # FP8 queries with an FP8 cache (per-tensor scaled) and 16-bit partials
+    fp8 = dict(q_dtype=msa.MSA_E4M3, kv_dtype=msa.MSA_E4M3, q_stride_tok=256, q_stride_head=64,
+               kv_stride_page_bytes=128 * 64, kv_stride_tok_bytes=64, kv_stride_head_bytes=64)
+    for pd in (msa.MSA_F32, msa.MSA_BF16, msa.MSA_F16):
+        assert msa.msa_prefill_workspace_bytes(_desc(partial_dtype=pd, **fp8)) > 0
 
 
 @pytest.mark.parametrize("over,status", [
@@ -65,6 +70,8 @@ def test_workspace_query_accepts_valid_descriptor():
     (dict(po_row_stride=32), msa.MsaError),
     (dict(q_dtype=msa.MSA_E4M3, kv_dtype=msa.MSA_NVFP4, head_dim_qk=128, head_dim_v=128,
           q_stride_tok=512, q_stride_head=128), msa.MsaError),  # NVFP4 without scales
+    (dict(partial_dtype=7), msa.MsaError),                  # unknown partial dtype
+    (dict(partial_dtype=msa.MSA_F16), msa.MsaError),        # FP32 queries take FP32 partials
 ])
 def test_host_validation_rejects(over, status):
     with pytest.raises(status) as ei:
@@ -108,6 +115,9 @@ def test_combine_validation():
     assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 4, 8, 126, FAKE, msa.MSA_BF16, 128, None, None) == 1
     assert lib.msa_combine(FAKE, 0, 128, FAKE, 0, 4, 8, 128, FAKE, 7, 128, None, None) == 1
     assert lib.msa_combine(FAKE + 4, 0, 128, FAKE, 0, 4, 8, 128, FAKE, 0, 128, None, None) == 1
+    # typed partials: F32 / BF16 / F16 only
+    assert lib.msa_combine_ex(FAKE, 3, 0, 128, FAKE, 0, 4, 8, 128, FAKE, 0, 128, None, None) == 1
+    assert lib.msa_combine_ex(FAKE, msa.MSA_F16, 0, 128, FAKE, 0, 4, 0, 128, FAKE, 0, 128, None, None) == 0
 
 
 def test_status_strings():

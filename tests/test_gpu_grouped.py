@@ -43,6 +43,24 @@ def test_grouped_small_all_rows(Hq, Hkv, d):
     _parity(_mb(31, Hq=Hq, Hkv=Hkv, d=d))
 
 
+@pytest.mark.parametrize("pd", ["f16", "bf16"])
+def test_grouped_16bit_partials(pd):
+    """16-bit partial storage on the grouped route: the rounding of the FP32
+    partials bit for bit, within the storage floor of the oracle's."""
+    p = _mb(35)
+    dp = DeviceProblem(p, partial_dtype=pd)
+    dp.run()
+    dp32 = DeviceProblem(p)
+    dp32.run()
+    torch.cuda.synchronize()
+    assert torch.equal(dp.partial_lse, dp32.partial_lse)
+    live = dp32.partial_lse > -float("inf")
+    assert torch.equal(dp.partial_o[live], dp32.partial_o[live].to(dp.partial_o.dtype))
+    ref = oracle.prefill_rows(p)
+    po, pl, _, _ = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, ref, stored=pd)
+
+
 def test_grouped_contiguous_cache_and_f32_output():
     _parity(_mb(32, interleaved=False), out_dtype="f32")
 

@@ -58,6 +58,27 @@ def test_combine_matches_oracle(S, rows, dv):
         assert torch.equal(o16, out32.to(dt))
 
 
+@pytest.mark.parametrize("S,rows,dv", [(16, 1000, 128), (3, 257, 64), (40, 130, 256)])
+@pytest.mark.parametrize("pdt", [torch.float16, torch.bfloat16])
+def test_combine_16bit_partials(S, rows, dv, pdt):
+    """msa_combine_ex on BF16 / FP16 partials equals the oracle's combine of
+    the same values widened to FP64, at FP32-combine accuracy."""
+    po, pl = synth.random_partials(200 + S, S, rows, dv, empty_frac=0.2, all_empty_rows=3)
+    po16 = po.to(pdt)
+    ref_out, ref_lse = oracle.combine(po16.double().numpy(), pl.numpy())
+    out = torch.empty((rows, dv), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    msa.msa_combine_ex(po16.cuda(), pl.cuda(), S, rows, dv, out, lse)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(l), empty)
+    assert np.all(o[empty] == 0.0) and not np.signbit(o[empty]).any()
+    fin = ~empty
+    assert np.abs(l[fin] - ref_lse[fin]).max() < 2e-6 * max(1.0, np.abs(ref_lse[fin]).max())
+    assert np.abs(o[fin] - ref_out[fin]).max() < 2e-6 * max(1.0, np.abs(ref_out).max())
+
+
 def test_combine_strided_buffers():
     """Wider row pitch, a split stride larger than the slab, and an output
     pitch: other entries stay untouched."""

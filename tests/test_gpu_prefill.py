@@ -15,7 +15,7 @@ import torch
 from block_sparse_paged_table_amd import synth
 from block_sparse_paged_table_amd.runner import DeviceProblem
 import oracle
-from parity import check_combined, check_partials, gpu_rows
+from parity import check_combined, check_partials, gpu_rows, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,8 @@ def test_tiny_fp32_config_all_rows():
 
 @pytest.mark.parametrize("qd,kd,d", [("bf16", "bf16", 128), ("f16", "f16", 128),
                                      ("bf16", "bf16", 64), ("f16", "f16", 64),
-                                     ("f32", "f32", 128), ("e4m3", "nvfp4", 128)])
+                                     ("f32", "f32", 128), ("e4m3", "nvfp4", 128),
+                                     ("e4m3", "e4m3", 128), ("e4m3", "e4m3", 64)])
 def test_small_all_rows(qd, kd, d):
     p = _small(11, q_dtype=qd, kv_dtype=kd, d=d, Hq=8, Hkv=2)
     _full_parity(p)
@@ -86,6 +87,35 @@ def test_ordering_slices_bitwise_identical(Hq, Hkv, qd, kd):
         assert torch.equal(dp.partial_lse, ref.partial_lse), st
         assert torch.equal(dp.partial_o[live], ref.partial_o[live]), st
         assert torch.equal(dp.out, ref.out) and torch.equal(dp.lse, ref.lse), st
+
+
+@pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "nvfp4"),
+                                   ("e4m3", "e4m3")])
+@pytest.mark.parametrize("pd", ["f16", "bf16"])
+def test_16bit_partials(qd, kd, pd):
+    """BF16 / FP16 partial storage: partials within the storage-rounding floor
+    of the oracle's; the combine of those partials equals the oracle's combine
+    of the same (widened) values; LSEs stay FP32."""
+    p = _small(23, q_dtype=qd, kv_dtype=kd, Hq=8, Hkv=2, out_dtype="f32")
+    dp = _run(p, partial_dtype=pd)
+    assert dp.partial_o.dtype == (torch.float16 if pd == "f16" else torch.bfloat16)
+    ref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, ref, stored=pd)
+    po = np.where(np.isfinite(pl)[..., None], po, 0.0)  # empty splits' rows are unspecified
+    own_out, own_lse = oracle.combine(po.reshape(-1, p.num_splits, p.d_v).transpose(1, 0, 2),
+                                      pl.reshape(-1, p.num_splits).T)
+    own_out = own_out.reshape(out.shape)
+    own_lse = own_lse.reshape(lse.shape)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(own_lse))
+    fin = np.isfinite(own_lse)
+    assert rel_l2(out, own_out) <= 1e-5 and np.abs(out - own_out).max() <= 1e-5
+    assert np.abs(lse[fin] - own_lse[fin]).max() <= 1e-5
+    # same kernel, FP32 partials: the 16-bit ones are their rounding
+    dp32 = _run(p)
+    live = dp32.partial_lse > -float("inf")
+    assert torch.equal(dp.partial_lse, dp32.partial_lse)
+    assert torch.equal(dp.partial_o[live], dp32.partial_o[live].to(dp.partial_o.dtype))
 
 
 def test_fp32_output_and_bf16_output_agree():
