@@ -94,6 +94,10 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens for the CPU oracle leg")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kv-dtype", choices=["nvfp4", "e4m3"], default=None,
+                    help="cache dtype variant of the Q8 workloads (e4m3: the Q8KV8 route)")
+    ap.add_argument("--partial-dtype", choices=["f32", "bf16", "f16"], default="f32",
+                    help="partial_o storage (the workloads specify f32)")
     ap.add_argument("--slice-tokens", type=int, default=0,
                     help="order_slice_tokens of the descriptor (0 = chosen by the library)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -123,17 +127,19 @@ def main():
     torch.cuda.set_device(0)
     cfg = args.config
     log(f"generating {args.sets} input sets of config {cfg} ({synth.CONFIG_NAMES[cfg]})")
-    probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i) for i in range(args.sets)]
+    probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i, kv_dtype=args.kv_dtype)
+             for i in range(args.sets)]
     p0 = probs[0]
     st = workload_stats(p0)
     for p in probs[1:]:  # rotated sets share the output buffers: same geometry only
         assert (p.total_q, p.num_rows, p.num_splits, p.d_v) == \
             (p0.total_q, p0.num_rows, p0.num_splits, p0.d_v), "input sets differ in shape"
     # one partial buffer / output shared by all sets (the biggest allocations)
-    dps = [DeviceProblem(probs[0], order_slice_tokens=args.slice_tokens)]
+    pd = args.partial_dtype
+    dps = [DeviceProblem(probs[0], order_slice_tokens=args.slice_tokens, partial_dtype=pd)]
     for p in probs[1:]:
         dps.append(DeviceProblem(p, partial_o=dps[0].partial_o, partial_lse=dps[0].partial_lse,
-                                 order_slice_tokens=args.slice_tokens))
+                                 order_slice_tokens=args.slice_tokens, partial_dtype=pd))
     for dp in dps[1:]:
         dp.out, dp.lse = dps[0].out, dps[0].lse
     torch.cuda.synchronize()
@@ -175,8 +181,10 @@ def main():
     out_b = dp.out.element_size()
     kv_bytes = sum(tensor_bytes(t) for t in (dp.k, dp.v) if t is not None)
     kv_bytes += sum(tensor_bytes(t) for t in (dp.k_sf, dp.v_sf) if t is not None)
-    attn_bytes = 4 * dv * st["nonempty"] + 4 * st["nonempty"] + tensor_bytes(dp.q) + kv_bytes
-    comb_bytes = 4 * dv * st["nonempty"] + 4 * rows * S + out_b * rows * dv + 4 * rows
+    pe = dp.partial_o.element_size()
+    wname = p.name + ("" if pd == "f32" else f"+{pd}_partials")
+    attn_bytes = pe * dv * st["nonempty"] + 4 * st["nonempty"] + tensor_bytes(dp.q) + kv_bytes
+    comb_bytes = pe * dv * st["nonempty"] + 4 * rows * S + out_b * rows * dv + 4 * rows
     attn_tflops = st["flops"] / (attn_ms * 1e-3) / 1e12
     attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
     comb_gbs = comb_bytes / (comb_ms * 1e-3) / 1e9
@@ -186,11 +194,11 @@ def main():
         kname = "k1_page_attend" if p.unit_tokens == p.page_size else "k_grouped_attend"
         roof = dict(kernel=kname, bound="hbm", achieved=round(attn_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4),
-                    traffic=recorded_traffic(kname, p.name), alg_bytes=attn_bytes)
+                    traffic=recorded_traffic(kname, wname), alg_bytes=attn_bytes)
     else:
         roof = dict(kernel="combine_kernel", bound="hbm", achieved=round(comb_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(comb_gbs / HBM_PEAK_GBS, 4),
-                    traffic=recorded_traffic("combine_kernel", p.name), alg_bytes=comb_bytes)
+                    traffic=recorded_traffic("combine_kernel", wname), alg_bytes=comb_bytes)
 
     cpu = None
     if not args.no_cpu:
@@ -216,7 +224,8 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": mfma_dtype, "data": "synthetic",
-        "config": {"workload": p.name, "description": p.description, "total_q": p.total_q,
+        "config": {"workload": wname,
+                   "description": p.description, "partial_dtype": pd, "total_q": p.total_q,
                    "Hq": p.Hq, "Hkv": p.Hkv, "head_dim": p.d_qk, "page_size": p.page_size,
                    "slots": p.num_slots, "input_sets": len(dps)},
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4),
@@ -227,7 +236,7 @@ def main():
                       "flops": st["flops"], "visible_keys": st["n_visible"]},
         "combine": {"gbs": round(comb_gbs, 1), "hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                     "alg_bytes": comb_bytes,
-                    "traffic": recorded_traffic("combine_kernel", p.name)},
+                    "traffic": recorded_traffic("combine_kernel", wname)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

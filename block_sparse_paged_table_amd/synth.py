@@ -310,9 +310,16 @@ CONFIG_NAMES = (
 )
 
 
-def make_config(idx: int, seed: Optional[int] = None) -> Problem:
-    """Synthetic stand-ins for the pages' workloads, seed 1000 + idx."""
+def make_config(idx: int, seed: Optional[int] = None, kv_dtype: Optional[str] = None) -> Problem:
+    """Synthetic stand-ins for the pages' workloads, seed 1000 + idx.
+
+    ``kv_dtype="e4m3"`` turns the two NVFP4-cache workloads (2 and 4) into
+    their FP8-cache (Q8KV8) variants: same shapes, selections and values
+    before quantisation."""
     seed = 1000 + idx if seed is None else seed
+    if kv_dtype not in (None, "nvfp4", "e4m3") or (kv_dtype == "e4m3" and idx not in (2, 4)):
+        raise ValueError(f"no {kv_dtype} variant of workload {idx}")
+    fp8 = kv_dtype == "e4m3"
     if idx == 0:
         return build_page_problem(
             name=CONFIG_NAMES[0], seed=seed, ctx_lens=[0], chunk_lens=[512],
@@ -329,11 +336,11 @@ def make_config(idx: int, seed: Optional[int] = None) -> Problem:
         )
     if idx == 2:
         return build_page_problem(
-            name=CONFIG_NAMES[2], seed=seed, ctx_lens=[0], chunk_lens=[16384],
-            page_size=128, Hq=32, Hkv=2, d=128, num_slots=16, q_dtype="e4m3",
-            kv_dtype="nvfp4", out_dtype="bf16",
-            description="1 x 16384 tokens, page 128, Hkv 2, Hq 32, d 128, E4M3 Q, NVFP4 KV, "
-                        "own + 15 earlier pages per (token, KV head)",
+            name="q8kv8_16k" if fp8 else CONFIG_NAMES[2], seed=seed, ctx_lens=[0],
+            chunk_lens=[16384], page_size=128, Hq=32, Hkv=2, d=128, num_slots=16,
+            q_dtype="e4m3", kv_dtype="e4m3" if fp8 else "nvfp4", out_dtype="bf16",
+            description=f"1 x 16384 tokens, page 128, Hkv 2, Hq 32, d 128, E4M3 Q, "
+                        f"{'E4M3' if fp8 else 'NVFP4'} KV, own + 15 earlier pages per (token, KV head)",
         )
     if idx == 3:
         return make_grouped_page4(seed=seed)
@@ -344,11 +351,13 @@ def make_config(idx: int, seed: Optional[int] = None) -> Problem:
         chunks = rng.choice([128, 256, 512, 1024, 2048, 4096], size=8)
         ctx = rng.integers(8192, 131072, size=8, endpoint=True)
         return build_page_problem(
-            name=CONFIG_NAMES[4], seed=seed + 7919, ctx_lens=[int(c) for c in ctx],
-            chunk_lens=[int(c) for c in chunks], page_size=128, Hq=16, Hkv=1, d=128,
-            num_slots=16, q_dtype="e4m3", kv_dtype="nvfp4", out_dtype="bf16",
+            name="chunked_batch_q8kv8" if fp8 else CONFIG_NAMES[4], seed=seed + 7919,
+            ctx_lens=[int(c) for c in ctx], chunk_lens=[int(c) for c in chunks], page_size=128,
+            Hq=16, Hkv=1, d=128, num_slots=16, q_dtype="e4m3",
+            kv_dtype="e4m3" if fp8 else "nvfp4", out_dtype="bf16",
             description="8 requests, chunks in {128..4096}, context U[8K,128K], page 128, "
-                        "Hkv 1, Hq 16, d 128, E4M3 Q, NVFP4 KV, own + 15 history pages",
+                        f"Hkv 1, Hq 16, d 128, E4M3 Q, {'E4M3' if fp8 else 'NVFP4'} KV, "
+                        "own + 15 history pages",
         )
     raise ValueError(idx)
 
