@@ -28,24 +28,71 @@ namespace {
 
 constexpr uint64_t kInvalidKey = ~0ull;
 
-__device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
-  // n is a power of two; ascending
+// Ascending bitonic sort of n = E * blockDim.x keys held in LDS.  Thread t
+// keeps the keys of sorted positions tE .. tE+E-1 in registers: compare-
+// exchange steps whose partner lies within the thread (stride < E) run in
+// registers; the others exchange through LDS, every thread computing its own
+// new key.  During the sort the LDS copy is laid out position p -> slot
+// (p % E) * nt + p / E, so a wave's accesses hit consecutive slots; the
+// input is taken in that layout too (any input order sorts the same), and
+// the result is written back in plain sorted order.
+template <int E>
+__device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
+  uint64_t r[E];
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int base = t * E;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) r[i] = k[i * nt + t];
   for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    for (int stride = size >> 1; stride >= E; stride >>= 1) {
+      __syncthreads();  // everyone is done reading the previous round
+#pragma unroll
+      for (int i = 0; i < E; ++i) k[i * nt + t] = r[i];
       __syncthreads();
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint64_t a = k[lo], b = k[hi];
-        if ((a > b) == up) {
-          k[lo] = b;
-          k[hi] = a;
+      const int tq = t ^ (stride / E);  // the partner thread (same register i)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int p = base + i, q = p ^ stride;
+        const uint64_t o = k[i * nt + tq];
+        const bool up = (p & size) == 0;
+        const bool keep_min = (p < q) == up;
+        r[i] = keep_min ? (r[i] < o ? r[i] : o) : (r[i] > o ? r[i] : o);
+      }
+    }
+    // strides below E: partners in this thread's registers (compile-time
+    // indices, so the keys stay in registers)
+#pragma unroll
+    for (int st = E >> 1; st >= 1; st >>= 1) {
+      if (st < size) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          if (i & st) continue;
+          const int j = i | st;
+          const bool up = ((base + i) & size) == 0;
+          const uint64_t x = r[i], y = r[j];
+          const bool sw = (x > y) == up;
+          r[i] = sw ? y : x;
+          r[j] = sw ? x : y;
         }
       }
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) k[base + i] = r[i];
+  __syncthreads();
+}
+
+// n: a power of two in [blockDim.x, 16 * blockDim.x]
+__device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
+  switch (n / (int)blockDim.x) {
+    case 1: bitonic_sort_e<1>(k, n); break;
+    case 2: bitonic_sort_e<2>(k, n); break;
+    case 4: bitonic_sort_e<4>(k, n); break;
+    case 8: bitonic_sort_e<8>(k, n); break;
+    default: bitonic_sort_e<16>(k, n); break;
+  }
 }
 
 // Exclusive block-wide scan of one int per thread (blockDim.x <= 1024).
@@ -151,7 +198,9 @@ __global__ void __launch_bounds__(kGPlanThreads) gplan_kernel(const GroupArgs a)
 
   // ---- 4. category keys: (tiles, tokens, index in the (request, unit) order)
   const int G = a.G;
-  for (int e = threadIdx.x; e < npow2; e += kGPlanThreads) {
+  int n2 = kGPlanThreads;  // the union is usually far smaller than npow2
+  while (n2 < total) n2 <<= 1;
+  for (int e = threadIdx.x; e < n2; e += kGPlanThreads) {
     uint64_t key = kInvalidKey;
     if (e < total) {
       const uint32_t m32 = stage[e].z;
@@ -167,7 +216,7 @@ __global__ void __launch_bounds__(kGPlanThreads) gplan_kernel(const GroupArgs a)
     }
     keys[e] = key;
   }
-  bitonic_sort(keys, npow2);
+  bitonic_sort(keys, n2);
 
   // ---- 5. final list: byte offset of the unit's first K/V row, mask, tiles
   for (int e = threadIdx.x; e < total; e += kGPlanThreads) {
