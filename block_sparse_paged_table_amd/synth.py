@@ -298,6 +298,95 @@ def build_page_problem(
 
 
 # ---------------------------------------------------------------------------
+# Paged prefill indexer problems (FP8 queries scored against an FP8 cache).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexProblem:
+    """Queries [total_q, H, d] and a paged cache [pages, page_size, H, d],
+    both per-tensor scaled E4M3; the indexer scores every visible page of
+    every (token, head) row and keeps the top ``top_k``."""
+
+    name: str
+    num_seqs: int
+    H: int
+    d: int
+    page_size: int
+    top_k: int
+    q: torch.Tensor
+    q_seq: torch.Tensor
+    q_pos: torch.Tensor
+    seq_lens: torch.Tensor
+    page_table: torch.Tensor
+    num_phys_pages: int
+    k_cache: torch.Tensor
+    q_scale: float
+    k_scale: float
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+
+def build_index_problem(*, name: str, seed: int, ctx_lens: Sequence[int], chunk_lens: Sequence[int],
+                        page_size: int, H: int, d: int, top_k: int, pad_rows: int = 0,
+                        extra_phys_pages: int = 0, page_bias: float = 0.0,
+                        description: str = "") -> IndexProblem:
+    """Same request geometry as ``build_page_problem`` (bottom-right aligned
+    chunks, one random physical permutation, padding rows at the end).  Values
+    N(0, 1); ``page_bias`` adds a per-(page, head) offset along a random query
+    direction so that some pages score clearly higher than others."""
+    rng = np.random.default_rng(seed)
+    B = len(ctx_lens)
+    seq_lens = np.array([c + n for c, n in zip(ctx_lens, chunk_lens)], dtype=np.int64)
+    pages_per_seq = [(int(x) + page_size - 1) // page_size for x in seq_lens]
+    max_pages = max(pages_per_seq)
+    total_pages = sum(pages_per_seq) + extra_phys_pages
+    perm = rng.permutation(total_pages).astype(np.int32)
+    page_table = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per_seq):
+        page_table[b, :n] = perm[off:off + n]
+        off += n
+    q_seq = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(chunk_lens)]
+                           + [np.zeros(pad_rows, np.int32)])
+    q_pos = np.concatenate([np.arange(c, c + n, dtype=np.int32) for c, n in zip(ctx_lens, chunk_lens)]
+                           + [np.full(pad_rows, -1, np.int32)])
+    total_q = len(q_seq)
+    qf = _randn(rng, (total_q, H, d))
+    kf = _randn(rng, (total_pages, page_size, H, d))
+    if page_bias:
+        u = _randn(rng, (H, d))
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        qf += 2.0 * u[None]
+        kf += (page_bias * rng.standard_normal((total_pages, 1, H, 1))).astype(np.float32) * u[None, None]
+    q8, q_scale = quantize_e4m3_tensor(torch.from_numpy(qf))
+    k8, k_scale = quantize_e4m3_tensor(torch.from_numpy(kf))
+    return IndexProblem(name=name, num_seqs=B, H=H, d=d, page_size=page_size, top_k=top_k,
+                        q=q8.contiguous(), q_seq=torch.from_numpy(q_seq),
+                        q_pos=torch.from_numpy(q_pos),
+                        seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
+                        page_table=torch.from_numpy(page_table), num_phys_pages=total_pages,
+                        k_cache=k8.contiguous(), q_scale=q_scale, k_scale=k_scale, seed=seed,
+                        description=description)
+
+
+def make_index_problem(seed: int = 2000) -> IndexProblem:
+    """The indexer workload measured beside the attention: the 16K-token
+    request of the Q8KV4 workload, 2 indexer heads of dim 128, 16 pages kept."""
+    return build_index_problem(
+        name="index_q8kv8_16k", seed=seed, ctx_lens=[0], chunk_lens=[16384], page_size=128,
+        H=2, d=128, top_k=16, page_bias=1.0,
+        description="1 x 16384 tokens, page 128, 2 indexer heads, d 128, E4M3 Q and cache, top 16 pages")
+
+
+# ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------
 

@@ -10,7 +10,9 @@ over rows); this module only builds it, marshals numpy arrays and exposes:
   * ``prefill_rows(problem, tokens)``: partial outputs / lse per split, their
     LSE combine, and an independent single-pass softmax;
   * ``combine(po, pl)``: the LSE combine on given partials;
-  * ``slot_nonempty(problem)``: which slots contribute at least one key.
+  * ``slot_nonempty(problem)``: which slots contribute at least one key;
+  * ``index_scores(problem)`` / ``topk(scores, k)``: the paged prefill
+    indexer's per-page scores and their top-k selection.
 
 ``bruteforce.py`` holds a second, independent numpy implementation for tiny
 inputs.
@@ -65,6 +67,18 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _IndexProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int), ("total_q", ctypes.c_int), ("H", ctypes.c_int),
+        ("d", ctypes.c_int), ("page_size", ctypes.c_int), ("max_pages", ctypes.c_int),
+        ("pt_stride", ctypes.c_int), ("num_phys_pages", ctypes.c_int),
+        ("q_scale", ctypes.c_double), ("k_scale", ctypes.c_double),
+        ("q_seq", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+    ]
+
+
 def lib():
     global _lib
     with _lock:
@@ -81,6 +95,9 @@ def lib():
             L.orc_prefill_rows.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, P, P, P, P, P, P, P]
             L.orc_prefill_rows.restype = ctypes.c_uint32
             L.orc_slot_nonempty.argtypes = [ctypes.POINTER(_Problem), P]
+            L.orc_index_scores.argtypes = [ctypes.POINTER(_IndexProblem), P]
+            L.orc_index_scores.restype = ctypes.c_uint32
+            L.orc_topk_rows.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_int, P, P]
             L.orc_abi_version.restype = ctypes.c_int
             _lib = L
         return _lib
@@ -242,3 +259,40 @@ def slot_nonempty(problem, keep: Optional[_Keep] = None) -> np.ndarray:
 
 def make_keep(problem) -> _Keep:
     return _Keep(problem)
+
+
+# ------------------------------------------------------------------ indexer
+
+def index_scores(problem):
+    """Per-page indexer scores of an IndexProblem: (scores [total_q, H,
+    max_pages] float64, -inf where the page has no visible key; error bits)."""
+    p = problem
+    q = np.ascontiguousarray(_as_np(p.q), np.uint8)
+    k = np.ascontiguousarray(_as_np(p.k_cache), np.uint8)
+    q_seq = np.ascontiguousarray(_as_np(p.q_seq), np.int32)
+    q_pos = np.ascontiguousarray(_as_np(p.q_pos), np.int32)
+    seq_lens = np.ascontiguousarray(_as_np(p.seq_lens), np.int32)
+    pt = np.ascontiguousarray(_as_np(p.page_table), np.int32)
+    T, H, d = q.shape
+    st = _IndexProblem(num_seqs=len(seq_lens), total_q=T, H=H, d=d, page_size=p.page_size,
+                       max_pages=pt.shape[1], pt_stride=pt.shape[1],
+                       num_phys_pages=p.num_phys_pages, q_scale=p.q_scale, k_scale=p.k_scale,
+                       q_seq=_ptr(q_seq), q_pos=_ptr(q_pos), seq_lens=_ptr(seq_lens),
+                       page_table=_ptr(pt), q=_ptr(q), k=_ptr(k))
+    out = np.empty((T, H, pt.shape[1]), np.float64)
+    err = lib().orc_index_scores(ctypes.byref(st), _ptr(out))
+    return out, int(err)
+
+
+def topk(scores, k: int):
+    """Top-k of each row of ``scores`` [..., n]: (idx [..., k] int32, mask
+    [..., k] uint8); descending score, ties by ascending index, -inf never
+    selected (index -1, mask 0)."""
+    sc = np.ascontiguousarray(np.asarray(scores, np.float64))
+    n = sc.shape[-1]
+    rows = sc.size // max(n, 1)
+    idx = np.empty(sc.shape[:-1] + (k,), np.int32)
+    mask = np.empty(sc.shape[:-1] + (k,), np.uint8)
+    lib().orc_topk_rows(rows, n, _ptr(sc), k, _ptr(idx), _ptr(mask))
+    return idx, mask
+

@@ -411,6 +411,107 @@ void orc_slot_nonempty(const orc_problem *p, uint8_t *nonempty /* [total_q][Hkv]
     }
 }
 
+/* ------------------------------------------------------- prefill indexer */
+
+/* Page scores of the paged prefill indexer (vllm-project/MSA PR 36, sections
+ * "Overview" and "Changes": an FP8-query / FP8-cache scorer whose per-page
+ * score is a max taken over the page, written to a per-(query, head) row of
+ * pages, followed by a top-k over that row).
+ *
+ * Readings (the page gives no formula):
+ *   - score(r, h, j) = q_scale * k_scale * max over the keys t of logical
+ *     page j of request q_seq[r] that are visible to the row (t <= q_pos[r],
+ *     t < seq_len) of sum_d q[r,h,d] * k[t,h,d], with q and k the decoded
+ *     E4M3 values; -inf when no key of the page is visible, for padding
+ *     rows and for pages past the request's table row;
+ *   - query head h scores against cache head h (one indexer head per KV
+ *     head). */
+typedef struct {
+    int num_seqs, total_q, H, d, page_size, max_pages, pt_stride, num_phys_pages;
+    double q_scale, k_scale;
+    const int32_t *q_seq, *q_pos, *seq_lens, *page_table;
+    const uint8_t *q;   /* E4M3 [total_q][H][d] */
+    const uint8_t *k;   /* E4M3 [phys page][page_size][H][d] */
+} orc_index_problem;
+
+/* scores: [total_q][H][max_pages].  Returns ORC_ERR_* bits (QSEQ_RANGE for a
+ * row naming a missing request, PHYS_RANGE for a page with visible keys whose
+ * table entry is outside the cache; both give -inf). */
+uint32_t orc_index_scores(const orc_index_problem *p, double *scores)
+{
+    uint32_t err_all = 0;
+#pragma omp parallel for reduction(| : err_all) schedule(dynamic, 4)
+    for (int r = 0; r < p->total_q; ++r) {
+        int b = p->q_seq[r], pos = p->q_pos[r];
+        int valid = pos >= 0;
+        if (valid && (b < 0 || b >= p->num_seqs)) {
+            err_all |= ORC_ERR_QSEQ_RANGE;
+            valid = 0;
+        }
+        for (int h = 0; h < p->H; ++h) {
+            double *row = scores + ((int64_t)r * p->H + h) * p->max_pages;
+            for (int j = 0; j < p->max_pages; ++j) {
+                row[j] = -INFINITY;
+                if (!valid)
+                    continue;
+                int seq_len = p->seq_lens[b];
+                int t0 = j * p->page_size;
+                int t1 = t0 + p->page_size - 1;     /* last key of the page */
+                if (t1 > pos) t1 = pos;
+                if (t1 > seq_len - 1) t1 = seq_len - 1;
+                if (t1 < t0)
+                    continue;                       /* nothing visible */
+                int phys = p->page_table[(int64_t)b * p->pt_stride + j];
+                if (phys < 0 || phys >= p->num_phys_pages) {
+                    err_all |= ORC_ERR_PHYS_RANGE;
+                    continue;
+                }
+                double best = -INFINITY;
+                for (int t = t0; t <= t1; ++t) {
+                    const uint8_t *kk = p->k + (((int64_t)phys * p->page_size + (t - t0)) * p->H + h) * p->d;
+                    const uint8_t *qq = p->q + ((int64_t)r * p->H + h) * p->d;
+                    double dot = 0.0;
+                    for (int d = 0; d < p->d; ++d)
+                        dot += orc_e4m3_decode(qq[d]) * orc_e4m3_decode(kk[d]);
+                    if (dot > best)
+                        best = dot;
+                }
+                row[j] = p->q_scale * p->k_scale * best;
+            }
+        }
+    }
+    return err_all;
+}
+
+/* Top-k of each of `rows` rows of n scores (reading: the K largest finite
+ * scores in descending order, equal scores by ascending page index; slots
+ * beyond the finite count get index -1 and mask 0). */
+void orc_topk_rows(int64_t rows, int n, const double *scores, int K, int32_t *idx, uint8_t *mask)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *row = scores + r * n;
+        int32_t *oi = idx + r * K;
+        uint8_t *om = mask + r * K;
+        for (int s = 0; s < K; ++s) {
+            int best = -1;
+            for (int j = 0; j < n; ++j) {
+                if (!(row[j] > -INFINITY))
+                    continue;
+                int taken = 0;
+                for (int q = 0; q < s; ++q)
+                    taken |= (oi[q] == j);
+                if (taken)
+                    continue;
+                if (best < 0 || row[j] > row[best])
+                    best = j;                       /* strict: the lower index keeps a tie */
+            }
+            oi[s] = best;
+            om[s] = best >= 0;
+        }
+    }
+}
+
 int orc_abi_version(void) { return 1; }
 
 /* Array forms of the format routines, for the tests. */
