@@ -26,7 +26,8 @@ from typing import Optional
 __all__ = [
     "MSA_F32", "MSA_BF16", "MSA_F16", "MSA_E4M3", "MSA_NVFP4",
     "MSA_ERRF_SEL_RANGE", "MSA_ERRF_PHYS_RANGE", "MSA_ERRF_QSEQ_RANGE", "MSA_ERRF_DUPLICATE",
-    "MsaError", "PrefillDesc", "library", "library_path", "msa_combine_ex",
+    "MsaError", "PrefillDesc", "IndexDesc", "library", "library_path", "msa_combine_ex",
+    "msa_index_scores", "msa_index_topk", "msa_prefill_index",
     "msa_prefill_workspace_bytes", "msa_prefill_plan", "msa_prefill_attend",
     "msa_sparse_prefill", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_device_supported",
     "msa_abi_version",
@@ -83,6 +84,28 @@ class PrefillDesc(ctypes.Structure):
         self.struct_size = ctypes.sizeof(PrefillDesc)
 
 
+class IndexDesc(ctypes.Structure):
+    """Mirror of ``msa_index_desc`` (include/msa.h), field for field."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_seqs", _c_i32), ("total_q", _c_i32), ("num_heads", _c_i32), ("head_dim", _c_i32),
+        ("page_size", _c_i32), ("q_scale", _c_f32), ("k_scale", _c_f32),
+        ("q", _c_p), ("q_stride_tok", _c_i64), ("q_stride_head", _c_i64),
+        ("q_seq", _c_p), ("q_pos", _c_p), ("seq_lens", _c_p),
+        ("k_cache", _c_p), ("kv_stride_page_bytes", _c_i64), ("kv_stride_tok_bytes", _c_i64),
+        ("kv_stride_head_bytes", _c_i64),
+        ("page_table", _c_p), ("page_table_stride", _c_i64), ("max_pages", _c_i32),
+        ("num_phys_pages", _c_i32),
+        ("scores", _c_p), ("score_stride", _c_i64), ("top_k", _c_i32),
+        ("sel_idx", _c_p), ("sel_mask", _c_p), ("sel_stride_tok", _c_i64),
+        ("sel_stride_head", _c_i64), ("err_flags", _c_p),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        self.struct_size = ctypes.sizeof(IndexDesc)
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -97,6 +120,9 @@ _SIGNATURES = [
     ("msa_combine_ex", ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64,
                                       _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     ("msa_nvfp4_dequant_e4m3", ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p]),
+    ("msa_index_scores", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
+    ("msa_index_topk", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
+    ("msa_prefill_index", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
     ("msa_device_supported", ctypes.c_int, [ctypes.c_int]),
     ("msa_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("msa_last_error", ctypes.c_char_p, []),
@@ -213,6 +239,18 @@ def msa_combine_ex(partial_o, partial_lse, num_splits: int, num_rows: int, head_
     _check(library().msa_combine_ex(_ptr(partial_o), pdt, pss, prs, _ptr(partial_lse), lss,
                                     num_splits, num_rows, head_dim_v, _ptr(out), odt, ors,
                                     _ptr(lse), _stream(stream)))
+
+
+def msa_index_scores(desc: IndexDesc, stream=None):
+    _check(library().msa_index_scores(ctypes.byref(desc), _stream(stream)))
+
+
+def msa_index_topk(desc: IndexDesc, stream=None):
+    _check(library().msa_index_topk(ctypes.byref(desc), _stream(stream)))
+
+
+def msa_prefill_index(desc: IndexDesc, stream=None):
+    _check(library().msa_prefill_index(ctypes.byref(desc), _stream(stream)))
 
 
 def msa_nvfp4_dequant_e4m3(codes, scales, out, stream=None):

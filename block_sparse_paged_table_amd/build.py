@@ -16,7 +16,7 @@ LIB = os.path.join(LIBDIR, "libmsa.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "plan.hip", "attend_page.hip", "combine.hip", "plan_grouped.hip",
-           "attend_grouped.hip"]
+           "attend_grouped.hip", "index.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 # Packed-FP32 instructions are disabled: ordinary float code only.
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",

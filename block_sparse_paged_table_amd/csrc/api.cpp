@@ -11,6 +11,7 @@
 
 #include "grouped.h"
 #include "launch.h"
+#include "index.h"
 
 using namespace msa;
 
@@ -322,6 +323,80 @@ msa_status hip_status(hipError_t e, const char *what) {
   return ok();
 }
 
+// Validated arguments of the indexer.  need_topk: the selection outputs are
+// used (msa_index_topk / msa_prefill_index).
+msa_status resolve_index(const msa_index_desc *d, bool need_topk, IndexArgs *r) {
+  if (!d) return fail(MSA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size != sizeof(msa_index_desc))
+    return fail(MSA_ERR_INVALID_ARG, "struct_size %u != %zu (ABI mismatch)", d->struct_size,
+                sizeof(msa_index_desc));
+  if (d->num_seqs < 1 || d->total_q < 0 || d->num_heads < 1 || d->max_pages < 1 ||
+      d->num_phys_pages < 1)
+    return fail(MSA_ERR_INVALID_ARG, "bad sizes");
+  if ((int64_t)d->total_q * d->num_heads >= (1ll << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "too many (token, head) rows");
+  if (d->page_size != 128) return fail(MSA_ERR_UNSUPPORTED, "indexer is built for page_size 128");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "indexer head_dim must be 64 or 128");
+  if (d->max_pages > kIndexMaxPages)
+    return fail(MSA_ERR_UNSUPPORTED, "max_pages %d > %d", d->max_pages, kIndexMaxPages);
+  if (d->page_table_stride < d->max_pages) return fail(MSA_ERR_INVALID_ARG, "page_table_stride < max_pages");
+  if (!(d->q_scale > 0.0f) || !std::isfinite(d->q_scale) || !(d->k_scale > 0.0f) || !std::isfinite(d->k_scale))
+    return fail(MSA_ERR_INVALID_ARG, "q_scale and k_scale must be finite and > 0");
+  if (!d->scores || d->score_stride < d->max_pages || !aligned(d->scores, 4))
+    return fail(MSA_ERR_INVALID_ARG, "scores must be a 4-byte aligned buffer with score_stride >= max_pages");
+  {  // inputs (checked for every call: one descriptor serves all three)
+    const void *need[] = {d->q, d->q_seq, d->q_pos, d->seq_lens, d->k_cache, d->page_table};
+    for (const void *p : need)
+      if (!p) return fail(MSA_ERR_INVALID_ARG, "NULL input pointer");
+    if (!aligned(d->q, 16) || d->q_stride_tok % 16 || d->q_stride_head % 16 || d->q_stride_tok < 0 ||
+        d->q_stride_head < 0)
+      return fail(MSA_ERR_INVALID_ARG, "q must be 16-byte aligned with 16-byte aligned strides");
+    if (!aligned(d->k_cache, 16) || d->kv_stride_page_bytes % 16 || d->kv_stride_tok_bytes % 16 ||
+        d->kv_stride_head_bytes % 16)
+      return fail(MSA_ERR_INVALID_ARG, "k_cache and its strides must be 16-byte aligned");
+  }
+  if (need_topk) {
+    if (d->top_k < 1 || d->top_k > 255) return fail(MSA_ERR_INVALID_ARG, "top_k must be in [1, 255]");
+    if (!d->sel_idx || !d->sel_mask) return fail(MSA_ERR_INVALID_ARG, "selection outputs are NULL");
+    if (!aligned(d->sel_idx, 4) || d->sel_stride_tok < 0 || d->sel_stride_head < 0 ||
+        (d->num_heads > 1 && d->sel_stride_head < d->top_k) ||
+        d->sel_stride_tok < (int64_t)d->top_k + (int64_t)(d->num_heads - 1) * d->sel_stride_head)
+      return fail(MSA_ERR_INVALID_ARG, "selection strides overlap");
+  }
+  IndexArgs &a = *r;
+  memset(&a, 0, sizeof(a));
+  a.num_seqs = d->num_seqs;
+  a.total_q = d->total_q;
+  a.H = d->num_heads;
+  a.D = d->head_dim;
+  a.page_size = d->page_size;
+  a.max_pages = d->max_pages;
+  a.num_phys_pages = d->num_phys_pages;
+  a.top_k = d->top_k;
+  a.scale = (float)((double)d->q_scale * d->k_scale);
+  a.q = (const uint8_t *)d->q;
+  a.q_stride_tok = d->q_stride_tok;
+  a.q_stride_head = d->q_stride_head;
+  a.q_seq = d->q_seq;
+  a.q_pos = d->q_pos;
+  a.seq_lens = d->seq_lens;
+  a.k_cache = (const uint8_t *)d->k_cache;
+  a.kv_stride_page = d->kv_stride_page_bytes;
+  a.kv_stride_tok = d->kv_stride_tok_bytes;
+  a.kv_stride_head = d->kv_stride_head_bytes;
+  a.page_table = d->page_table;
+  a.pt_stride = d->page_table_stride;
+  a.scores = d->scores;
+  a.score_stride = d->score_stride;
+  a.sel_idx = d->sel_idx;
+  a.sel_mask = d->sel_mask;
+  a.sel_stride_tok = d->sel_stride_tok;
+  a.sel_stride_head = d->sel_stride_head;
+  a.err_flags = d->err_flags;
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,6 +464,29 @@ msa_status msa_combine(const float *po, int64_t po_split, int64_t po_row, const 
                        int32_t out_dtype, int64_t out_row, float *lse, void *stream) {
   return msa_combine_ex(po, MSA_F32, po_split, po_row, pl, pl_split, num_splits, num_rows, dv, out,
                         out_dtype, out_row, lse, stream);
+}
+
+msa_status msa_index_scores(const msa_index_desc *d, void *stream) {
+  IndexArgs a;
+  msa_status s = resolve_index(d, false, &a);
+  if (s != MSA_OK) return s;
+  return hip_status(launch_index_scores(a, (hipStream_t)stream), "index scores launch");
+}
+
+msa_status msa_index_topk(const msa_index_desc *d, void *stream) {
+  IndexArgs a;
+  msa_status s = resolve_index(d, true, &a);
+  if (s != MSA_OK) return s;
+  return hip_status(launch_index_topk(a, (hipStream_t)stream), "index top-k launch");
+}
+
+msa_status msa_prefill_index(const msa_index_desc *d, void *stream) {
+  IndexArgs a;
+  msa_status s = resolve_index(d, true, &a);
+  if (s != MSA_OK) return s;
+  hipError_t e = launch_index_scores(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_index_topk(a, (hipStream_t)stream);
+  return hip_status(e, "indexer launch");
 }
 
 msa_status msa_nvfp4_dequant_e4m3(const uint8_t *codes, const uint8_t *scales, uint8_t *out,

@@ -1,0 +1,282 @@
+// Paged prefill indexer (vllm-project/MSA PR 36, sections "Overview" and
+// "Changes": an FP8-query, FP8-cache scorer that keeps one score per page --
+// the page's max -- for every (query, head) row, then a top-k over the row),
+// written for gfx950.
+//
+// k_index_scores: one workgroup per (64 query tokens, head, chunk of 16
+// logical pages).  The 64 Q rows live in registers (16 per wave); each page
+// of the chunk that some row of the tile can see is copied into LDS
+// (double-buffered, the next page's loads in flight while the current one is
+// scored), and every wave computes S^T = K Q^T for its 16 rows with FP8 MFMA
+// (exact E4M3 products, FP32 accumulation), masks keys the row cannot see
+// (t > q_pos, t >= seq_len), and reduces each row's max over the page's 128
+// keys.  Scores collect in LDS and leave as contiguous row segments.  A tile
+// whose tokens belong to several requests scores each request's pages in
+// turn.
+//
+// k_index_topk: one wave per (token, head) row; the row's page scores sit in
+// registers and top_k rounds of a wave-wide arg-max (ties: lower page) pick
+// the selection.
+#include "index.h"
+
+namespace msa {
+namespace {
+
+constexpr int IT = 256;     // threads per workgroup
+constexpr int ITQ = 64;     // query tokens per workgroup
+constexpr int IPC = 16;     // logical pages per workgroup
+constexpr int IPAGE = 128;  // tokens per page
+
+template <int D> struct IGeom {
+  static constexpr int RB = D;              // bytes per K row (E4M3)
+  static constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  static constexpr int LANE_CH = CPR / 4;   // chunks of a row one lane holds
+  static constexpr int KCH = IPAGE * CPR / IT;  // chunks per thread per page
+  static constexpr int PAGE_BYTES = IPAGE * RB;
+};
+
+// Byte offset of chunk c of K row `key` in LDS, XOR-swizzled so that the 16
+// rows an MFMA operand reads fall into different banks.
+template <int D> __device__ __forceinline__ int ik_off(int key, int c) {
+  using Gm = IGeom<D>;
+  return key * Gm::RB + ((c ^ (key & (Gm::CPR - 1))) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ void load_kpage(const IndexArgs &a, int phys, int h, u32x4 *r) {
+  using Gm = IGeom<D>;
+  const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)h * a.kv_stride_head;
+#pragma unroll
+  for (int it = 0; it < Gm::KCH; ++it) {
+    const int q = it * IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
+    r[it] = *(const u32x4 *)(kb + key * a.kv_stride_tok + c * 16);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_kpage(uint8_t *sk, const u32x4 *r) {
+  using Gm = IGeom<D>;
+#pragma unroll
+  for (int it = 0; it < Gm::KCH; ++it) {
+    const int q = it * IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
+    *(u32x4 *)(sk + ik_off<D>(key, c)) = r[it];
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(IT, 2) k_index_scores(const IndexArgs a) {
+  using Gm = IGeom<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][Gm::PAGE_BYTES];
+  __shared__ float sScore[ITQ][IPC + 1];
+  __shared__ int sRowB[ITQ], sRowLast[ITQ];
+  __shared__ int sReq[ITQ], sReqLast[ITQ];
+  __shared__ int sNreq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+  const int tok0 = blockIdx.x * ITQ, h = blockIdx.y, j0 = blockIdx.z * IPC;
+  const int npg = min(IPC, a.max_pages - j0);
+
+  // ---- rows of the tile: request and last visible position (-1: none)
+  if (tid < ITQ) {
+    const int tok = tok0 + tid;
+    int b = -1, last = -1;
+    if (tok < a.total_q) {
+      const int pos = a.q_pos[tok], bb = a.q_seq[tok];
+      if (pos >= 0) {
+        if (bb < 0 || bb >= a.num_seqs) {
+          if (a.err_flags && h == 0 && blockIdx.z == 0) atomicOr(a.err_flags, MSA_ERRF_QSEQ_RANGE);
+        } else {
+          b = bb;
+          last = min(pos, a.seq_lens[bb] - 1);
+          if (last < 0) b = -1;
+        }
+      }
+    }
+    sRowB[tid] = b;
+    sRowLast[tid] = last;
+  }
+  for (int i = tid; i < ITQ * (IPC + 1); i += IT) (&sScore[0][0])[i] = -INFINITY;
+  __syncthreads();
+  if (tid == 0) {  // the distinct requests of the tile, in order of appearance
+    int nr = 0;
+    for (int r = 0; r < ITQ; ++r) {
+      const int b = sRowB[r];
+      if (b < 0) continue;
+      int k = 0;
+      while (k < nr && sReq[k] != b) ++k;
+      if (k == nr) {
+        sReq[nr] = b;
+        sReqLast[nr] = sRowLast[r];
+        ++nr;
+      } else {
+        sReqLast[k] = max(sReqLast[k], sRowLast[r]);
+      }
+    }
+    sNreq = nr;
+  }
+  __syncthreads();
+
+  // ---- this lane's Q row (row wave*16 + n of the tile), its quarter of d
+  const int rho = wave * 16 + n;
+  const int my_b = sRowB[rho], my_last = sRowLast[rho];
+  u32x4 qr[Gm::LANE_CH];
+  {
+    const int tok = my_b >= 0 ? tok0 + rho : 0;  // rows that see nothing read token 0
+    const uint8_t *qp = a.q + (int64_t)tok * a.q_stride_tok + (int64_t)h * a.q_stride_head + grp * (Gm::RB / 4);
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) qr[c] = *(const u32x4 *)(qp + c * 16);
+  }
+
+  const int nreq = sNreq;
+  for (int ri = 0; ri < nreq; ++ri) {
+    const int cb = sReq[ri];
+    const int lastmax = sReqLast[ri];
+    // pages of this chunk that some row of request cb can see
+    const int jn = min(npg, lastmax / IPAGE - j0 + 1);
+    if (jn <= 0) continue;
+    const int32_t *ptrow = a.page_table + (int64_t)cb * a.pt_stride + j0;
+    auto phys_of = [&](int jj) {
+      const int p = ptrow[jj];
+      return (p >= 0 && p < a.num_phys_pages) ? p : -1;
+    };
+    u32x4 kr[Gm::KCH];
+    int phys_next = phys_of(0);
+    if (phys_next >= 0) load_kpage<D>(a, phys_next, h, kr);
+    for (int jj = 0; jj < jn; ++jj) {
+      const int phys = phys_next;
+      uint8_t *sk = sK[jj & 1];
+      if (phys >= 0) store_kpage<D>(sk, kr);
+      __syncthreads();
+      if (jj + 1 < jn) {
+        phys_next = phys_of(jj + 1);
+        if (phys_next >= 0) load_kpage<D>(a, phys_next, h, kr);
+      }
+      if (phys < 0) {
+        if (a.err_flags && tid == 0) atomicOr(a.err_flags, MSA_ERRF_PHYS_RANGE);
+        continue;  // scores stay -inf
+      }
+      // ---- S^T = K Q^T: lane holds keys 16t + 4grp + i of row n
+      f32x4 acc[IPAGE / 16];
+#pragma unroll
+      for (int t = 0; t < IPAGE / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < Gm::LANE_CH; ++c)
+#pragma unroll
+        for (int t = 0; t < IPAGE / 16; ++t) {
+          const u32x4 k4 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * Gm::LANE_CH + c));
+          acc[t] = mfma_fp8(u32x2{k4[0], k4[1]}, u32x2{qr[c][0], qr[c][1]}, acc[t]);
+          acc[t] = mfma_fp8(u32x2{k4[2], k4[3]}, u32x2{qr[c][2], qr[c][3]}, acc[t]);
+        }
+      // ---- max over the keys this row sees
+      const int jabs = j0 + jj;
+      const int vis_to = (my_b == cb) ? my_last - jabs * IPAGE : -1;  // last visible in-page key
+      float m = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < IPAGE / 16; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[t][i]);
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (grp == 0 && my_b == cb) sScore[rho][jj] = m == -INFINITY ? m : m * a.scale;
+    }
+    __syncthreads();  // the last page's buffer is reused by the next request
+  }
+  __syncthreads();
+
+  // ---- scores out: each row's npg pages are one contiguous segment
+  for (int i = tid; i < ITQ * npg; i += IT) {
+    const int r = i / npg, jj = i - r * npg;
+    const int tok = tok0 + r;
+    if (tok < a.total_q)
+      a.scores[((int64_t)tok * a.H + h) * a.score_stride + j0 + jj] = sScore[r][jj];
+  }
+}
+
+// One wave per (token, head) row: NPL page scores per lane (page i*64+lane).
+template <int NPL>
+__global__ void __launch_bounds__(256) k_index_topk(const IndexArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.total_q * a.H) return;
+  const int tok = (int)(row / a.H), h = (int)(row - (int64_t)tok * a.H);
+  const float *sr = a.scores + row * a.score_stride;
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = i * 64 + lane;
+    v[i] = j < a.max_pages ? sr[j] : -INFINITY;
+  }
+  int32_t *oi = a.sel_idx + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+  uint8_t *om = a.sel_mask + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+  bool done = false;  // wave-uniform
+  for (int s = 0; s < a.top_k; ++s) {
+    float bv = -INFINITY;
+    int bj = 0x7fffffff;
+    if (!done) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (v[i] > bv) {  // ascending pages: a tie keeps the lower one
+          bv = v[i];
+          bj = i * 64 + lane;
+        }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oj = __shfl_xor(bj, off);
+        if (ov > bv || (ov == bv && oj < bj)) {
+          bv = ov;
+          bj = oj;
+        }
+      }
+      done = !(bv > -INFINITY);
+    }
+    if (done) {
+      if (lane == 0) {
+        oi[s] = -1;
+        om[s] = 0;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (i * 64 + lane == bj) v[i] = -INFINITY;
+    if (lane == 0) {
+      oi[s] = bj;
+      om[s] = 1;
+    }
+  }
+}
+
+__global__ void k_index_zero(uint32_t *err) { *err = 0u; }
+
+}  // namespace
+
+hipError_t launch_index_scores(const IndexArgs &a, hipStream_t s) {
+  if (a.err_flags) k_index_zero<<<1, 1, 0, s>>>(a.err_flags);
+  if (a.total_q == 0) return hipGetLastError();
+  dim3 grid((unsigned)((a.total_q + ITQ - 1) / ITQ), (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
+  if (a.D == 64)
+    k_index_scores<64><<<grid, IT, 0, s>>>(a);
+  else
+    k_index_scores<128><<<grid, IT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.total_q * a.H;
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (a.max_pages <= 128)
+    k_index_topk<2><<<blocks, 256, 0, s>>>(a);
+  else if (a.max_pages <= 512)
+    k_index_topk<8><<<blocks, 256, 0, s>>>(a);
+  else
+    k_index_topk<kIndexMaxPages / 64><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -7,7 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (MSA_BF16, MSA_E4M3, MSA_F16, MSA_F32, MSA_NVFP4, PrefillDesc, msa_combine_ex,
+from . import (MSA_BF16, MSA_E4M3, MSA_F16, MSA_F32, MSA_NVFP4, IndexDesc, PrefillDesc,
+               msa_combine_ex, msa_index_scores, msa_index_topk, msa_prefill_index,
                msa_prefill_attend, msa_prefill_plan, msa_prefill_workspace_bytes,
                msa_sparse_prefill)
 from .synth import Problem
@@ -129,3 +130,54 @@ class DeviceProblem:
 
     def err_flags(self) -> int:
         return int(self.err.item()) & 0xffffffff
+
+
+class DeviceIndexProblem:
+    """An IndexProblem resident on `device`, with its score and selection
+    buffers (scores [total_q * H, max_pages + score_pad], selections
+    [total_q, H, top_k])."""
+
+    def __init__(self, ip, device: str = "cuda", top_k: int = None, score_pad: int = 0):
+        self.p = ip
+        dev = torch.device(device)
+        self.device = dev
+        self.q = ip.q.to(dev)
+        self.q_seq = ip.q_seq.to(dev)
+        self.q_pos = ip.q_pos.to(dev)
+        self.seq_lens = ip.seq_lens.to(dev)
+        self.page_table = ip.page_table.to(dev)
+        self.k = ip.k_cache.to(dev)
+        self.top_k = top_k or ip.top_k
+        T, H = ip.total_q, ip.H
+        self.scores = torch.empty((T * H, ip.max_pages + score_pad), dtype=torch.float32, device=dev)
+        self.sel_idx = torch.empty((T, H, self.top_k), dtype=torch.int32, device=dev)
+        self.sel_mask = torch.empty((T, H, self.top_k), dtype=torch.uint8, device=dev)
+        self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        kb = _bstrides(self.k)
+        self.desc = IndexDesc(
+            num_seqs=ip.num_seqs, total_q=T, num_heads=H, head_dim=ip.d, page_size=ip.page_size,
+            q_scale=ip.q_scale, k_scale=ip.k_scale,
+            q=self.q.data_ptr(), q_stride_tok=self.q.stride(0), q_stride_head=self.q.stride(1),
+            q_seq=self.q_seq.data_ptr(), q_pos=self.q_pos.data_ptr(),
+            seq_lens=self.seq_lens.data_ptr(),
+            k_cache=self.k.data_ptr(), kv_stride_page_bytes=kb[0], kv_stride_tok_bytes=kb[1],
+            kv_stride_head_bytes=kb[2],
+            page_table=self.page_table.data_ptr(), page_table_stride=self.page_table.stride(0),
+            max_pages=ip.max_pages, num_phys_pages=ip.num_phys_pages,
+            scores=self.scores.data_ptr(), score_stride=self.scores.stride(0), top_k=self.top_k,
+            sel_idx=self.sel_idx.data_ptr(), sel_mask=self.sel_mask.data_ptr(),
+            sel_stride_tok=self.sel_idx.stride(0), sel_stride_head=self.sel_idx.stride(1),
+            err_flags=self.err.data_ptr())
+
+    def scores_only(self, stream=None):
+        msa_index_scores(self.desc, stream)
+
+    def topk(self, stream=None):
+        msa_index_topk(self.desc, stream)
+
+    def run(self, stream=None):
+        msa_prefill_index(self.desc, stream)
+
+    def err_flags(self) -> int:
+        return int(self.err.item()) & 0xffffffff
+

@@ -216,6 +216,67 @@ msa_status msa_combine_ex(const void *partial_o, int32_t partial_dtype, int64_t 
                           void *out, int32_t out_dtype, int64_t out_row_stride,
                           float *lse, void *stream);
 
+/*
+ * Paged prefill indexer (vllm-project/MSA PR 36, sections "Overview",
+ * "Changes" and "Wrapper API"): FP8 queries score every page of their
+ * request against an FP8 paged cache, one score per (query token, head,
+ * logical page), then keep the top_k pages per (token, head) as a selection
+ * the attention entry points take (sel_idx / sel_mask layout of
+ * msa_prefill_desc, one indexer head per KV head).
+ *   score(r, h, j) = q_scale * k_scale * max over the keys t of page j that
+ *                    row r sees (t <= q_pos[r], t < seq_len) of q[r,h] . k[t,h]
+ *                    (FP32 accumulation of exact E4M3 products); -inf if the
+ *                    page has no visible key, for padding rows (q_pos < 0) and
+ *                    for pages past the request's table row.
+ *   top-k:          the top_k largest finite scores of the row in descending
+ *                   order, equal scores by ascending page; slots beyond the
+ *                   finite count get sel_idx -1 and sel_mask 0.
+ * Data errors (q_seq outside [0, num_seqs), a page-table entry outside the
+ * cache for a page with visible keys) give -inf and set *err_flags
+ * (MSA_ERRF_QSEQ_RANGE / MSA_ERRF_PHYS_RANGE), cleared by msa_index_scores.
+ */
+typedef struct msa_index_desc {
+    uint32_t struct_size;      /* = sizeof(msa_index_desc) */
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t num_heads;         /* indexer heads H (query head h reads cache head h) */
+    int32_t head_dim;          /* 64 or 128 */
+    int32_t page_size;         /* 128 */
+    float q_scale;             /* per-tensor E4M3 scales (> 0) */
+    float k_scale;
+    const void *q;             /* E4M3 [total_q][H][head_dim], d contiguous */
+    int64_t q_stride_tok;      /* elements (bytes) */
+    int64_t q_stride_head;
+    const int32_t *q_seq;      /* [total_q] */
+    const int32_t *q_pos;      /* [total_q]; < 0 = padding row */
+    const int32_t *seq_lens;   /* [num_seqs] */
+    const void *k_cache;       /* E4M3, element (page, offset, head, d) at
+                                  p*stride_page + o*stride_tok + h*stride_head + d */
+    int64_t kv_stride_page_bytes;
+    int64_t kv_stride_tok_bytes;
+    int64_t kv_stride_head_bytes;
+    const int32_t *page_table; /* [num_seqs][page_table_stride] logical -> physical */
+    int64_t page_table_stride;
+    int32_t max_pages;         /* <= 2048 */
+    int32_t num_phys_pages;
+    float *scores;             /* [total_q * H][score_stride], row = token * H + h,
+                                  pages 0 .. max_pages-1 written */
+    int64_t score_stride;      /* >= max_pages */
+    int32_t top_k;             /* 1 .. 255 */
+    int32_t *sel_idx;          /* selection out: [r*sel_stride_tok + h*sel_stride_head + s] */
+    uint8_t *sel_mask;         /* same layout */
+    int64_t sel_stride_tok;
+    int64_t sel_stride_head;
+    uint32_t *err_flags;       /* nullable */
+} msa_index_desc;
+
+/* Page scores only (no top-k). */
+msa_status msa_index_scores(const msa_index_desc *d, void *stream);
+/* Top-k of the scores already in d->scores. */
+msa_status msa_index_topk(const msa_index_desc *d, void *stream);
+/* msa_index_scores then msa_index_topk. */
+msa_status msa_prefill_index(const msa_index_desc *d, void *stream);
+
 /* Exact NVFP4 dequantisation used by the attention kernel, as a standalone
  * device routine (MiniMax-AI/MSA PR 21, section "Build the prefill for
  * SM107": the product of an E2M1 code and an E4M3 scale, rounded once to

@@ -149,3 +149,33 @@ def test_rotated_input_sets_share_geometry():
         assert (a.total_q, a.num_rows, a.max_pages) == (b.total_q, b.num_rows, b.max_pages)
         assert np.array_equal(a.seq_lens.numpy(), b.seq_lens.numpy())
         assert not np.array_equal(a.sel_idx.numpy(), b.sel_idx.numpy())
+
+
+def _idesc(**over):
+    d = dict(num_seqs=1, total_q=16, num_heads=2, head_dim=128, page_size=128, q_scale=1.0,
+             k_scale=1.0, q=FAKE, q_stride_tok=256, q_stride_head=128, q_seq=FAKE, q_pos=FAKE,
+             seq_lens=FAKE, k_cache=FAKE, kv_stride_page_bytes=128 * 256, kv_stride_tok_bytes=256,
+             kv_stride_head_bytes=128, page_table=FAKE, page_table_stride=4, max_pages=4,
+             num_phys_pages=4, scores=FAKE, score_stride=4, top_k=3, sel_idx=FAKE, sel_mask=FAKE,
+             sel_stride_tok=6, sel_stride_head=3)
+    d.update(over)
+    return msa.IndexDesc(**d)
+
+
+@pytest.mark.parametrize("over", [
+    dict(head_dim=96), dict(page_size=64), dict(score_stride=3), dict(q_scale=0.0),
+    dict(max_pages=4096, page_table_stride=4096, score_stride=4096), dict(q=FAKE + 8),
+    dict(kv_stride_tok_bytes=200), dict(top_k=0), dict(top_k=300), dict(sel_stride_head=2),
+    dict(sel_stride_tok=5), dict(sel_idx=0), dict(struct_size=4)])
+def test_index_validation_rejects(over):
+    """Indexer descriptors are checked on the host before any launch."""
+    d = _idesc(**{k: v for k, v in over.items() if k != "struct_size"})
+    if "struct_size" in over:
+        d.struct_size = over["struct_size"]
+    lib = msa.library()
+    calls = [lib.msa_prefill_index, lib.msa_index_topk]
+    if not set(over) & {"top_k", "sel_stride_head", "sel_stride_tok", "sel_idx"}:
+        calls.append(lib.msa_index_scores)  # (it does not use the selection outputs)
+    for fn in calls:  # every case is rejected on the host: nothing is launched
+        assert fn(ctypes.byref(d), None) in (1, 2), fn
+
