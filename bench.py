@@ -98,6 +98,8 @@ def main():
                     help="cache dtype variant of the Q8 workloads (e4m3: the Q8KV8 route)")
     ap.add_argument("--partial-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="partial_o storage (the workloads specify f32)")
+    ap.add_argument("--index", action="store_true",
+                    help="time the paged prefill indexer (page scores + top-k) instead")
     ap.add_argument("--slice-tokens", type=int, default=0,
                     help="order_slice_tokens of the descriptor (0 = chosen by the library)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -118,6 +120,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the method shards without exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.index:
+        return bench_index(args)
 
     import torch
     from block_sparse_paged_table_amd import synth
@@ -238,6 +242,84 @@ def main():
                     "alg_bytes": comb_bytes,
                     "traffic": recorded_traffic("combine_kernel", wname)},
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def index_visible_keys(ip):
+    """(token, head) x visible key pairs the indexer scores."""
+    pos = ip.q_pos.numpy().astype(np.int64)
+    sl = ip.seq_lens.numpy().astype(np.int64)
+    seq = ip.q_seq.numpy()
+    last = np.where(pos >= 0, np.minimum(pos, sl[np.clip(seq, 0, len(sl) - 1)] - 1), -1)
+    return int((last + 1).sum()) * ip.H
+
+
+def bench_index(args):
+    """The indexer workload: page scores + top-k per step, rotated inputs."""
+    import torch
+    from block_sparse_paged_table_amd import synth
+    from block_sparse_paged_table_amd.runner import DeviceIndexProblem
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ips = [synth.make_index_problem(seed=2000 + 100 * i) for i in range(args.sets)]
+    devs = [DeviceIndexProblem(ip) for ip in ips]
+    ip = ips[0]
+    for i in range(args.warmup):
+        devs[i % len(devs)].run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        d = devs[i % len(devs)]
+        ev[i][0].record(stream)
+        d.scores_only()
+        ev[i][1].record(stream)
+        d.topk()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms = wall * 1e3 / K
+    nvis = index_visible_keys(ip)
+    flops = 2.0 * ip.d * nvis
+    score_bytes = ip.total_q * ip.H * ip.max_pages * 4
+    sc_tflops = flops / (sc_ms * 1e-3) / 1e12
+    log(f"scores {sc_ms:.4f} ms, top-k {tk_ms:.4f} ms, step(wall) {ms:.4f} ms")
+    cpu = None
+    if not args.no_cpu:
+        import dataclasses
+        import oracle
+        n = min(args.cpu_sample // 4, ip.total_q)
+        toks = np.linspace(0, ip.total_q - 1, n).astype(np.int64)
+        sub = dataclasses.replace(ip, q=ip.q[toks], q_seq=ip.q_seq[toks], q_pos=ip.q_pos[toks])
+        t = time.perf_counter()
+        sc, _ = oracle.index_scores(sub)
+        oracle.topk(sc, ip.top_k)
+        dt = time.perf_counter() - t
+        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        cpu = dict(value=round(2.0 * ip.d * index_visible_keys(sub) / dt / 1e12, 6), unit="TFLOP/s",
+                   cores=cores, kind="oracle",
+                   sample=f"{n} of {ip.total_q} query tokens (evenly spaced), all heads and pages; "
+                          f"{dt:.2f} s, FP64 C oracle, OpenMP")
+    res = {
+        "metric": "prefill indexer page-score TFLOP/s over visible keys (scores + top-k), 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": ip.name, "description": ip.description, "total_q": ip.total_q,
+                   "heads": ip.H, "head_dim": ip.d, "page_size": ip.page_size,
+                   "top_k": ip.top_k, "input_sets": len(devs)},
+        "kernels_ms": {"scores": round(sc_ms, 4), "topk": round(tk_ms, 4)},
+        "roofline": dict(kernel="k_index_scores", bound="mfma", achieved=round(sc_tflops, 2),
+                         peak=MFMA_PEAK_TFLOPS["fp8"], unit="TFLOP/s",
+                         frac=round(sc_tflops / MFMA_PEAK_TFLOPS["fp8"], 4), traffic=None,
+                         alg_bytes=score_bytes + ip.q.numel() + ip.k_cache.numel()),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -210,43 +210,45 @@ __global__ void __launch_bounds__(256) k_index_topk(const IndexArgs a) {
     const int j = i * 64 + lane;
     v[i] = j < a.max_pages ? sr[j] : -INFINITY;
   }
-  int32_t *oi = a.sel_idx + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
-  uint8_t *om = a.sel_mask + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+  // slot s of the result is kept by lane s % 64 (register s / 64) and
+  // written once at the end, one coalesced store per register
+  int32_t res[4] = {-1, -1, -1, -1};
   bool done = false;  // wave-uniform
-  for (int s = 0; s < a.top_k; ++s) {
+  for (int s = 0; s < a.top_k && !done; ++s) {
     float bv = -INFINITY;
     int bj = 0x7fffffff;
-    if (!done) {
 #pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (v[i] > bv) {  // ascending pages: a tie keeps the lower one
-          bv = v[i];
-          bj = i * 64 + lane;
-        }
+    for (int i = 0; i < NPL; ++i)
+      if (v[i] > bv) {  // ascending pages: a tie keeps the lower one
+        bv = v[i];
+        bj = i * 64 + lane;
+      }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) {
-          bv = ov;
-          bj = oj;
-        }
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oj = __shfl_xor(bj, off);
+      if (ov > bv || (ov == bv && oj < bj)) {
+        bv = ov;
+        bj = oj;
       }
-      done = !(bv > -INFINITY);
     }
-    if (done) {
-      if (lane == 0) {
-        oi[s] = -1;
-        om[s] = 0;
-      }
-      continue;
-    }
+    done = !(bv > -INFINITY);
+    if (done) break;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (i * 64 + lane == bj) v[i] = -INFINITY;
-    if (lane == 0) {
-      oi[s] = bj;
-      om[s] = 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (s == k * 64 + lane) res[k] = bj;
+  }
+  int32_t *oi = a.sel_idx + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+  uint8_t *om = a.sel_mask + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = k * 64 + lane;
+    if (s < a.top_k) {
+      oi[s] = res[k];
+      om[s] = res[k] >= 0 ? 1 : 0;
     }
   }
 }
