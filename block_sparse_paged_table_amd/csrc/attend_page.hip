@@ -45,6 +45,7 @@ namespace {
 constexpr int PAGE = 128;
 constexpr int NT = PAGE / 16;  // key tiles of 16 keys
 constexpr int THREADS = 256;
+constexpr bool kPipelineLds = true;  // batch a chunk's LDS operand reads ahead of its MFMAs
 constexpr int NWAVES = THREADS / kWave;
 
 template <int ROUTE> struct RouteInfo;
@@ -317,7 +318,7 @@ __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int
 // PO: dtype of partial_o (MSA_F32, or MSA_BF16 / MSA_F16 to halve the
 // partial bytes; the LSE stays FP32).
 template <int ROUTE, int D, int PO>
-__global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2 : 1))
+__global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3 : (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2 : 1)))
     k1_page_attend(const PageArgs a) {
   using Gm = Geom<ROUTE, D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Gm::LDS];
@@ -442,9 +443,17 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < Gm::LANE_CH; ++c) {
+      // all of this chunk's K fragments are read before its MFMAs (the empty
+      // asm keeps the compiler from sinking the reads next to their uses),
+      // so the LDS latency is paid once per chunk, not once per MFMA pair
+      u32x4 kf[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        kf[t] = *(const u32x4 *)(sK + k_off<ROUTE, D>(key_of<ROUTE>(t, n), grp * Gm::LANE_CH + c));
+      if constexpr (kPipelineLds) __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x4 kr = *(const u32x4 *)(sK + k_off<ROUTE, D>(key_of<ROUTE>(t, n), grp * Gm::LANE_CH + c));
+        const u32x4 kr = kf[t];
         const u32x4 qr = qb[J][c];
         if constexpr (ROUTE == kRouteF32) {
 #pragma unroll
@@ -525,11 +534,12 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 80 * 1024 ? 2
 #pragma unroll
       for (int kb = 0; kb < PAGE / 32; ++kb) {
         const u32x4 pf = {pk[4 * kb], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+        u32x4 vf[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const u32x4 vf = *(const u32x4 *)(sV + vt_off(mt * 16 + n, kb * 4 + grp));
-          o[mt] = mfma_f16(vf, pf, o[mt]);
-        }
+        for (int mt = 0; mt < MT; ++mt) vf[mt] = *(const u32x4 *)(sV + vt_off(mt * 16 + n, kb * 4 + grp));
+        if constexpr (kPipelineLds) __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] = mfma_f16(vf[mt], pf, o[mt]);
       }
     } else {
 #pragma unroll
