@@ -158,7 +158,7 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
                         d->page_table, d->sel_idx, d->sel_mask, d->partial_o, d->partial_lse};
   const char *names[] = {"q", "q_seq", "q_pos", "seq_lens", "k_cache", "v_cache",
                          "page_table", "sel_idx", "sel_mask", "partial_o", "partial_lse"};
-  for (int i = 0; i < 11; ++i)
+  for (int i = 0; i < 11 && d->total_q > 0; ++i)  // an empty batch reads nothing
     if (!need[i]) return fail(MSA_ERR_INVALID_ARG, "%s is NULL", names[i]);
   if (d->sel_stride_tok < d->num_slots || d->sel_stride_head < 0)
     return fail(MSA_ERR_INVALID_ARG, "selection strides too small");

@@ -27,6 +27,8 @@
  *     never cause an out-of-bounds access: the offending unit contributes
  *     nothing and a bit is set in *err_flags (MSA_ERRF_*).
  *   - Strides are in ELEMENTS unless the name ends in _bytes.
+ *   - An empty batch (total_q = 0) is valid: nothing is read or launched
+ *     beyond clearing *err_flags, and its buffers may be NULL.
  *   - Calls on different streams with different workspaces may run
  *     concurrently; a workspace must not be shared by calls in flight.
  */

@@ -171,6 +171,31 @@ def test_error_flags_and_invalid_rows():
     assert dp.err_flags() == 1 | 2 | 4 | 8
 
 
+def test_empty_and_all_padding_batches():
+    """total_q = 0 launches nothing and touches nothing; a batch of padding rows
+    only gives +0 outputs, lse = -inf and every split empty."""
+    p = _small(24, Hq=8, Hkv=2)
+    empty = dataclasses.replace(p, q=p.q[:0], q_seq=p.q_seq[:0], q_pos=p.q_pos[:0],
+                                sel_idx=p.sel_idx[:0], sel_mask=p.sel_mask[:0])
+    dp = DeviceProblem(empty)
+    dp.run()
+    torch.cuda.synchronize()
+    assert dp.err_flags() == 0
+    pad = dataclasses.replace(p, q_pos=torch.full_like(p.q_pos, -1))
+    dp = _run(pad)
+    assert torch.all(torch.isneginf(dp.partial_lse)) and torch.all(torch.isneginf(dp.lse))
+    assert torch.all(dp.out == 0) and not torch.any(torch.signbit(dp.out.float()))
+
+
+@pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("e4m3", "nvfp4")])
+def test_max_slots_255(qd, kd):
+    """The page route's largest slot count (slot ids are 8-bit in the plan):
+    255 slots, most of them empty or later than the own page."""
+    p = _small(25, q_dtype=qd, kv_dtype=kd, Hq=4, Hkv=1, ctx_lens=[3000, 0],
+               chunk_lens=[300, 200], num_slots=255, pad_rows=2)
+    _full_parity(p)
+
+
 def test_physical_permutation_bitwise_invariant():
     p = _small(17, extra_phys_pages=5)
     perm = np.random.default_rng(3).permutation(p.num_phys_pages)
