@@ -39,6 +39,22 @@ __device__ __forceinline__ f32x4 load_partial4(const void *base, int64_t off) {
   }
 }
 
+// Eight consecutive 16-bit partial elements (one 16-byte load) as FP32.
+template <int IN>
+__device__ __forceinline__ void load_partial8(const void *base, int64_t off, f32x4 &lo, f32x4 &hi) {
+  if constexpr (IN == MSA_F16) {
+    const f16x8 h = __builtin_nontemporal_load((const f16x8 *)((const uint16_t *)base + off));
+    lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+  } else {
+    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)base + off));
+    lo = f32x4{bf16_bits_to_f32(w[0] & 0xffffu), bf16_bits_to_f32(w[0] >> 16),
+               bf16_bits_to_f32(w[1] & 0xffffu), bf16_bits_to_f32(w[1] >> 16)};
+    hi = f32x4{bf16_bits_to_f32(w[2] & 0xffffu), bf16_bits_to_f32(w[2] >> 16),
+               bf16_bits_to_f32(w[3] & 0xffffu), bf16_bits_to_f32(w[3] >> 16)};
+  }
+}
+
 template <int CPT, int B, int OUT, int IN>
 __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ po, int64_t po_split,
                                                       int64_t po_row, const float *__restrict__ pl,
@@ -81,10 +97,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ p
       f32x4 v[B][NV];
 #pragma unroll
       for (int i = 0; i < B; ++i)
-        if (l[i] != -INFINITY)
+        if (l[i] != -INFINITY) {
+          if constexpr (IN != MSA_F32 && NV % 2 == 0) {  // 16 bytes per 16-bit load
 #pragma unroll
-          for (int k = 0; k < NV; ++k)
-            v[i][k] = load_partial4<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k);
+            for (int k = 0; k < NV; k += 2)
+              load_partial8<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k, v[i][k], v[i][k + 1]);
+          } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+              v[i][k] = load_partial4<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k);
+          }
+        }
 #pragma unroll
       for (int i = 0; i < B; ++i)
         if (l[i] != -INFINITY) {
@@ -143,6 +166,12 @@ template <int IN>
 hipError_t launch_in(const void *po, int64_t po_split, int64_t po_row, const float *pl,
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
                      int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+  if constexpr (IN != MSA_F32) {  // 8 columns per thread: one 16-byte load per split
+    if (dv % 8 == 0) {
+      if (S <= 4) return launch_cb<8, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+      return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+    }
+  }
   if (S <= 4) return launch_cb<4, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
   if (S <= 8) return launch_cb<4, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
   return launch_cb<4, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
