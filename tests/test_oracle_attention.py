@@ -94,6 +94,54 @@ def test_split_combine_equals_single_pass(seed):
     assert _rel(res["out"], res["out1"]) < TOL
 
 
+def _mb_split(seed, spp, dup_rows=()):
+    """Microblock (4-token unit) selections cut into splits of `spp` slots
+    (the split-k form of the grouped route, 1Cat-vLLM PR 387, section
+    "Purpose": the single-row Page4 route kept as a many-partition
+    fallback).  `dup_rows` repeat slot 2's unit in slot 13 (a later split)."""
+    p = synth.build_microblock_problem(
+        name="mb_split", seed=seed, ctx_len=72, chunk_len=19, pad_rows=2, Hq=4, Hkv=2, d=16,
+        num_slots=16, page_size=16, spare_pages=2)
+    p = dataclasses.replace(p, slots_per_split=spp)
+    if dup_rows:
+        si, sm = p.sel_idx.numpy().copy(), p.sel_mask.numpy().copy()
+        for r in dup_rows:
+            si[r, 0, 13], sm[r, 0, 13] = si[r, 0, 2], 0xF
+        p = dataclasses.replace(p, sel_idx=torch.from_numpy(si), sel_mask=torch.from_numpy(sm))
+    return p
+
+
+@pytest.mark.parametrize("spp", [1, 4, 8])
+def test_microblock_splits_combine_to_one_split(spp):
+    """Merging the per-split partials equals the one-split (spp = K) result,
+    and equals the single softmax over the union of the selected keys."""
+    split = oracle.prefill_rows(_mb_split(40, spp))
+    whole = oracle.prefill_rows(_mb_split(40, 16))
+    assert split["part_lse"].shape[2] == 16 // spp
+    _assert_same_finite(split["lse"], whole["lse"])
+    assert _rel(split["out"], whole["out"]) < TOL
+    _assert_same_finite(split["lse"], split["lse1"])
+    assert _rel(split["out"], split["out1"]) < TOL
+
+
+def test_microblock_split_duplicate_in_later_split():
+    """A unit selected again in a later split is ignored there (first slot
+    wins, over all splits) and flagged."""
+    p = _mb_split(41, 4, dup_rows=(3, 10))
+    a = oracle.prefill_rows(p)
+    b = bruteforce.run(p)
+    assert a["err"] == oracle.ERR_DUPLICATE
+    _assert_same_finite(a["part_lse"], b["part_lse"])
+    fin = np.isfinite(b["part_lse"])
+    assert np.abs(a["part_o"][fin] - b["part_o"][fin]).max() < 1e-12
+    # the repeated slot adds nothing: same result as with that slot masked off
+    sm = p.sel_mask.numpy().copy()
+    sm[[3, 10], 0, 13] = 0
+    c = oracle.prefill_rows(dataclasses.replace(p, sel_mask=torch.from_numpy(sm)))
+    assert c["err"] == 0
+    assert np.array_equal(a["part_o"], c["part_o"]) and np.array_equal(a["part_lse"], c["part_lse"])
+
+
 def test_combine_matches_logaddexp():
     po, pl = synth.random_partials(3, 7, 257, 24, empty_frac=0.3, all_empty_rows=5)
     po = po.numpy().astype(np.float64)
@@ -292,9 +340,11 @@ def _tiny_cases():
         num_slots=8, page_size=8, spare_pages=1)
     yield dataclasses.replace(mb, slots_per_split=2)
     yield _small(seed=28, Hq=4, Hkv=2, d=32, q_dtype="e4m3", kv_dtype="e4m3", num_slots=4)
+    yield _mb_split(29, 4)
+    yield _mb_split(30, 1)
 
 
-@pytest.mark.parametrize("case", list(range(9)))
+@pytest.mark.parametrize("case", list(range(11)))
 def test_bruteforce_agrees(case):
     p = list(_tiny_cases())[case]
     a = oracle.prefill_rows(p)
