@@ -13,6 +13,7 @@ usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -100,6 +101,11 @@ def main():
                     help="partial_o storage (the workloads specify f32)")
     ap.add_argument("--index", action="store_true",
                     help="time the paged prefill indexer (page scores + top-k) instead")
+    ap.add_argument("--workload", choices=["page4_small_chunk"], default=None,
+                    help="a named workload instead of --config (page4_small_chunk: 48 rows, "
+                         "512 microblocks per row in splits, the split-k microblock route)")
+    ap.add_argument("--slots-per-split", type=int, default=0,
+                    help="microblock workloads: slots merged into one split (0 = the workload's)")
     ap.add_argument("--slice-tokens", type=int, default=0,
                     help="order_slice_tokens of the descriptor (0 = chosen by the library)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -130,9 +136,18 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = args.config
-    log(f"generating {args.sets} input sets of config {cfg} ({synth.CONFIG_NAMES[cfg]})")
-    probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i, kv_dtype=args.kv_dtype)
-             for i in range(args.sets)]
+    if args.workload == "page4_small_chunk":
+        log(f"generating {args.sets} input sets of {args.workload}")
+        kw = {"slots_per_split": args.slots_per_split} if args.slots_per_split else {}
+        probs = [synth.make_page4_small_chunk(seed=1005 + 100 * i, **kw) for i in range(args.sets)]
+    else:
+        log(f"generating {args.sets} input sets of config {cfg} ({synth.CONFIG_NAMES[cfg]})")
+        probs = [synth.make_config(cfg, seed=1000 + cfg + 100 * i, kv_dtype=args.kv_dtype)
+                 for i in range(args.sets)]
+        if args.slots_per_split:
+            if probs[0].unit_tokens == probs[0].page_size:
+                sys.exit("--slots-per-split applies to microblock workloads only")
+            probs = [dataclasses.replace(p, slots_per_split=args.slots_per_split) for p in probs]
     p0 = probs[0]
     st = workload_stats(p0)
     for p in probs[1:]:  # rotated sets share the output buffers: same geometry only
@@ -187,6 +202,8 @@ def main():
     kv_bytes += sum(tensor_bytes(t) for t in (dp.k_sf, dp.v_sf) if t is not None)
     pe = dp.partial_o.element_size()
     wname = p.name + ("" if pd == "f32" else f"+{pd}_partials")
+    if args.slots_per_split:
+        wname += f"+{p.num_splits}_splits"
     attn_bytes = pe * dv * st["nonempty"] + 4 * st["nonempty"] + tensor_bytes(dp.q) + kv_bytes
     comb_bytes = pe * dv * st["nonempty"] + 4 * rows * S + out_b * rows * dv + 4 * rows
     attn_tflops = st["flops"] / (attn_ms * 1e-3) / 1e12
@@ -231,7 +248,7 @@ def main():
         "config": {"workload": wname,
                    "description": p.description, "partial_dtype": pd, "total_q": p.total_q,
                    "Hq": p.Hq, "Hkv": p.Hkv, "head_dim": p.d_qk, "page_size": p.page_size,
-                   "slots": p.num_slots, "input_sets": len(dps)},
+                   "slots": p.num_slots, "splits": p.num_splits, "input_sets": len(dps)},
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4),
                        "combine": round(comb_ms, 4)},
         "attention": {"tflops": round(attn_tflops, 2),

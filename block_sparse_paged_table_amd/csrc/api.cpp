@@ -56,12 +56,12 @@ int page_route(const msa_prefill_desc *d) {
   return -1;
 }
 
-// Grouped microblock route (4-token units with per-row bit masks, one split).
+// Grouped microblock route (4-token units with per-row bit masks).  With
+// slots_per_split < num_slots it is the split-k form: every (group, KV head,
+// split) is a work item of its own and writes that split's partials.
 msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   if (d->unit_tokens != 4 || d->page_size % 4)
     return fail(MSA_ERR_UNSUPPORTED, "microblock route needs unit_tokens 4 and page_size %% 4 == 0");
-  if (d->slots_per_split != d->num_slots)
-    return fail(MSA_ERR_UNSUPPORTED, "microblock route writes one split (slots_per_split == num_slots)");
   if (d->num_slots > 512) return fail(MSA_ERR_UNSUPPORTED, "microblock route: at most 512 slots");
   if (d->q_dtype != MSA_F16 || d->kv_dtype != MSA_F16)
     return fail(MSA_ERR_UNSUPPORTED, "microblock route is built for FP16 Q and KV");
@@ -77,7 +77,8 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   if (!aligned(d->k_cache, 16) || !aligned(d->v_cache, 16) || d->kv_stride_page_bytes % 16 ||
       d->kv_stride_tok_bytes % 16 || d->kv_stride_head_bytes % 16)
     return fail(MSA_ERR_INVALID_ARG, "k/v cache and strides must be 16-byte aligned");
-  if (!aligned(d->partial_o, 16) || d->po_row_stride % 4 || d->po_row_stride < d->head_dim_v)
+  if (!aligned(d->partial_o, 16) || d->po_row_stride % 4 || d->po_split_stride % 4 ||
+      d->po_row_stride < d->head_dim_v)
     return fail(MSA_ERR_INVALID_ARG, "partial_o must be 16-byte aligned, row stride >= head_dim_v");
   if (!aligned(d->partial_lse, 4)) return fail(MSA_ERR_INVALID_ARG, "partial_lse misaligned");
   GroupArgs &r = *a;
@@ -95,7 +96,12 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   r.num_phys_pages = d->num_phys_pages;
   r.num_groups = (d->total_q + kGroupTokens - 1) / kGroupTokens;
   r.list_cap = kGroupTokens * d->num_slots;
-  r.sort_n = kGPlanThreads;
+  r.slots_per_split = d->slots_per_split;
+  r.num_splits = d->num_slots / d->slots_per_split;
+  // few groups: one wide planner workgroup per CU finishes sooner; many:
+  // narrow workgroups keep every CU busy
+  r.plan_threads = (int64_t)r.num_groups * r.Hkv <= 256 ? kGPlanThreadsFew : kGPlanThreads;
+  r.sort_n = r.plan_threads;
   while (r.sort_n < r.list_cap) r.sort_n <<= 1;
   const float sm = d->sm_scale > 0.0f ? d->sm_scale : 1.0f / std::sqrt((float)d->head_dim_qk);
   r.scale_log2 = (float)((double)sm * d->q_scale * d->k_scale * 1.4426950408889634);
@@ -119,9 +125,11 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   r.sel_stride_head = d->sel_stride_head;
   r.partial_o = d->partial_o;
   r.po_dtype = d->partial_dtype;
+  r.po_split_stride = d->po_split_stride;
   r.po_row_stride = d->po_row_stride;
   r.partial_lse = d->partial_lse;
-  r.lay = group_layout((int64_t)r.num_groups * r.Hkv, r.list_cap);
+  r.pl_split_stride = d->pl_split_stride;
+  r.lay = group_layout((int64_t)r.num_groups * r.Hkv, r.list_cap, r.num_splits);
   return MSA_OK;
 }
 

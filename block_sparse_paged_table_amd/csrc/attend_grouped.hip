@@ -3,7 +3,7 @@
 // sparse K/V blocks while each row keeps its exact 4-bit mask; inactive row
 // tiles are skipped), written for gfx950.
 //
-// One workgroup per (group of 8 query tokens, KV head).  The group's
+// One workgroup per (group of 8 query tokens, KV head, split).  The group's
 // G query heads per token make 8*G (token, head) rows, cut into 16-row
 // tiles; wave w owns tile w.  The union of the group's microblocks (built by
 // the planner, ordered by category) streams through LDS in batches of 8
@@ -19,9 +19,10 @@
 //   O^T += V^T . P^T  f16 MFMA, P in FP16, V^T built in LDS at load time
 //
 // A tile none of whose rows selected any unit of the batch skips it (the
-// wave-uniform test uses the units' active-tile bits).  The route writes one
-// split: partial_o = O / l * v_scale and lse = m + ln l (or -inf with zeros
-// for a row that sees nothing).
+// wave-uniform test uses the units' active-tile bits).  Each split (the
+// units whose first slot for a row lies in that split's slot range) is an
+// independent softmax: partial_o = O / l * v_scale and lse = m + ln l (or
+// -inf with zeros for a row that sees nothing in the split).
 #include "grouped.h"
 
 namespace msa {
@@ -137,10 +138,11 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
   using Gm = GGeom<D>;
   constexpr int MT = D / 16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Gm::STAGE];
-  const int grp = blockIdx.x, g = blockIdx.y;
+  const int grp = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
   const int64_t li = (int64_t)g * a.num_groups + grp;
-  const int count = ((const int *)(a.ws + a.lay.counts))[li];
-  const uint4 *list = (const uint4 *)(a.ws + a.lay.lists) + li * a.list_cap;
+  const int *soff = (const int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1) + split;
+  const int count = soff[1] - soff[0];
+  const uint4 *list = (const uint4 *)(a.ws + a.lay.lists) + li * a.list_cap + soff[0];
   const int nb = (count + kGUnitsPerBatch - 1) / kGUnitsPerBatch;
 
   const int lane = threadIdx.x & 63;
@@ -255,16 +257,17 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
   lp += __shfl_xor(lp, 16);
   lp += __shfl_xor(lp, 32);
   const int64_t row = (int64_t)tok * a.Hq + h;
-  const int64_t off = row * a.po_row_stride + gl * 4;
+  const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + gl * 4;
+  float *lse_dst = a.partial_lse + (int64_t)split * a.pl_split_stride + row;
   if (l > 0.0f) {
     const float inv = a.v_scale / lp;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, o[mt] * inv);
-    if (gl == 0) a.partial_lse[row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    if (gl == 0) *lse_dst = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   } else {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, f32x4{0.f, 0.f, 0.f, 0.f});
-    if (gl == 0) a.partial_lse[row] = -INFINITY;
+    if (gl == 0) *lse_dst = -INFINITY;
   }
 }
 
@@ -272,7 +275,7 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
 
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;
-  dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv);
+  dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv, (unsigned)a.num_splits);
   switch ((a.D == 256 ? 8 : 0) + a.po_dtype) {
     case 8 + MSA_F32: k_grouped_attend<256, MSA_F32><<<grid, GT, 0, s>>>(a); break;
     case 8 + MSA_BF16: k_grouped_attend<256, MSA_BF16><<<grid, GT, 0, s>>>(a); break;

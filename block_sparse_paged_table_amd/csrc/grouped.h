@@ -6,21 +6,23 @@
 namespace msa {
 
 constexpr int kGroupTokens = 8;        // adjacent query tokens per group
-constexpr int kGPlanThreads = 256;
+constexpr int kGPlanThreads = 256;       // planner workgroup, many groups
+constexpr int kGPlanThreadsFew = 1024;  // planner workgroup when groups are few
 constexpr int kGUnitsPerBatch = 8;     // microblocks per attention batch (32 keys)
 
-// Workspace of the grouped route.  Per (KV head, group): the number of
-// distinct units and a list of up to list_cap entries
-// {K/V byte offset (lo, hi), mask32, active row tiles}.
+// Workspace of the grouped route.  Per (KV head, group): a list of up to
+// list_cap entries {K/V byte offset (lo, hi), mask32, active row tiles},
+// ordered by split, and the num_splits + 1 offsets of the splits' runs in it
+// (split s owns entries [split_off[s], split_off[s + 1])).
 struct GroupLayout {
-  size_t meta, counts, stage, lists, total;
+  size_t meta, split_off, stage, lists, total;
 };
 
-__host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap) {
+__host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, int64_t num_splits) {
   GroupLayout L;
   size_t off = 0;
   L.meta = off;   off = align_up(off + 64 * 4, 256);
-  L.counts = off; off = align_up(off + (size_t)num_lists * 4, 256);
+  L.split_off = off; off = align_up(off + (size_t)num_lists * (num_splits + 1) * 4, 256);
   L.stage = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
   L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
   L.total = off;
@@ -31,8 +33,11 @@ struct GroupArgs {
   int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, unit_tokens, num_slots, max_pages,
       num_phys_pages;
   int32_t num_groups;  // ceil(total_q / kGroupTokens)
-  int32_t sort_n;      // power of two >= kGroupTokens * num_slots and >= kGPlanThreads
+  int32_t plan_threads;  // kGPlanThreads, or kGPlanThreadsFew when at most one planner
+                         // workgroup per CU is launched (latency over throughput)
+  int32_t sort_n;      // power of two >= kGroupTokens * num_slots and >= plan_threads
   int32_t list_cap;    // kGroupTokens * num_slots
+  int32_t num_splits, slots_per_split;  // split s merges slots [s * spp, (s + 1) * spp)
   float scale_log2, v_scale;
   const void *q;
   int64_t q_stride_tok, q_stride_head;
@@ -46,8 +51,9 @@ struct GroupArgs {
   int64_t sel_stride_tok, sel_stride_head;
   void *partial_o;             // po_dtype elements
   int32_t po_dtype;            // MSA_F32, MSA_BF16 or MSA_F16
-  int64_t po_row_stride;
+  int64_t po_split_stride, po_row_stride;  // elements
   float *partial_lse;
+  int64_t pl_split_stride;
   uint32_t *err_flags;
   uint8_t *ws;
   GroupLayout lay;

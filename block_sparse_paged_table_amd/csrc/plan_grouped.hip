@@ -13,14 +13,17 @@
 //      (invalid selections sort to the end);
 //   2. bitonic sort of the keys in LDS;
 //   3. duplicates of a (request, unit, token) beyond the first slot are
-//      dropped and flagged; each distinct (request, unit) gets a 32-bit mask,
-//      4 visible-token bits per token of the group; units no row sees are
-//      dropped; the physical page is looked up and checked;
-//   4. the union is sorted again by (active row tiles, active tokens,
-//      request, unit) so consecutive units share their category and whole
-//      row tiles can skip a batch;
+//      dropped and flagged; the first slot of each (request, unit, token)
+//      names its split (slot / slots_per_split); each distinct (split,
+//      request, unit) gets a 32-bit mask, 4 visible-token bits per token of
+//      the group; units no row sees are dropped; the physical page is looked
+//      up and checked;
+//   4. the union is sorted again by (split, active row tiles, active tokens,
+//      request, unit) so each split's units are contiguous and consecutive
+//      units share their category, letting whole row tiles skip a batch;
 //   5. the group's list is written: {K/V row offset of the unit's first
-//      token in bytes (low, high), mask32, active tiles} per unit.
+//      token in bytes (low, high), mask32, active tiles} per unit, and the
+//      offsets of the splits' runs in it.
 #include "grouped.h"
 
 namespace msa {
@@ -34,8 +37,11 @@ constexpr uint64_t kInvalidKey = ~0ull;
 // registers; the others exchange through LDS, every thread computing its own
 // new key.  During the sort the LDS copy is laid out position p -> slot
 // (p % E) * nt + p / E, so a wave's accesses hit consecutive slots; the
-// input is taken in that layout too (any input order sorts the same), and
-// the result is written back in plain sorted order.
+// input is taken in that layout too (any input order sorts the same).  The
+// result is written back in sorted order with one padding slot after each
+// thread's E keys (position p at p + p / E, see sorted_at): a thread that
+// then walks its own E consecutive positions has its lanes 8 * (E + 1)
+// bytes apart, at most two to an LDS bank, instead of E / 2.
 template <int E>
 __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
   uint64_t r[E];
@@ -80,11 +86,17 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < E; ++i) k[base + i] = r[i];
+  for (int i = 0; i < E; ++i) k[base + t + i] = r[i];
   __syncthreads();
 }
 
-// n: a power of two in [blockDim.x, 16 * blockDim.x]
+// Sorted position p of a bitonic_sort whose threads held 2^sh keys each.
+__device__ __forceinline__ uint64_t sorted_at(const uint64_t *k, int sh, int p) {
+  return k[p + (p >> sh)];
+}
+
+// n: a power of two in [blockDim.x, 16 * blockDim.x]; k holds n + blockDim.x
+// keys (the sorted output is padded)
 __device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
   switch (n / (int)blockDim.x) {
     case 1: bitonic_sort_e<1>(k, n); break;
@@ -95,115 +107,176 @@ __device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
   }
 }
 
-// Exclusive block-wide scan of one int per thread (blockDim.x <= 1024).
-__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int &total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    const int x = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += x;
-    __syncthreads();
-  }
-  total = tmp[blockDim.x - 1];
-  const int r = tmp[t] - v;
-  __syncthreads();
-  return r;
-}
-
-__global__ void __launch_bounds__(kGPlanThreads) gplan_kernel(const GroupArgs a) {
-  extern __shared__ uint64_t keys[];  // npow2 entries
-  __shared__ int scan_tmp[kGPlanThreads];
+template <int NT>
+__global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
+  extern __shared__ uint64_t keys[];  // npow2 + NT entries
   const int grp = blockIdx.x, g = blockIdx.y;
   const int K = a.num_slots;
   const int npow2 = a.sort_n;
   const int tok0 = grp * kGroupTokens;
   uint32_t err = 0;
 
-  // ---- 1. keys
-  for (int e = threadIdx.x; e < npow2; e += kGPlanThreads) {
-    uint64_t key = kInvalidKey;
-    if (e < kGroupTokens * K) {
-      const int tau = e / K, j = e - tau * K;
-      const int tok = tok0 + tau;
-      if (tok < a.total_q) {
-        const int pos = a.q_pos[tok];
-        const int b = a.q_seq[tok];
-        const int64_t so = (int64_t)tok * a.sel_stride_tok + (int64_t)g * a.sel_stride_head + j;
-        const uint32_t mk = a.sel_mask[so];
-        if (pos >= 0 && mk != 0) {
-          if (b < 0 || b >= a.num_seqs) {
-            err |= MSA_ERRF_QSEQ_RANGE;
-          } else {
-            const int u = a.sel_idx[so];
-            if (u < 0 || (int64_t)(u + 1) * a.unit_tokens > (int64_t)a.max_pages * a.page_size) {
-              err |= MSA_ERRF_SEL_RANGE;
-            } else {
-              // visible bits: t = u*4 + i with t <= pos, t < seq_len, bit i set
-              const int last = min(pos, a.seq_lens[b] - 1);
-              const int nvis = min(max(last - u * a.unit_tokens + 1, 0), a.unit_tokens);
-              const uint32_t vis = mk & ((1u << nvis) - 1u) & 0xfu;
-              key = ((uint64_t)b << 41) | ((uint64_t)u << 17) | ((uint64_t)tau << 14) |
-                    ((uint64_t)j << 4) | vis;
-            }
-          }
+  // ---- 1. keys.  Every thread issues all of its loads (the group's 8 token
+  // rows, then 8 tokens x up to 2 slots of selections) before using any.
+  constexpr int JI = (512 + NT - 1) / NT;  // slot iterations per token (K <= 512)
+  int pos_t[kGroupTokens], b_t[kGroupTokens], last_t[kGroupTokens];
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau) {
+    const int tok = min(tok0 + tau, a.total_q - 1);
+    pos_t[tau] = a.q_pos[tok];
+    b_t[tau] = a.q_seq[tok];
+    if (tok0 + tau >= a.total_q) pos_t[tau] = -1;  // past the batch: no row
+  }
+  uint32_t mk[kGroupTokens][JI];
+  int ui[kGroupTokens][JI];
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const int tok = min(tok0 + tau, a.total_q - 1);
+      const int j = min((int)threadIdx.x + i * NT, K - 1);
+      const int64_t so = (int64_t)tok * a.sel_stride_tok + (int64_t)g * a.sel_stride_head + j;
+      mk[tau][i] = a.sel_mask[so];
+      ui[tau][i] = a.sel_idx[so];
+    }
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau) {
+    const int bc = min(max(b_t[tau], 0), a.num_seqs - 1);
+    last_t[tau] = min(pos_t[tau], a.seq_lens[bc] - 1);
+  }
+  for (int e = kGroupTokens * K + threadIdx.x; e < npow2; e += NT) keys[e] = kInvalidKey;
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const int j = threadIdx.x + i * NT;
+      if (j >= K) continue;
+      uint64_t key = kInvalidKey;
+      if (pos_t[tau] >= 0 && mk[tau][i] != 0) {
+        const int b = b_t[tau], u = ui[tau][i];
+        if (b < 0 || b >= a.num_seqs) {
+          err |= MSA_ERRF_QSEQ_RANGE;
+        } else if (u < 0 || (int64_t)(u + 1) * a.unit_tokens > (int64_t)a.max_pages * a.page_size) {
+          err |= MSA_ERRF_SEL_RANGE;
+        } else {
+          // visible bits: t = u*4 + i with t <= pos, t < seq_len, bit i set
+          const int nvis = min(max(last_t[tau] - u * a.unit_tokens + 1, 0), a.unit_tokens);
+          const uint32_t vis = mk[tau][i] & ((1u << nvis) - 1u) & 0xfu;
+          key = ((uint64_t)b << 41) | ((uint64_t)u << 17) | ((uint64_t)tau << 14) |
+                ((uint64_t)j << 4) | vis;
         }
       }
+      keys[tau * K + j] = key;
     }
-    keys[e] = key;
-  }
   bitonic_sort(keys, npow2);
 
-  // ---- 3. distinct units, their masks, physical pages.  Each thread owns a
-  // contiguous run of sorted positions, so scans preserve the sorted order.
-  const int per = npow2 / kGPlanThreads;  // npow2 >= kGPlanThreads
-  const int p0 = threadIdx.x * per;
-  int emit_n = 0;
-  for (int p = p0; p < p0 + per; ++p) {
-    const uint64_t k = keys[p];
-    if (k == kInvalidKey) break;
-    const uint64_t unit_id = k >> 17;
-    if (p > 0 && (keys[p - 1] >> 17) == unit_id) {
-      if ((keys[p - 1] >> 14) == (k >> 14)) err |= MSA_ERRF_DUPLICATE;
-      continue;  // not the unit's first entry
+  // ---- 3. distinct (split, unit) pairs, their masks.  In sorted order,
+  // position p is the first entry of its token in its (request, unit) run
+  // when the previous key has another (request, unit, token): it holds the
+  // token's lowest slot, whose split is the token's split for that unit.
+  // Such an entry leads its (split, unit) pair when no earlier first entry
+  // of the run has the same split; the leader emits the pair with the
+  // visible bits of every first entry of the run in that split.  Positions
+  // are taken strided (p = i * NT + thread), and leaders are
+  // numbered in sorted order by wave ballots.
+  const int per = npow2 / NT;  // npow2 >= NT, per <= 16 (8 * 512 keys)
+  const int sh1 = __builtin_ctz((unsigned)per);
+  const bool one_split = a.num_splits == 1;
+  // slot / slots_per_split as (slot * ceil(2^20 / spp)) >> 20: exact for
+  // slot < 1024 and spp <= 512 (the rounding excess stays below 1 / 1024)
+  const uint32_t split_mul = ((1u << 20) + (uint32_t)a.slots_per_split - 1u) / (uint32_t)a.slots_per_split;
+  auto at = [&](int p) { return sorted_at(keys, sh1, p); };
+  auto split_of = [&](uint64_t k) {
+    return one_split ? 0 : (int)((((uint32_t)(k >> 4) & 0x3ffu) * split_mul) >> 20);
+  };
+  auto tok_bits = [](uint64_t k) { return (uint32_t)(k & 0xfu) << (4 * ((k >> 14) & 7u)); };
+  struct Lead {
+    bool on;
+    int split;
+    uint32_t m32;
+    uint64_t unit;
+  };
+  auto analyze = [&](int p, bool flag_dups) {
+    Lead L{false, 0, 0u, 0ull};
+    const uint64_t k = at(p);
+    if (k == kInvalidKey) return L;
+    const uint64_t unit = k >> 17;
+    const uint64_t kp = p > 0 ? at(p - 1) : kInvalidKey;
+    if ((kp >> 14) == (k >> 14)) {  // a later slot of the same (request, unit, token)
+      if (flag_dups) err |= MSA_ERRF_DUPLICATE;
+      return L;
     }
-    uint32_t m32 = 0;
-    for (int q = p; q < npow2 && (keys[q] >> 17) == unit_id; ++q) {
-      const bool first_of_tok = (q == p) || ((keys[q - 1] >> 14) != (keys[q] >> 14));
-      if (first_of_tok) m32 |= (uint32_t)(keys[q] & 0xfu) << (4 * ((keys[q] >> 14) & 7u));
+    const int sg = split_of(k);
+    if (one_split) {
+      if ((kp >> 17) == unit) return L;  // the run start leads
+    } else {
+      uint64_t kq = kp;
+      for (int q = p - 1; q >= 0 && (kq >> 17) == unit; --q) {
+        const uint64_t kb = q > 0 ? at(q - 1) : kInvalidKey;
+        if ((kb >> 14) != (kq >> 14) && split_of(kq) == sg) return L;  // an earlier first entry
+        kq = kb;
+      }
     }
-    if (m32 != 0) ++emit_n;
+    uint32_t m32 = tok_bits(k);
+    uint64_t last = k;
+    for (int q = p + 1; q < npow2; ++q) {
+      const uint64_t kq = at(q);
+      if ((kq >> 17) != unit) break;
+      if ((kq >> 14) != (last >> 14) && split_of(kq) == sg) m32 |= tok_bits(kq);
+      last = kq;
+    }
+    L.on = m32 != 0u;
+    L.split = sg;
+    L.m32 = m32;
+    L.unit = unit;
+    return L;
+  };
+  constexpr int NW = NT / 64;
+  __shared__ int wave_count[16][NW];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int i = 0; i < per; ++i) {
+    const Lead L = analyze(i * NT + threadIdx.x, true);
+    const uint64_t bal = __ballot(L.on);
+    if (lane == 0) wave_count[i][wv] = __popcll(bal);
   }
-  int total;
-  int wpos = block_exclusive_scan(emit_n, scan_tmp, total);
-  // stage the distinct units' (unit id, mask32) in the workspace staging area
-  const int64_t list_base = ((int64_t)g * a.num_groups + grp) * a.list_cap;
+  __syncthreads();
+  int total = 0;
+  for (int i = 0; i < per; ++i)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += wave_count[i][w];
+  // stage the distinct (split, unit)s: (unit id lo, hi, mask32, split)
+  const int64_t li = (int64_t)g * a.num_groups + grp;
+  const int64_t list_base = li * a.list_cap;
   uint4 *stage = (uint4 *)(a.ws + a.lay.stage) + list_base;
   uint4 *out = (uint4 *)(a.ws + a.lay.lists) + list_base;
-  for (int p = p0; p < p0 + per; ++p) {
-    const uint64_t k = keys[p];
-    if (k == kInvalidKey) break;
-    const uint64_t unit_id = k >> 17;
-    if (p > 0 && (keys[p - 1] >> 17) == unit_id) continue;
-    uint32_t m32 = 0;
-    for (int q = p; q < npow2 && (keys[q] >> 17) == unit_id; ++q) {
-      const bool first_of_tok = (q == p) || ((keys[q - 1] >> 14) != (keys[q] >> 14));
-      if (first_of_tok) m32 |= (uint32_t)(keys[q] & 0xfu) << (4 * ((keys[q] >> 14) & 7u));
+  {
+    int base = 0;
+    for (int i = 0; i < per; ++i) {
+      int before = base;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w < wv) before += wave_count[i][w];
+        base += wave_count[i][w];
+      }
+      const Lead L = analyze(i * NT + threadIdx.x, false);
+      const uint64_t bal = __ballot(L.on);
+      if (L.on) {
+        const int off = before + __popcll(bal & ((1ull << lane) - 1ull));
+        stage[off] = make_uint4((uint32_t)L.unit, (uint32_t)(L.unit >> 32), L.m32, (uint32_t)L.split);
+      }
     }
-    if (m32 == 0) continue;
-    stage[wpos++] = make_uint4((uint32_t)unit_id, (uint32_t)(unit_id >> 32), m32, 0u);
   }
   __syncthreads();
 
-  // ---- 4. category keys: (tiles, tokens, index in the (request, unit) order)
+  // ---- 4. category keys: (split, tiles, tokens, index in the staged order)
   const int G = a.G;
-  int n2 = kGPlanThreads;  // the union is usually far smaller than npow2
+  int n2 = NT;  // the union is usually far smaller than npow2
   while (n2 < total) n2 <<= 1;
-  for (int e = threadIdx.x; e < n2; e += kGPlanThreads) {
+  for (int e = threadIdx.x; e < n2; e += NT) {
     uint64_t key = kInvalidKey;
     if (e < total) {
-      const uint32_t m32 = stage[e].z;
+      const uint4 st = stage[e];
+      const uint32_t m32 = st.z;
       uint32_t toks = 0, tiles = 0;
 #pragma unroll
       for (int tau = 0; tau < kGroupTokens; ++tau)
@@ -212,32 +285,59 @@ __global__ void __launch_bounds__(kGPlanThreads) gplan_kernel(const GroupArgs a)
           const int r0 = tau * G, r1 = tau * G + G - 1;  // rows of this token
           tiles |= (1u << (r0 >> 4)) | (1u << (r1 >> 4));
         }
-      key = ((uint64_t)tiles << 40) | ((uint64_t)toks << 32) | (uint64_t)e;
+      key = ((uint64_t)st.w << 48) | ((uint64_t)tiles << 40) | ((uint64_t)toks << 32) | (uint64_t)e;
     }
     keys[e] = key;
   }
   bitonic_sort(keys, n2);
+  const int sh2 = __builtin_ctz((unsigned)(n2 / NT));
 
   // ---- 5. final list: byte offset of the unit's first K/V row, mask, tiles
-  for (int e = threadIdx.x; e < total; e += kGPlanThreads) {
-    const uint64_t ck = keys[e];
-    const uint4 st = stage[(int)(ck & 0xffffffffu)];
-    const uint64_t unit_id = (uint64_t)st.x | ((uint64_t)st.y << 32);
-    const int b = (int)(unit_id >> 24), u = (int)(unit_id & 0xffffffu);
-    const int t0 = u * a.unit_tokens;
-    const int phys = a.page_table[(int64_t)b * a.pt_stride + t0 / a.page_size];
-    uint4 r;
-    if (phys < 0 || phys >= a.num_phys_pages) {
-      err |= MSA_ERRF_PHYS_RANGE;
-      r = make_uint4(0u, 0u, 0u, 0u);  // mask 0: contributes nothing
-    } else {
-      const int64_t off = (int64_t)phys * a.kv_stride_page + (int64_t)(t0 % a.page_size) * a.kv_stride_tok +
-                          (int64_t)g * a.kv_stride_head;
-      r = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), st.z, (uint32_t)(ck >> 40));
+  // (four entries per thread in flight: their page-table loads overlap)
+  for (int e0 = threadIdx.x; e0 < total; e0 += 4 * NT) {
+    uint64_t ck[4];
+    uint4 st[4];
+    int phys[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ck[i] = sorted_at(keys, sh2, min(e0 + i * NT, total - 1));
+      st[i] = stage[(int)(ck[i] & 0xffffffffu)];
     }
-    out[e] = r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t unit_id = (uint64_t)st[i].x | ((uint64_t)st[i].y << 32);
+      const int b = (int)(unit_id >> 24), u = (int)(unit_id & 0xffffffu);
+      phys[i] = a.page_table[(int64_t)b * a.pt_stride + u * a.unit_tokens / a.page_size];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i * NT;
+      if (e >= total) continue;
+      const uint64_t unit_id = (uint64_t)st[i].x | ((uint64_t)st[i].y << 32);
+      const int t0 = (int)(unit_id & 0xffffffu) * a.unit_tokens;
+      uint4 r;
+      if (phys[i] < 0 || phys[i] >= a.num_phys_pages) {
+        err |= MSA_ERRF_PHYS_RANGE;
+        r = make_uint4(0u, 0u, 0u, 0u);  // mask 0: contributes nothing
+      } else {
+        const int64_t off = (int64_t)phys[i] * a.kv_stride_page +
+                            (int64_t)(t0 % a.page_size) * a.kv_stride_tok + (int64_t)g * a.kv_stride_head;
+        r = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), st[i].z,
+                       (uint32_t)(ck[i] >> 40) & 0xffu);
+      }
+      out[e] = r;
+    }
   }
-  if (threadIdx.x == 0) ((int *)(a.ws + a.lay.counts))[(int64_t)g * a.num_groups + grp] = total;
+  // split s owns sorted entries [first with split >= s, first with split >= s + 1)
+  int *soff = (int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1);
+  for (int sp = threadIdx.x; sp <= a.num_splits; sp += NT) {
+    int lo = 0, hi = total;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(sorted_at(keys, sh2, mid) >> 48) < sp) lo = mid + 1; else hi = mid;
+    }
+    soff[sp] = lo;
+  }
   if (err) atomicOr(a.err_flags, err);
 }
 
@@ -249,7 +349,11 @@ hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s) {
   gplan_zero<<<1, 1, 0, s>>>(a.err_flags);
   if (a.num_groups == 0) return hipGetLastError();
   dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv);
-  gplan_kernel<<<grid, kGPlanThreads, (size_t)a.sort_n * 8, s>>>(a);
+  const size_t lds = ((size_t)a.sort_n + a.plan_threads) * 8;
+  if (a.plan_threads == kGPlanThreadsFew)
+    gplan_kernel<kGPlanThreadsFew><<<grid, kGPlanThreadsFew, lds, s>>>(a);
+  else
+    gplan_kernel<kGPlanThreads><<<grid, kGPlanThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -593,6 +593,24 @@ def make_grouped_page4(seed: int = 1003, chunk_len: int = 8120, pad_rows: int = 
     )
 
 
+def make_page4_small_chunk(seed: int = 1005, chunk_len: int = 48, ctx_len: int = 150288,
+                           num_slots: int = 512, slots_per_split: int = 32) -> Problem:
+    """A chunk below 64 rows on the grouped Page4 geometry (Hq 6 on one KV
+    head of dim 256, 4-token units, 512 units per row, FP16), with the
+    selections cut into num_slots / slots_per_split splits: the split-k form
+    of the microblock route for small chunks (1Cat-vLLM PR 387, section
+    "Purpose": the single-row route kept as a many-partition fallback; the
+    pages' kernel benchmark runs at 24,240 and 150,288 tokens of context)."""
+    p = build_microblock_problem(
+        name="page4_small_chunk", seed=seed, ctx_len=ctx_len, chunk_len=chunk_len, pad_rows=0,
+        Hq=6, Hkv=1, d=256, num_slots=num_slots,
+        description=f"{chunk_len} rows at positions {ctx_len}.., block 16, unit 4, Hq 6 on 1 "
+                    f"latent KV head of dim 256, {num_slots} units/row in "
+                    f"{num_slots // slots_per_split} splits, FP16",
+    )
+    return dataclasses.replace(p, slots_per_split=slots_per_split)
+
+
 def random_partials(seed: int, num_splits: int, num_rows: int, d_v: int,
                     empty_frac: float = 0.1, all_empty_rows: int = 3):
     """Random FP32 partials for a standalone combine test.

@@ -89,7 +89,18 @@ typedef struct msa_prefill_desc {
                                   4-bit mask) */
     int32_t num_slots;         /* K selections per (token, KV head) */
     int32_t slots_per_split;   /* slots merged into one partial; the number of
-                                  partial splits is num_slots / slots_per_split */
+                                  partial splits is num_slots / slots_per_split,
+                                  split s holding slots [s*spp, (s+1)*spp).
+                                  Page selections: 1 (one partial per page).
+                                  Microblocks: any divisor of num_slots; below
+                                  num_slots this is the split-k form for small
+                                  chunks (1Cat-vLLM PR 387, section "Purpose":
+                                  the single-row route kept as a
+                                  many-partition fallback), every (8-token
+                                  group, KV head, split) then being its own
+                                  work item.  A unit selected again by a row
+                                  in a later slot is ignored there, whichever
+                                  split that slot is in. */
     float sm_scale;            /* softmax scale; 0 selects 1/sqrt(head_dim_qk) */
     float q_scale;             /* per-tensor dequant scales (1 for float data): */
     float k_scale;             /*   logit = sm_scale*q_scale*k_scale * (q . k) */
@@ -175,8 +186,9 @@ msa_status msa_prefill_workspace_bytes(const msa_prefill_desc *d, size_t *bytes)
 /* Step 1: build the work plan in `workspace` from the selections: the
  * inverted index of queries per (request, logical page, KV head) for page
  * selections (MiniMax-AI/MSA PR 21, section "K1": one workgroup per (page,
- * head, query split)), or the per-group unit union for microblock
- * selections (1Cat-vLLM PR 387, section "Purpose": deterministic planner).
+ * head, query split)), or the per-group unit union, ordered by split, for
+ * microblock selections (1Cat-vLLM PR 387, section "Purpose":
+ * deterministic planner).
  * Writes lse = -inf for every empty split and sets *err_flags. */
 msa_status msa_prefill_plan(const msa_prefill_desc *d, void *workspace, size_t workspace_bytes,
                             void *stream);

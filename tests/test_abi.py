@@ -57,6 +57,29 @@ def test_workspace_query_accepts_valid_descriptor():
         assert msa.msa_prefill_workspace_bytes(_desc(partial_dtype=pd, **fp8)) > 0
 
 
+_MICROBLOCK = dict(page_size=16, unit_tokens=4, q_dtype=msa.MSA_F16, kv_dtype=msa.MSA_F16,
+                  head_dim_qk=128, head_dim_v=128, num_q_heads=6, q_stride_tok=6 * 128,
+                  q_stride_head=128, kv_stride_page_bytes=16 * 256, kv_stride_tok_bytes=256,
+                  kv_stride_head_bytes=256, num_slots=8, sel_stride_tok=8, sel_stride_head=8,
+                  max_pages=64, page_table_stride=64, po_split_stride=96 * 128, po_row_stride=128,
+                  pl_split_stride=96, total_q=1024)
+
+
+@pytest.mark.parametrize("spp", [8, 4, 2, 1])
+def test_microblock_route_takes_any_split_count(spp):
+    """Microblock selections may be cut into num_slots / slots_per_split splits
+    (the split-k form of the grouped route); the workspace grows with them."""
+    n = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=spp, **_MICROBLOCK))
+    assert n > 0
+    if spp < 8:
+        assert n > msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **_MICROBLOCK))
+
+
+def test_microblock_route_rejects_uneven_splits():
+    with pytest.raises(msa.MsaError):
+        msa.msa_prefill_workspace_bytes(_desc(slots_per_split=3, **_MICROBLOCK))
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(q=0), msa.MsaError),
     (dict(num_q_heads=5, num_kv_heads=2), msa.MsaError),

@@ -1,6 +1,7 @@
 """GPU parity of the grouped microblock route (4-token units with exact
-per-row masks, 8-token groups, one split) against the FP64 oracle, through
-the C ABI.  Tolerances are defined in tests/parity.py."""
+per-row masks, 8-token groups; one split, or several in its split-k form)
+against the FP64 oracle, through the C ABI.  Tolerances are defined in
+tests/parity.py."""
 import dataclasses
 
 import numpy as np
@@ -127,3 +128,51 @@ def test_grouped_full_size_config_sampled():
     rows = (pad[:, None] * p.Hq + np.arange(p.Hq)[None]).ravel()
     o = dp.out[torch.as_tensor(rows, device="cuda")].float().cpu().numpy()
     assert np.all(o == 0.0) and not np.signbit(o).any()
+
+
+# ------------------------------------------------------------ split-k form
+
+@pytest.mark.parametrize("spp", [1, 4, 12, 16, 48])
+def test_grouped_splits(spp):
+    """slots_per_split < num_slots: every (group, KV head, split) is its own
+    softmax over the units whose first slot for a row lies in the split."""
+    p = dataclasses.replace(_mb(37), slots_per_split=spp)
+    dp = _parity(p)
+    assert dp.partial_lse.shape[0] == 48 // spp
+
+
+def test_grouped_split_duplicate_in_later_split():
+    p = dataclasses.replace(_mb(38, num_slots=24), slots_per_split=4)
+    si, sm = p.sel_idx.numpy().copy(), p.sel_mask.numpy().copy()
+    for r in (3, 20, 44):
+        si[r, 0, 13], sm[r, 0, 13] = si[r, 0, 2], 0xF   # repeated in split 3: ignored
+    si[9, 0, 19], sm[9, 0, 19] = si[9, 0, 17], 0x5       # repeated within split 4
+    p = dataclasses.replace(p, sel_idx=torch.from_numpy(si), sel_mask=torch.from_numpy(sm))
+    dp = _parity(p)
+    assert dp.err_flags() == 8
+
+
+def test_grouped_splits_ragged_early_rows_and_padding():
+    # the chunk starts at position 0: early rows leave most splits empty
+    _parity(dataclasses.replace(_mb(39, ctx_len=0, chunk_len=29, pad_rows=5, num_slots=16),
+                                slots_per_split=2))
+
+
+def test_grouped_splits_bitwise_repeatable():
+    p = dataclasses.replace(_mb(40), slots_per_split=8)
+    dp = DeviceProblem(p)
+    snaps = []
+    for _ in range(3):
+        dp.partial_o.fill_(0)
+        dp.run()
+        torch.cuda.synchronize()
+        snaps.append((dp.partial_o.clone(), dp.partial_lse.clone(), dp.out.clone()))
+    for s in snaps[1:]:
+        assert all(torch.equal(x, y) for x, y in zip(snaps[0], s))
+
+
+def test_page4_small_chunk_workload():
+    """The small-chunk workload at its full size (48 rows, 512 units per row,
+    16 splits), every row against the oracle."""
+    p = synth.make_page4_small_chunk(ctx_len=24240)
+    _parity(p)
