@@ -22,7 +22,9 @@
 // scores in exactly the register layout the B operand of O^T = V^T P^T
 // needs (the key order inside a 32-key block is chosen to make that true),
 // and leaves each lane holding one output row for the epilogue, so no
-// cross-lane shuffles are needed except the 4-lane row reductions.
+// cross-lane shuffles are needed except the 4-lane row reductions (and, for
+// FP32 partials, one swap between half rows that turns the stores into
+// whole 128-byte lines).
 //
 // Routes (Q / KV storage -> MFMA types):
 //   F32   : f32 / f32    -> QK 16x16x4 f32, PV 16x16x4 f32
@@ -92,6 +94,11 @@ template <int ROUTE, int D> __device__ __forceinline__ int k_off(int key, int c)
 __device__ __forceinline__ int vt_off(int dv, int c) { return dv * (PAGE * 2) + ((c ^ (dv & 15)) << 4); }
 
 template <typename T> __device__ __forceinline__ T ld(const void *p) { return *(const T *)p; }
+
+// x of lane (l ^ 8) within each 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ uint32_t swap_half_row(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+}
 
 // f(integral_constant<J>) for J = 0 .. N-1, unrolled at compile time.
 template <typename F, int... Js>
@@ -564,8 +571,37 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
     const int64_t row = (int64_t)tok * a.Hq + h;
     void *dst = active ? a.partial_o : (void *)dump;
     const int64_t po_off = active ? (int64_t)slot * a.po_split_stride + row * a.po_row_stride + grp * 4 : grp * 4;
+    if constexpr (PO == MSA_F32) {
+      // Whole 128-byte lines, streamed past the caches: lanes n and n + 8 of a
+      // quarter swap one of each pair of column tiles (a DPP move within the
+      // 16-lane row), so each store instruction covers 128 contiguous bytes
+      // of 8 rows -- tiles 2k, 2k+1 of rows 0-7, then of rows 8-15 -- instead
+      // of 64 bytes of 16 rows.  Non-temporal stores of whole lines go to
+      // memory without a read for ownership or a merge in L2; the combine
+      // reads the partials from HBM in any case.
+      uint8_t *own = (uint8_t *)dst + po_off * 4;
+      const uint64_t oa = (uint64_t)own;
+      uint8_t *partner = (uint8_t *)(((uint64_t)swap_half_row((uint32_t)(oa >> 32)) << 32) |
+                                     swap_half_row((uint32_t)oa));
+      const bool lo_half = n < 8;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(dst, po_off + mt * 16, o[mt] * inv);
+      for (int k = 0; k < MT / 2; ++k) {
+        const f32x4 e0 = o[2 * k] * inv, e1 = o[2 * k + 1] * inv;
+        const f32x4 send = lo_half ? e1 : e0;
+        f32x4 recv;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) recv[w] = __uint_as_float(swap_half_row(__float_as_uint(send[w])));
+        // rows 0-7: own tile 2k (lanes 0-7), the partner's tile 2k+1 (lanes 8-15)
+        __builtin_nontemporal_store(lo_half ? e0 : recv,
+                                    (f32x4 *)(lo_half ? own + 128 * k : partner + 128 * k + 64));
+        // rows 8-15: the partner's tile 2k (lanes 0-7), own tile 2k+1 (lanes 8-15)
+        __builtin_nontemporal_store(lo_half ? recv : e1,
+                                    (f32x4 *)(lo_half ? partner + 128 * k : own + 128 * k + 64));
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(dst, po_off + mt * 16, o[mt] * inv);
+    }
     float *ldst = (active && grp == 0) ? a.partial_lse + (int64_t)slot * a.pl_split_stride + row
                                        : dump + D + lane;
     *ldst = (msc + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
