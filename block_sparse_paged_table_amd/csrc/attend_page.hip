@@ -97,7 +97,13 @@ template <typename T> __device__ __forceinline__ T ld(const void *p) { return *(
 
 // x of lane (l ^ 8) within each 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ uint32_t swap_half_row(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, true);
+}
+// On the lanes of the 4-lane banks in BANKS (0x3: lanes 0-7 of each 16-lane
+// row, 0xc: lanes 8-15) x of lane (l ^ 8); elsewhere `keep` (one DPP move).
+template <int BANKS>
+__device__ __forceinline__ uint32_t from_half_row(uint32_t keep, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)x, 0x128, 0xf, BANKS, false);
 }
 
 // f(integral_constant<J>) for J = 0 .. N-1, unrolled at compile time.
@@ -579,24 +585,31 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
       // of 64 bytes of 16 rows.  Non-temporal stores of whole lines go to
       // memory without a read for ownership or a merge in L2; the combine
       // reads the partials from HBM in any case.
-      uint8_t *own = (uint8_t *)dst + po_off * 4;
-      const uint64_t oa = (uint64_t)own;
-      uint8_t *partner = (uint8_t *)(((uint64_t)swap_half_row((uint32_t)(oa >> 32)) << 32) |
-                                     swap_half_row((uint32_t)oa));
+      // Byte offsets from partial_o (the scratch row as well), so that the
+      // exchanged address still derives from a global pointer and the stores
+      // stay global stores (a flat store would also count as an LDS access).
+      uint8_t *const base = (uint8_t *)a.partial_o;
+      const int64_t own_off = ((uint8_t *)dst - base) + po_off * 4;
+      const int64_t partner_off = (int64_t)(((uint64_t)swap_half_row((uint32_t)((uint64_t)own_off >> 32)) << 32) |
+                                            swap_half_row((uint32_t)own_off));
+      uint8_t *const own = base + own_off;
+      uint8_t *const partner = base + partner_off;
       const bool lo_half = n < 8;
 #pragma unroll
       for (int k = 0; k < MT / 2; ++k) {
         const f32x4 e0 = o[2 * k] * inv, e1 = o[2 * k + 1] * inv;
-        const f32x4 send = lo_half ? e1 : e0;
-        f32x4 recv;
+        f32x4 va, vb;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) recv[w] = __uint_as_float(swap_half_row(__float_as_uint(send[w])));
+        for (int w = 0; w < 4; ++w) {
+          // va: e0 on lanes 0-7, the partner's e1 on lanes 8-15;
+          // vb: the partner's e0 on lanes 0-7, e1 on lanes 8-15
+          va[w] = __uint_as_float(from_half_row<0xc>(__float_as_uint(e0[w]), __float_as_uint(e1[w])));
+          vb[w] = __uint_as_float(from_half_row<0x3>(__float_as_uint(e1[w]), __float_as_uint(e0[w])));
+        }
         // rows 0-7: own tile 2k (lanes 0-7), the partner's tile 2k+1 (lanes 8-15)
-        __builtin_nontemporal_store(lo_half ? e0 : recv,
-                                    (f32x4 *)(lo_half ? own + 128 * k : partner + 128 * k + 64));
+        __builtin_nontemporal_store(va, (f32x4 *)(lo_half ? own + 128 * k : partner + 128 * k + 64));
         // rows 8-15: the partner's tile 2k (lanes 0-7), own tile 2k+1 (lanes 8-15)
-        __builtin_nontemporal_store(lo_half ? recv : e1,
-                                    (f32x4 *)(lo_half ? partner + 128 * k : own + 128 * k + 64));
+        __builtin_nontemporal_store(vb, (f32x4 *)(lo_half ? partner + 128 * k : own + 128 * k + 64));
       }
     } else {
 #pragma unroll
