@@ -210,8 +210,7 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
           acc[t][i] = x;
           mb = fmaxf(mb, x);
         }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = quarter_reduce<true>(mb);
       const float mn = fmaxf(m, mb);
       // ---- rescale when some row's running max grew
       if (__any(mn > m)) {
@@ -252,10 +251,8 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
 
   // ---- epilogue: row n of the tile, columns 16*mt + 4*gl + [0,4)
   if (!has_tile || !active) return;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  lp += __shfl_xor(lp, 16);
-  lp += __shfl_xor(lp, 32);
+  l = quarter_reduce<false>(l);
+  lp = quarter_reduce<false>(lp);
   const int64_t row = (int64_t)tok * a.Hq + h;
   const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + gl * 4;
   float *lse_dst = a.partial_lse + (int64_t)split * a.pl_split_stride + row;

@@ -506,8 +506,7 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
       for (int i = 0; i < 4; ++i) acc[t][i] *= sc;
       m = fmaxf(m, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
     }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = quarter_reduce<true>(m);
     const float msc = (m == -INFINITY) ? 0.0f : m;  // inactive row: stay finite
 
     // ---- P = exp2(S - m).  l (exact FP32 sum) gives the LSE; lp, the sum of
@@ -530,11 +529,9 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
         lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2 * t + 1]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
       }
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = quarter_reduce<false>(l);
     if constexpr (RouteInfo<ROUTE>::F16PV) {
-      lp += __shfl_xor(lp, 16);
-      lp += __shfl_xor(lp, 32);
+      lp = quarter_reduce<false>(lp);
     } else {
       lp = l;
     }

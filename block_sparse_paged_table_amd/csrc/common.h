@@ -174,4 +174,19 @@ __host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel) {
   return L;
 }
 
+// Max (MAX) or sum of x over the four lanes l, l^16, l^32, l^48 -- the
+// quarters of one row -- on every lane, through the gfx950 row swaps
+// (v_permlane16_swap: rows 0<->1 and 2<->3; v_permlane32_swap: rows 0,1 <->
+// 2,3), VALU operations instead of LDS-routed permutes.  Both lanes of a
+// pair add the same two values, so every lane holds the same bits.
+template <bool MAX>
+__device__ __forceinline__ float quarter_reduce(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y0 = __uint_as_float(a[0]), y1 = __uint_as_float(a[1]);
+  const float y = MAX ? fmaxf(y0, y1) : y0 + y1;
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  const float z0 = __uint_as_float(b[0]), z1 = __uint_as_float(b[1]);
+  return MAX ? fmaxf(z0, z1) : z0 + z1;
+}
+
 }  // namespace msa

@@ -179,8 +179,7 @@ __global__ void __launch_bounds__(IT, 2) k_index_scores(const IndexArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[t][i]);
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+      m = quarter_reduce<true>(m);
       if (grp == 0 && my_b == cb) sScore[rho][jj] = m == -INFINITY ? m : m * a.scale;
     }
     __syncthreads();  // the last page's buffer is reused by the next request
