@@ -589,9 +589,11 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
       const int64_t own_off = ((uint8_t *)dst - base) + po_off * 4;
       const int64_t partner_off = (int64_t)(((uint64_t)swap_half_row((uint32_t)((uint64_t)own_off >> 32)) << 32) |
                                             swap_half_row((uint32_t)own_off));
-      uint8_t *const own = base + own_off;
-      uint8_t *const partner = base + partner_off;
       const bool lo_half = n < 8;
+      // rows 0-7 of each tile pair: lanes 0-7 write their own row, lanes 8-15
+      // the partner's second tile; rows 8-15 the other way round
+      uint8_t *const pa = base + (lo_half ? own_off : partner_off + 64);
+      uint8_t *const pb = base + (lo_half ? partner_off : own_off + 64);
 #pragma unroll
       for (int k = 0; k < MT / 2; ++k) {
         const f32x4 e0 = o[2 * k] * inv, e1 = o[2 * k + 1] * inv;
@@ -603,10 +605,8 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
           va[w] = __uint_as_float(from_half_row<0xc>(__float_as_uint(e0[w]), __float_as_uint(e1[w])));
           vb[w] = __uint_as_float(from_half_row<0x3>(__float_as_uint(e1[w]), __float_as_uint(e0[w])));
         }
-        // rows 0-7: own tile 2k (lanes 0-7), the partner's tile 2k+1 (lanes 8-15)
-        __builtin_nontemporal_store(va, (f32x4 *)(lo_half ? own + 128 * k : partner + 128 * k + 64));
-        // rows 8-15: the partner's tile 2k (lanes 0-7), own tile 2k+1 (lanes 8-15)
-        __builtin_nontemporal_store(vb, (f32x4 *)(lo_half ? partner + 128 * k : own + 128 * k + 64));
+        __builtin_nontemporal_store(va, (f32x4 *)(pa + 128 * k));
+        __builtin_nontemporal_store(vb, (f32x4 *)(pb + 128 * k));
       }
     } else {
 #pragma unroll
