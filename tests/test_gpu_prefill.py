@@ -128,9 +128,13 @@ def test_fp32_output_and_bf16_output_agree():
     check_combined(p, out, lse, ref, "bf16")
 
 
-def test_strided_partial_buffer():
-    p = _small(14)
-    dp = _run(p, po_row_pad=32)
+@pytest.mark.parametrize("qd,kd,d,pad", [("f32", "f32", 64, 32), ("e4m3", "nvfp4", 128, 4),
+                                         ("bf16", "bf16", 128, 12), ("e4m3", "e4m3", 64, 4)])
+def test_strided_partial_buffer(qd, kd, d, pad):
+    """Padded partial rows (row stride d + pad, so rows are not 128-byte aligned):
+    the whole-line stores of FP32 partials must land on each row's own bytes."""
+    p = _small(14, q_dtype=qd, kv_dtype=kd, d=d, Hq=8, Hkv=2)
+    dp = _run(p, po_row_pad=pad)
     ref = oracle.prefill_rows(p)
     po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
     check_partials(p, po, pl, ref)
