@@ -482,6 +482,11 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
       }
     }
 
+    // ---- softmax phase at raised wave priority (back to 0 before PV): the
+    // VALU-bound stretch of one wave gets issue slots first while the other
+    // waves of the SIMD keep the matrix cores busy (measured ~1-4 %)
+    __builtin_amdgcn_s_setprio(1);
+
     // ---- prefetch tile + PF * NWAVES (inactive, in-bounds rows past the end)
     ri[J] = row_of(tile + PF * NWAVES);
     load_q(ri[J], qb[J]);
@@ -535,6 +540,8 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
     } else {
       lp = l;
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- O^T = V^T P^T
     f32x4 o[MT];
