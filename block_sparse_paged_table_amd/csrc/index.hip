@@ -3,8 +3,8 @@
 // the page's max -- for every (query, head) row, then a top-k over the row),
 // written for gfx950.
 //
-// k_index_scores: one workgroup per (64 query tokens, head, chunk of 16
-// logical pages).  The 64 Q rows live in registers (16 per wave); each page
+// k_index_scores: one workgroup per (128 query tokens, head, chunk of 16
+// logical pages).  The 128 Q rows live in registers (16 per wave); each page
 // of the chunk that some row of the tile can see is copied into LDS
 // (double-buffered, the next page's loads in flight while the current one is
 // scored), and every wave computes S^T = K Q^T for its 16 rows with FP8 MFMA
@@ -22,17 +22,21 @@
 namespace msa {
 namespace {
 
-constexpr int IT = 256;     // threads per workgroup
-constexpr int ITQ = 64;     // query tokens per workgroup
+constexpr int ITQ_WAVES = 8;  // waves per workgroup (16 query rows each)
 constexpr int IPC = 16;     // logical pages per workgroup
 constexpr int IPAGE = 128;  // tokens per page
 
 template <int D> struct IGeom {
+  // waves per workgroup: each thread copies at least one 16-byte chunk of a page
+  static constexpr int WAVES = ITQ_WAVES * 64 > IPAGE * D / 16 ? IPAGE * D / 16 / 64 : ITQ_WAVES;
+  static constexpr int IT = 64 * WAVES;    // threads per workgroup
+  static constexpr int ITQ = 16 * WAVES;   // query tokens per workgroup
   static constexpr int RB = D;              // bytes per K row (E4M3)
   static constexpr int CPR = RB / 16;       // 16-byte chunks per row
   static constexpr int LANE_CH = CPR / 4;   // chunks of a row one lane holds
   static constexpr int KCH = IPAGE * CPR / IT;  // chunks per thread per page
   static constexpr int PAGE_BYTES = IPAGE * RB;
+  static_assert(KCH >= 1 && KCH * IT == IPAGE * CPR, "page copy must cover the page exactly");
 };
 
 // Byte offset of chunk c of K row `key` in LDS, XOR-swizzled so that the 16
@@ -48,7 +52,7 @@ __device__ __forceinline__ void load_kpage(const IndexArgs &a, int phys, int h, 
   const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)h * a.kv_stride_head;
 #pragma unroll
   for (int it = 0; it < Gm::KCH; ++it) {
-    const int q = it * IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
+    const int q = it * Gm::IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
     r[it] = *(const u32x4 *)(kb + key * a.kv_stride_tok + c * 16);
   }
 }
@@ -58,19 +62,20 @@ __device__ __forceinline__ void store_kpage(uint8_t *sk, const u32x4 *r) {
   using Gm = IGeom<D>;
 #pragma unroll
   for (int it = 0; it < Gm::KCH; ++it) {
-    const int q = it * IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
+    const int q = it * Gm::IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
     *(u32x4 *)(sk + ik_off<D>(key, c)) = r[it];
   }
 }
 
 template <int D>
-__global__ void __launch_bounds__(IT, 2) k_index_scores(const IndexArgs a) {
+__global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a) {
   using Gm = IGeom<D>;
+  constexpr int IT = Gm::IT, ITQ = Gm::ITQ;
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][Gm::PAGE_BYTES];
   __shared__ float sScore[ITQ][IPC + 1];
   __shared__ int sRowB[ITQ], sRowLast[ITQ];
   __shared__ int sReq[ITQ], sReqLast[ITQ];
-  __shared__ int sNreq;
+  __shared__ int sNreq, sMinB, sMaxB, sMaxLast;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,9 +103,24 @@ __global__ void __launch_bounds__(IT, 2) k_index_scores(const IndexArgs a) {
     sRowB[tid] = b;
     sRowLast[tid] = last;
   }
+  if (tid == 0) {
+    sMinB = INT32_MAX;
+    sMaxB = -1;
+    sMaxLast = -1;
+  }
   for (int i = tid; i < ITQ * (IPC + 1); i += IT) (&sScore[0][0])[i] = -INFINITY;
   __syncthreads();
-  if (tid == 0) {  // the distinct requests of the tile, in order of appearance
+  if (tid < ITQ && sRowB[tid] >= 0) {
+    atomicMin(&sMinB, sRowB[tid]);
+    atomicMax(&sMaxB, sRowB[tid]);
+    atomicMax(&sMaxLast, sRowLast[tid]);
+  }
+  __syncthreads();
+  if (tid == 0 && sMinB == sMaxB) {  // one request (or none): the usual tile
+    sReq[0] = sMinB;
+    sReqLast[0] = sMaxLast;
+    sNreq = sMaxB >= 0 ? 1 : 0;
+  } else if (tid == 0) {  // the distinct requests of the tile, in order of appearance
     int nr = 0;
     for (int r = 0; r < ITQ; ++r) {
       const int b = sRowB[r];
@@ -259,11 +279,12 @@ __global__ void k_index_zero(uint32_t *err) { *err = 0u; }
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t s) {
   if (a.err_flags) k_index_zero<<<1, 1, 0, s>>>(a.err_flags);
   if (a.total_q == 0) return hipGetLastError();
-  dim3 grid((unsigned)((a.total_q + ITQ - 1) / ITQ), (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
+  const int itq = a.D == 64 ? IGeom<64>::ITQ : IGeom<128>::ITQ;
+  dim3 grid((unsigned)((a.total_q + itq - 1) / itq), (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
   if (a.D == 64)
-    k_index_scores<64><<<grid, IT, 0, s>>>(a);
+    k_index_scores<64><<<grid, IGeom<64>::IT, 0, s>>>(a);
   else
-    k_index_scores<128><<<grid, IT, 0, s>>>(a);
+    k_index_scores<128><<<grid, IGeom<128>::IT, 0, s>>>(a);
   return hipGetLastError();
 }
 
