@@ -56,19 +56,22 @@ __device__ __forceinline__ RowCtx row_ctx(const PageArgs &a, int r, uint32_t &er
   return c;
 }
 
+constexpr int kCountThreads = 64;  // rows per plan_count workgroup (slice_rows is a multiple)
+constexpr int kRegSlots = 16;      // rows with at most this many slots keep them in registers
+
 template <bool LDS_HIST>
-__global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
+__global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
   extern __shared__ int32_t hist[];
   const int64_t L = a.lists_per_slice;
   const int tid = threadIdx.x;
   // slice_rows is a multiple of the block size: one slice per workgroup
-  const int64_t lbase = ((int64_t)blockIdx.x * kPlanThreads) / a.slice_rows * L;
+  const int64_t lbase = ((int64_t)blockIdx.x * kCountThreads) / a.slice_rows * L;
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
   if constexpr (LDS_HIST) {
-    for (int64_t i = tid; i < L; i += kPlanThreads) hist[i] = 0;
+    for (int64_t i = tid; i < L; i += kCountThreads) hist[i] = 0;
     __syncthreads();
   }
-  const int64_t idx = (int64_t)blockIdx.x * kPlanThreads + tid;
+  const int64_t idx = (int64_t)blockIdx.x * kCountThreads + tid;
   const bool live = idx < (int64_t)a.total_q * a.Hkv;
   const int K = a.num_slots;
   int32_t *slot_list = (int32_t *)(a.ws + a.lay.slot_list) + idx * K;
@@ -79,25 +82,20 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
     const uint8_t *smask = a.sel_mask + r * a.sel_stride_tok + g * a.sel_stride_head;
     uint32_t err = 0;
     const RowCtx c = row_ctx(a, r, err);
-    for (int j = 0; j < K; ++j) {
+    const int bb = c.valid ? c.b : 0;  // an in-bounds table row for the loads below
+    // slot j: validate, find its list, claim a position (or mark the split empty)
+    auto visit = [&](int j, uint32_t mk, int u, bool dup, int pp) {
       int list = -1;
-      const uint32_t mk = smask[j];
       if (c.valid && mk) {
-        const int u = sidx[j];
         if (u < 0 || u >= a.max_pages) {
           err |= MSA_ERRF_SEL_RANGE;
-        } else {
-          bool dup = false;
-          for (int jj = 0; jj < j; ++jj) dup |= (smask[jj] != 0) && (sidx[jj] == u);
-          if (dup) {
-            err |= MSA_ERRF_DUPLICATE;
-          } else if ((int64_t)u * a.page_size <= c.last) {
-            const int pp = a.page_table[c.b * a.pt_stride + u];
-            if (pp < 0 || pp >= a.num_phys_pages)
-              err |= MSA_ERRF_PHYS_RANGE;
-            else
-              list = (g * a.num_seqs + c.b) * a.max_pages + u;  // KV head outermost
-          }
+        } else if (dup) {
+          err |= MSA_ERRF_DUPLICATE;
+        } else if ((int64_t)u * a.page_size <= c.last) {
+          if (pp < 0 || pp >= a.num_phys_pages)
+            err |= MSA_ERRF_PHYS_RANGE;
+          else
+            list = (g * a.num_seqs + c.b) * a.max_pages + u;  // KV head outermost
         }
       }
       slot_list[j] = list >= 0 ? (int32_t)(lbase + list) : -1;
@@ -107,12 +105,47 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count(const PageArgs a) {
         float *pl = a.partial_lse + j * a.pl_split_stride + (int64_t)r * a.Hq + g * a.G;
         for (int h = 0; h < a.G; ++h) pl[h] = -INFINITY;
       }
+    };
+    if (K <= kRegSlots) {
+      // every load of the row is issued before any is used; the duplicate
+      // test runs on registers
+      uint32_t mk[kRegSlots];
+      int uu[kRegSlots], pp[kRegSlots];
+#pragma unroll
+      for (int j = 0; j < kRegSlots; ++j) {
+        const int jc = j < K ? j : 0;
+        mk[j] = j < K ? (uint32_t)smask[jc] : 0u;
+        uu[j] = sidx[jc];
+      }
+#pragma unroll
+      for (int j = 0; j < kRegSlots; ++j) {
+        const int uc = (uu[j] >= 0 && uu[j] < a.max_pages) ? uu[j] : 0;
+        pp[j] = a.page_table[bb * a.pt_stride + uc];
+      }
+#pragma unroll
+      for (int j = 0; j < kRegSlots; ++j) {
+        if (j < K) {
+          bool dup = false;
+#pragma unroll
+          for (int jj = 0; jj < j; ++jj) dup |= (mk[jj] != 0u) && (uu[jj] == uu[j]);
+          visit(j, mk[j], uu[j], dup, pp[j]);
+        }
+      }
+    } else {
+      for (int j = 0; j < K; ++j) {
+        const uint32_t mk = smask[j];
+        const int u = sidx[j];
+        bool dup = false;
+        for (int jj = 0; jj < j; ++jj) dup |= (smask[jj] != 0) && (sidx[jj] == u);
+        const int uc = (u >= 0 && u < a.max_pages) ? u : 0;
+        visit(j, mk, u, dup, a.page_table[bb * a.pt_stride + uc]);
+      }
     }
     if (err) atomicOr(a.err_flags, err);
   }
   if constexpr (LDS_HIST) {
     __syncthreads();
-    for (int64_t i = tid; i < L; i += kPlanThreads) {
+    for (int64_t i = tid; i < L; i += kCountThreads) {
       const int32_t n = hist[i];
       if (n) hist[i] = atomicAdd(&counts[lbase + i], n);  // this workgroup's block of list i
     }
@@ -272,11 +305,12 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   plan_zero<<<(unsigned)zero_blocks, 256, 0, s>>>(counts, L, a.err_flags);
   const int64_t rows = (int64_t)a.total_q * a.Hkv;
   const unsigned blocks = (unsigned)((rows + kPlanThreads - 1) / kPlanThreads);
-  if (blocks) {
+  const unsigned count_blocks = (unsigned)((rows + kCountThreads - 1) / kCountThreads);
+  if (count_blocks) {
     if (a.lists_per_slice <= kMaxLdsLists)
-      plan_count<true><<<blocks, kPlanThreads, (size_t)a.lists_per_slice * 4, s>>>(a);
+      plan_count<true><<<count_blocks, kCountThreads, (size_t)a.lists_per_slice * 4, s>>>(a);
     else
-      plan_count<false><<<blocks, kPlanThreads, 0, s>>>(a);
+      plan_count<false><<<count_blocks, kCountThreads, 0, s>>>(a);
   }
   const int nt = (int)((L + kScanTile - 1) / kScanTile);
   plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
