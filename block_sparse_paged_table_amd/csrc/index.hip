@@ -215,6 +215,47 @@ __global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a
   }
 }
 
+// (bv, bj) := the better of (bv, bj) and (ov, oj): higher score, then lower page.
+__device__ __forceinline__ void take_better(float &bv, int &bj, float ov, int oj) {
+  if (ov > bv || (ov == bv && oj < bj)) {
+    bv = ov;
+    bj = oj;
+  }
+}
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL> __device__ __forceinline__ void take_better_dpp(float &bv, int &bj) {
+  take_better(bv, bj, __uint_as_float(dpp_u32<CTRL>(__float_as_uint(bv))), (int)dpp_u32<CTRL>((uint32_t)bj));
+}
+// The wave's best (score, page) on every lane.  The order is total, so any
+// combining pattern gives every lane the same winner: DPP within each 16-lane
+// row (quad swaps, then rotations by 4 and 8), then the gfx950 row swaps.
+__device__ __forceinline__ void wave_best(float &bv, int &bj) {
+  take_better_dpp<0xb1>(bv, bj);   // quad_perm [1,0,3,2]
+  take_better_dpp<0x4e>(bv, bj);   // quad_perm [2,3,0,1]
+  take_better_dpp<0x124>(bv, bj);  // row_ror:4
+  take_better_dpp<0x128>(bv, bj);  // row_ror:8
+  {
+    const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto j = __builtin_amdgcn_permlane16_swap((uint32_t)bj, (uint32_t)bj, false, false);
+    float v0 = __uint_as_float(v[0]);
+    int j0 = (int)j[0];
+    take_better(v0, j0, __uint_as_float(v[1]), (int)j[1]);
+    bv = v0;
+    bj = j0;
+  }
+  {
+    const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto j = __builtin_amdgcn_permlane32_swap((uint32_t)bj, (uint32_t)bj, false, false);
+    float v0 = __uint_as_float(v[0]);
+    int j0 = (int)j[0];
+    take_better(v0, j0, __uint_as_float(v[1]), (int)j[1]);
+    bv = v0;
+    bj = j0;
+  }
+}
+
 // One wave per (token, head) row: NPL page scores per lane (page i*64+lane).
 template <int NPL>
 __global__ void __launch_bounds__(256) k_index_topk(const IndexArgs a) {
@@ -242,15 +283,7 @@ __global__ void __launch_bounds__(256) k_index_topk(const IndexArgs a) {
         bv = v[i];
         bj = i * 64 + lane;
       }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oj = __shfl_xor(bj, off);
-      if (ov > bv || (ov == bv && oj < bj)) {
-        bv = ov;
-        bj = oj;
-      }
-    }
+    wave_best(bv, bj);
     done = !(bv > -INFINITY);
     if (done) break;
 #pragma unroll
