@@ -62,45 +62,51 @@ template <int D> struct BatchRegs {
   uint32_t mask, tiles;
 };
 
+// Byte offset (within the K / V caches) of unit u of the group's list, or -1
+// past the end of the list.
+__device__ __forceinline__ int64_t unit_off(const uint4 *list, int count, int u) {
+  if (u >= count) return -1;
+  const uint2 e = *(const uint2 *)&list[u];
+  return (int64_t)((uint64_t)e.x | ((uint64_t)e.y << 32));
+}
+
+// Batch beta's K and V chunks of this thread into registers.  All of the
+// thread's unit offsets are read first and all K / V loads issued after one
+// wait: a wait between an offset and its data load would also wait for every
+// data load before it, one round trip each.
 template <int D>
 __device__ __forceinline__ void load_batch(const GroupArgs &a, const uint4 *list, int count, int beta,
                                            BatchRegs<D> &r) {
   using Gm = GGeom<D>;
   const int tid = threadIdx.x;
   const int u0 = beta * kGUnitsPerBatch;
+  const int kp = tid & 15, db = tid >> 4;  // V: key pair, block of D/16 dims
+  int64_t koff[Gm::KLD];
+#pragma unroll
+  for (int it = 0; it < Gm::KLD; ++it) {
+    const int key = (it * GT + tid) / Gm::CPR;
+    koff[it] = unit_off(list, count, u0 + (key >> 2));
+  }
+  const int64_t voff = unit_off(list, count, u0 + (kp >> 1));
+  r.mask = r.tiles = 0u;
+  if (tid < kGUnitsPerBatch && u0 + tid < count) {
+    const uint2 e = *(const uint2 *)((const uint32_t *)&list[u0 + tid] + 2);
+    r.mask = e.x;
+    r.tiles = e.y;
+  }
 #pragma unroll
   for (int it = 0; it < Gm::KLD; ++it) {
     const int q = it * GT + tid, key = q / Gm::CPR, c = q % Gm::CPR;
-    const int u = u0 + (key >> 2);
-    if (u < count) {
-      const uint4 e = list[u];
-      const int64_t off = (int64_t)((uint64_t)e.x | ((uint64_t)e.y << 32));
-      r.k[it] = gld<u32x4>(a.k_cache + off + (key & 3) * a.kv_stride_tok + c * 16);
-    } else {
-      r.k[it] = u32x4{0u, 0u, 0u, 0u};
-    }
+    r.k[it] = koff[it] >= 0 ? gld<u32x4>(a.k_cache + koff[it] + (key & 3) * a.kv_stride_tok + c * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
   }
-  const int kp = tid & 15, db = tid >> 4;  // key pair, block of D/16 dims
-  const int u = u0 + (kp >> 1);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int c = 0; c < Gm::VLD; ++c) {
-      if (u < count) {
-        const uint4 e = list[u];
-        const int64_t off = (int64_t)((uint64_t)e.x | ((uint64_t)e.y << 32));
-        r.v[kk][c] = gld<u32x4>(a.v_cache + off + ((2 * kp + kk) & 3) * a.kv_stride_tok +
-                                db * Gm::VDB * 2 + c * 16);
-      } else {
-        r.v[kk][c] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  r.mask = r.tiles = 0u;
-  if (tid < kGUnitsPerBatch && u0 + tid < count) {
-    const uint4 e = list[u0 + tid];
-    r.mask = e.z;
-    r.tiles = e.w;
-  }
+    for (int c = 0; c < Gm::VLD; ++c)
+      r.v[kk][c] = voff >= 0 ? gld<u32x4>(a.v_cache + voff + ((2 * kp + kk) & 3) * a.kv_stride_tok +
+                                          db * Gm::VDB * 2 + c * 16)
+                             : u32x4{0u, 0u, 0u, 0u};
 }
 
 template <int D>
