@@ -70,43 +70,55 @@ __device__ __forceinline__ int64_t unit_off(const uint4 *list, int count, int u)
   return (int64_t)((uint64_t)e.x | ((uint64_t)e.y << 32));
 }
 
-// Batch beta's K and V chunks of this thread into registers.  All of the
-// thread's unit offsets are read first and all K / V loads issued after one
-// wait: a wait between an offset and its data load would also wait for every
-// data load before it, one round trip each.
+// Unit offsets (and the batch's mask / active-tile words) of this thread's
+// chunks of batch beta.  They are fetched one batch ahead of the K / V loads
+// that use them: a wait between an offset and its data load would also wait
+// for every data load issued before it, one round trip each.
+template <int D> struct BatchOffs {
+  int64_t k[GGeom<D>::KLD];
+  int64_t v;
+  uint32_t mask, tiles;
+};
 template <int D>
-__device__ __forceinline__ void load_batch(const GroupArgs &a, const uint4 *list, int count, int beta,
-                                           BatchRegs<D> &r) {
+__device__ __forceinline__ void fetch_offs(const uint4 *list, int count, int beta, BatchOffs<D> &o) {
   using Gm = GGeom<D>;
   const int tid = threadIdx.x;
   const int u0 = beta * kGUnitsPerBatch;
-  const int kp = tid & 15, db = tid >> 4;  // V: key pair, block of D/16 dims
-  int64_t koff[Gm::KLD];
 #pragma unroll
   for (int it = 0; it < Gm::KLD; ++it) {
     const int key = (it * GT + tid) / Gm::CPR;
-    koff[it] = unit_off(list, count, u0 + (key >> 2));
+    o.k[it] = unit_off(list, count, u0 + (key >> 2));
   }
-  const int64_t voff = unit_off(list, count, u0 + (kp >> 1));
-  r.mask = r.tiles = 0u;
+  o.v = unit_off(list, count, u0 + ((tid & 15) >> 1));
+  o.mask = o.tiles = 0u;
   if (tid < kGUnitsPerBatch && u0 + tid < count) {
     const uint2 e = *(const uint2 *)((const uint32_t *)&list[u0 + tid] + 2);
-    r.mask = e.x;
-    r.tiles = e.y;
+    o.mask = e.x;
+    o.tiles = e.y;
   }
+}
+
+// The K and V chunks of this thread for the batch whose offsets are `o`.
+template <int D>
+__device__ __forceinline__ void load_batch(const GroupArgs &a, const BatchOffs<D> &o, BatchRegs<D> &r) {
+  using Gm = GGeom<D>;
+  const int tid = threadIdx.x;
+  const int kp = tid & 15, db = tid >> 4;  // V: key pair, block of D/16 dims
 #pragma unroll
   for (int it = 0; it < Gm::KLD; ++it) {
     const int q = it * GT + tid, key = q / Gm::CPR, c = q % Gm::CPR;
-    r.k[it] = koff[it] >= 0 ? gld<u32x4>(a.k_cache + koff[it] + (key & 3) * a.kv_stride_tok + c * 16)
-                            : u32x4{0u, 0u, 0u, 0u};
+    r.k[it] = o.k[it] >= 0 ? gld<u32x4>(a.k_cache + o.k[it] + (key & 3) * a.kv_stride_tok + c * 16)
+                           : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int c = 0; c < Gm::VLD; ++c)
-      r.v[kk][c] = voff >= 0 ? gld<u32x4>(a.v_cache + voff + ((2 * kp + kk) & 3) * a.kv_stride_tok +
-                                          db * Gm::VDB * 2 + c * 16)
-                             : u32x4{0u, 0u, 0u, 0u};
+      r.v[kk][c] = o.v >= 0 ? gld<u32x4>(a.v_cache + o.v + ((2 * kp + kk) & 3) * a.kv_stride_tok +
+                                         db * Gm::VDB * 2 + c * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
+  r.mask = o.mask;
+  r.tiles = o.tiles;
 }
 
 template <int D>
@@ -180,14 +192,20 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
   const float sc = a.scale_log2;
 
   BatchRegs<D> br;
+  BatchOffs<D> bo;  // offsets of the next batch to load
   if (nb > 0) {
-    load_batch<D>(a, list, count, 0, br);
+    fetch_offs<D>(list, count, 0, bo);
+    load_batch<D>(a, bo, br);
+    fetch_offs<D>(list, count, 1, bo);
     store_batch<D>(smem, br);
   }
   __syncthreads();
 
   for (int beta = 0; beta < nb; ++beta) {
-    if (beta + 1 < nb) load_batch<D>(a, list, count, beta + 1, br);
+    if (beta + 1 < nb) {
+      load_batch<D>(a, bo, br);                     // batch beta + 1
+      fetch_offs<D>(list, count, beta + 2, bo);     // offsets of batch beta + 2
+    }
     const uint8_t *st = smem + (beta & 1) * Gm::STAGE;
     const uint32_t *meta = (const uint32_t *)(st + Gm::K_BYTES + Gm::V_BYTES);
     uint32_t tiles = 0;
