@@ -305,6 +305,72 @@ __global__ void __launch_bounds__(256) k_index_topk(const IndexArgs a) {
   }
 }
 
+// The best (score, page) of each 16-lane row of the wave on every lane of that
+// row: the DPP steps of wave_best, which stay within a row.
+__device__ __forceinline__ void row16_best(float &bv, int &bj) {
+  take_better_dpp<0xb1>(bv, bj);   // quad_perm [1,0,3,2]
+  take_better_dpp<0x4e>(bv, bj);   // quad_perm [2,3,0,1]
+  take_better_dpp<0x124>(bv, bj);  // row_ror:4
+  take_better_dpp<0x128>(bv, bj);  // row_ror:8
+}
+
+// Rows of at most 128 pages and top_k <= 64: 16 lanes per (token, head) row,
+// four rows per wave, 8 page scores per lane (page i*16 + lane % 16).  The same
+// rounds as k_index_topk (arg-max by score, then lower page; the winner is
+// removed), with a 16-lane arg-max, so a round costs a quarter of the wave's
+// instructions per row.  A row whose scores run out (-inf) stops taking
+// slots; the wave runs until all four rows are done.
+__global__ void __launch_bounds__(256) k_index_topk16(const IndexArgs a) {
+  constexpr int NV = 8;
+  const int ll = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = row < (int64_t)a.total_q * a.H;
+  const int64_t rr = live ? row : 0;
+  const int tok = (int)(rr / a.H), h = (int)(rr - (int64_t)tok * a.H);
+  const float *sr = a.scores + rr * a.score_stride;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = i * 16 + ll;
+    v[i] = (live && j < a.max_pages) ? sr[j] : -INFINITY;
+  }
+  // slot s of the row's result is kept by lane s % 16 (register s / 16)
+  int32_t res[4] = {-1, -1, -1, -1};
+  bool done = false;  // per row (uniform over its 16 lanes)
+  for (int s = 0; s < a.top_k; ++s) {
+    float bv = -INFINITY;
+    int bj = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (v[i] > bv) {  // ascending pages: a tie keeps the lower one
+        bv = v[i];
+        bj = i * 16 + ll;
+      }
+    row16_best(bv, bj);
+    done = done || !(bv > -INFINITY);
+    if (__all(done)) break;
+    if (!done) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (i * 16 + ll == bj) v[i] = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (s == k * 16 + ll) res[k] = bj;
+    }
+  }
+  if (!live) return;
+  int32_t *oi = a.sel_idx + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+  uint8_t *om = a.sel_mask + (int64_t)tok * a.sel_stride_tok + (int64_t)h * a.sel_stride_head;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = k * 16 + ll;
+    if (s < a.top_k) {
+      oi[s] = res[k];
+      om[s] = res[k] >= 0 ? 1 : 0;
+    }
+  }
+}
+
 __global__ void k_index_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
@@ -325,7 +391,9 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   const int64_t rows = (int64_t)a.total_q * a.H;
   if (rows == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (a.max_pages <= 128)
+  if (a.max_pages <= 128 && a.top_k <= 64)
+    k_index_topk16<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a);
+  else if (a.max_pages <= 128)
     k_index_topk<2><<<blocks, 256, 0, s>>>(a);
   else if (a.max_pages <= 512)
     k_index_topk<8><<<blocks, 256, 0, s>>>(a);

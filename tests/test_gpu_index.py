@@ -112,6 +112,23 @@ def test_index_tiny_chunks_many_requests_and_long_context():
     _check(ip, dev)
 
 
+@pytest.mark.parametrize("ctx,chunk,top_k", [
+    (9000, 200, 100),   # <= 128 pages, top_k > 64: one wave per row, 2 pages per lane
+    (40000, 200, 20),   # 129 .. 512 pages: one wave per row, 8 pages per lane
+    (70000, 130, 255),  # > 512 pages and the largest top_k: 32 pages per lane
+])
+def test_index_topk_wide_rows(ctx, chunk, top_k):
+    """The top-k variants for long rows or many slots (rows of at most 128
+    pages with top_k <= 64 take 16 lanes per row, covered above), checked on
+    sampled tokens of one long request."""
+    ip = _small(46, ctx_lens=[ctx], chunk_lens=[chunk], top_k=top_k, H=1)
+    dev = DeviceIndexProblem(ip)
+    dev.run()
+    torch.cuda.synchronize()
+    err, exact = _check(ip, dev, tokens=[0, 1, chunk // 2, chunk - 1, chunk])
+    assert err == 0 and exact > 0
+
+
 def test_index_deterministic():
     ip = _small(44)
     dev = DeviceIndexProblem(ip)
