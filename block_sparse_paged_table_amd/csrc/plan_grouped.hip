@@ -34,8 +34,9 @@ constexpr uint64_t kInvalidKey = ~0ull;
 // Ascending bitonic sort of n = E * blockDim.x keys held in LDS.  Thread t
 // keeps the keys of sorted positions tE .. tE+E-1 in registers: compare-
 // exchange steps whose partner lies within the thread (stride < E) run in
-// registers; the others exchange through LDS, every thread computing its own
-// new key.  During the sort the LDS copy is laid out position p -> slot
+// registers, those whose partner thread is in the same wave (stride < 64 E)
+// through cross-lane shuffles, the others through LDS; every thread computes
+// its own new key.  During the sort the LDS copy is laid out position p -> slot
 // (p % E) * nt + p / E, so a wave's accesses hit consecutive slots; the
 // input is taken in that layout too (any input order sorts the same).  The
 // result is written back in sorted order with one padding slot after each
@@ -52,11 +53,27 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
   for (int i = 0; i < E; ++i) r[i] = k[i * nt + t];
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride >= E; stride >>= 1) {
+      const int m = stride / E;  // the partner thread is t ^ m (same register i)
+      if (m < kWave) {
+        // partner in this wave: a cross-lane shuffle, no LDS round trip and
+        // no barrier (the wave's lanes run in lockstep)
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int p = base + i, q = p ^ stride;
+          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)r[i], m);
+          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(r[i] >> 32), m);
+          const uint64_t o = ((uint64_t)hi << 32) | lo;
+          const bool up = (p & size) == 0;
+          const bool keep_min = (p < q) == up;
+          r[i] = keep_min ? (r[i] < o ? r[i] : o) : (r[i] > o ? r[i] : o);
+        }
+        continue;
+      }
       __syncthreads();  // everyone is done reading the previous round
 #pragma unroll
       for (int i = 0; i < E; ++i) k[i * nt + t] = r[i];
       __syncthreads();
-      const int tq = t ^ (stride / E);  // the partner thread (same register i)
+      const int tq = t ^ m;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const int p = base + i, q = p ^ stride;
