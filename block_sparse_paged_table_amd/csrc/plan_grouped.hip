@@ -51,21 +51,47 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < E; ++i) r[i] = k[i * nt + t];
-  for (int size = 2; size <= n; size <<= 1) {
+  // sizes up to E: within the thread's registers; base is a multiple of E,
+  // so the direction of position base + i is fixed by i (compile time) below
+  // size E and by base at size E
+#pragma unroll
+  for (int size = 2; size <= E; size <<= 1) {
+#pragma unroll
+    for (int st = size >> 1; st >= 1; st >>= 1) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if (i & st) continue;
+        const int j = i | st;
+        const bool up = size < E ? (i & size) == 0 : (base & size) == 0;
+        const uint64_t x = r[i], y = r[j];
+        const bool sw = (x > y) == up;
+        r[i] = sw ? y : x;
+        r[j] = sw ? x : y;
+      }
+    }
+  }
+  for (int size = 2 * E; size <= n; size <<= 1) {
+    // every position of the thread has the direction of its block, (base &
+    // size) == 0, as size > E > i
+    const bool up = (base & size) == 0;
     for (int stride = size >> 1; stride >= E; stride >>= 1) {
       const int m = stride / E;  // the partner thread is t ^ m (same register i)
+      // Position p = base + i, partner p ^ stride: as stride >= E > i, whether
+      // p is the lower of the pair (bit `stride` clear) depends on base only,
+      // so every register of the thread keeps the minimum, or every one the
+      // maximum.  It keeps its own key exactly when (own < partner) ==
+      // keep_min (equal keys are interchangeable: valid keys are distinct,
+      // invalid ones all-ones).
+      const bool keep_min = ((base & stride) == 0) == up;
       if (m < kWave) {
         // partner in this wave: a cross-lane shuffle, no LDS round trip and
         // no barrier (the wave's lanes run in lockstep)
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          const int p = base + i, q = p ^ stride;
           const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)r[i], m);
           const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(r[i] >> 32), m);
           const uint64_t o = ((uint64_t)hi << 32) | lo;
-          const bool up = (p & size) == 0;
-          const bool keep_min = (p < q) == up;
-          r[i] = keep_min ? (r[i] < o ? r[i] : o) : (r[i] > o ? r[i] : o);
+          r[i] = ((r[i] < o) == keep_min) ? r[i] : o;
         }
         continue;
       }
@@ -76,28 +102,22 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
       const int tq = t ^ m;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        const int p = base + i, q = p ^ stride;
         const uint64_t o = k[i * nt + tq];
-        const bool up = (p & size) == 0;
-        const bool keep_min = (p < q) == up;
-        r[i] = keep_min ? (r[i] < o ? r[i] : o) : (r[i] > o ? r[i] : o);
+        r[i] = ((r[i] < o) == keep_min) ? r[i] : o;
       }
     }
     // strides below E: partners in this thread's registers (compile-time
     // indices, so the keys stay in registers)
 #pragma unroll
     for (int st = E >> 1; st >= 1; st >>= 1) {
-      if (st < size) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-          if (i & st) continue;
-          const int j = i | st;
-          const bool up = ((base + i) & size) == 0;
-          const uint64_t x = r[i], y = r[j];
-          const bool sw = (x > y) == up;
-          r[i] = sw ? y : x;
-          r[j] = sw ? x : y;
-        }
+      for (int i = 0; i < E; ++i) {
+        if (i & st) continue;
+        const int j = i | st;
+        const uint64_t x = r[i], y = r[j];
+        const bool sw = (x > y) == up;
+        r[i] = sw ? y : x;
+        r[j] = sw ? x : y;
       }
     }
   }
