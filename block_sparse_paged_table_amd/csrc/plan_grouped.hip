@@ -233,14 +233,14 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     uint32_t m32;
     uint64_t unit;
   };
-  auto analyze = [&](int p, bool flag_dups) {
+  auto analyze = [&](int p) {
     Lead L{false, 0, 0u, 0ull};
     const uint64_t k = at(p);
     if (k == kInvalidKey) return L;
     const uint64_t unit = k >> 17;
     const uint64_t kp = p > 0 ? at(p - 1) : kInvalidKey;
     if ((kp >> 14) == (k >> 14)) {  // a later slot of the same (request, unit, token)
-      if (flag_dups) err |= MSA_ERRF_DUPLICATE;
+      err |= MSA_ERRF_DUPLICATE;
       return L;
     }
     const int sg = split_of(k);
@@ -271,36 +271,28 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   constexpr int NW = NT / 64;
   __shared__ int wave_count[16][NW];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int i = 0; i < per; ++i) {
-    const Lead L = analyze(i * NT + threadIdx.x, true);
-    const uint64_t bal = __ballot(L.on);
-    if (lane == 0) wave_count[i][wv] = __popcll(bal);
-  }
-  __syncthreads();
-  int total = 0;
-  for (int i = 0; i < per; ++i)
-#pragma unroll
-    for (int w = 0; w < NW; ++w) total += wave_count[i][w];
-  // stage the distinct (split, unit)s: (unit id lo, hi, mask32, split)
+  // stage the distinct (split, unit)s: (unit id lo, hi, mask32, split), in
+  // sorted order: round i's leaders follow every leader of the rounds before
+  // it and, within the round, those of lower waves and lanes
   const int64_t li = (int64_t)g * a.num_groups + grp;
   const int64_t list_base = li * a.list_cap;
   uint4 *stage = (uint4 *)(a.ws + a.lay.stage) + list_base;
   uint4 *out = (uint4 *)(a.ws + a.lay.lists) + list_base;
-  {
-    int base = 0;
-    for (int i = 0; i < per; ++i) {
-      int before = base;
+  int total = 0;
+  for (int i = 0; i < per; ++i) {
+    const Lead L = analyze(i * NT + threadIdx.x);
+    const uint64_t bal = __ballot(L.on);
+    if (lane == 0) wave_count[i][wv] = __popcll(bal);
+    __syncthreads();
+    int before = total;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (w < wv) before += wave_count[i][w];
-        base += wave_count[i][w];
-      }
-      const Lead L = analyze(i * NT + threadIdx.x, false);
-      const uint64_t bal = __ballot(L.on);
-      if (L.on) {
-        const int off = before + __popcll(bal & ((1ull << lane) - 1ull));
-        stage[off] = make_uint4((uint32_t)L.unit, (uint32_t)(L.unit >> 32), L.m32, (uint32_t)L.split);
-      }
+    for (int w = 0; w < NW; ++w) {
+      if (w < wv) before += wave_count[i][w];
+      total += wave_count[i][w];
+    }
+    if (L.on) {
+      const int off = before + __popcll(bal & ((1ull << lane) - 1ull));
+      stage[off] = make_uint4((uint32_t)L.unit, (uint32_t)(L.unit >> 32), L.m32, (uint32_t)L.split);
     }
   }
   __syncthreads();
