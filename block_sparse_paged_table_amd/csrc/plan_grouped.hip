@@ -43,14 +43,10 @@ constexpr uint64_t kInvalidKey = ~0ull;
 // thread's E keys (position p at p + p / E, see sorted_at): a thread that
 // then walks its own E consecutive positions has its lanes 8 * (E + 1)
 // bytes apart, at most two to an LDS bank, instead of E / 2.
-template <int E>
-__device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
-  uint64_t r[E];
+template <int E, typename T>
+__device__ __forceinline__ void bitonic_core(T *k, int n, T (&r)[E]) {
   const int t = threadIdx.x, nt = blockDim.x;
   const int base = t * E;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < E; ++i) r[i] = k[i * nt + t];
   // sizes up to E: within the thread's registers; base is a multiple of E,
   // so the direction of position base + i is fixed by i (compile time) below
   // size E and by base at size E
@@ -63,7 +59,7 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
         if (i & st) continue;
         const int j = i | st;
         const bool up = size < E ? (i & size) == 0 : (base & size) == 0;
-        const uint64_t x = r[i], y = r[j];
+        const T x = r[i], y = r[j];
         const bool sw = (x > y) == up;
         r[i] = sw ? y : x;
         r[j] = sw ? x : y;
@@ -88,9 +84,14 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
         // no barrier (the wave's lanes run in lockstep)
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)r[i], m);
-          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(r[i] >> 32), m);
-          const uint64_t o = ((uint64_t)hi << 32) | lo;
+          T o;
+          if constexpr (sizeof(T) == 8) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)r[i], m);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)((uint64_t)r[i] >> 32), m);
+            o = (T)(((uint64_t)hi << 32) | lo);
+          } else {
+            o = (T)__shfl_xor((int)r[i], m);
+          }
           r[i] = ((r[i] < o) == keep_min) ? r[i] : o;
         }
         continue;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
       const int tq = t ^ m;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        const uint64_t o = k[i * nt + tq];
+        const T o = k[i * nt + tq];
         r[i] = ((r[i] < o) == keep_min) ? r[i] : o;
       }
     }
@@ -114,16 +115,46 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
       for (int i = 0; i < E; ++i) {
         if (i & st) continue;
         const int j = i | st;
-        const uint64_t x = r[i], y = r[j];
+        const T x = r[i], y = r[j];
         const bool sw = (x > y) == up;
         r[i] = sw ? y : x;
         r[j] = sw ? x : y;
       }
     }
   }
+}
+
+
+// 64-bit keys: loaded from, exchanged through and written back to k.
+template <int E>
+__device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
+  uint64_t r[E];
+  const int t = threadIdx.x, nt = blockDim.x;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < E; ++i) k[base + t + i] = r[i];
+  for (int i = 0; i < E; ++i) r[i] = k[i * nt + t];
+  bitonic_core<E, uint64_t>(k, n, r);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) k[t * E + t + i] = r[i];
+  __syncthreads();
+}
+
+// The same sort of 64-bit keys that share their top bits `hi` and whose low
+// 32 bits alone order them (all-ones low words only on invalid keys): run on
+// the 32-bit low words (half the compares, selects and exchanges), then
+// written back as 64-bit keys.
+template <int E>
+__device__ __forceinline__ void bitonic_sort_e32(uint64_t *k, int n, uint64_t hi) {
+  uint32_t r[E];
+  const int t = threadIdx.x, nt = blockDim.x;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) r[i] = (uint32_t)k[i * nt + t];
+  bitonic_core<E, uint32_t>((uint32_t *)k, n, r);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) k[t * E + t + i] = r[i] == ~0u ? kInvalidKey : (hi | r[i]);
   __syncthreads();
 }
 
@@ -141,6 +172,15 @@ __device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
     case 4: bitonic_sort_e<4>(k, n); break;
     case 8: bitonic_sort_e<8>(k, n); break;
     default: bitonic_sort_e<16>(k, n); break;
+  }
+}
+__device__ __forceinline__ void bitonic_sort32(uint64_t *k, int n, uint64_t hi) {
+  switch (n / (int)blockDim.x) {
+    case 1: bitonic_sort_e32<1>(k, n, hi); break;
+    case 2: bitonic_sort_e32<2>(k, n, hi); break;
+    case 4: bitonic_sort_e32<4>(k, n, hi); break;
+    case 8: bitonic_sort_e32<8>(k, n, hi); break;
+    default: bitonic_sort_e32<16>(k, n, hi); break;
   }
 }
 
@@ -201,11 +241,29 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
           const uint32_t vis = mk[tau][i] & ((1u << nvis) - 1u) & 0xfu;
           key = ((uint64_t)b << 41) | ((uint64_t)u << 17) | ((uint64_t)tau << 14) |
                 ((uint64_t)j << 4) | vis;
+
         }
       }
       keys[tau * K + j] = key;
     }
-  bitonic_sort(keys, npow2);
+  // One request among the group's valid rows (every thread holds their
+  // request ids) and units below 2^15 - 1 (valid units are below max_pages *
+  // page_size / unit_tokens: contexts under ~128K tokens): the low 32 bits of
+  // the keys order them (the request bits are common, and no valid key has an
+  // all-ones low word), so the sort runs on 32-bit keys.
+  int b0 = -1;
+  bool one_req = true;
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau) {
+    const int b = b_t[tau];
+    if (pos_t[tau] < 0 || b < 0 || b >= a.num_seqs) continue;
+    if (b0 < 0) b0 = b;
+    else if (b != b0) one_req = false;
+  }
+  if (one_req && (int64_t)a.max_pages * a.page_size / a.unit_tokens <= 32767)
+    bitonic_sort32(keys, npow2, b0 < 0 ? 0ull : (uint64_t)b0 << 41);
+  else
+    bitonic_sort(keys, npow2);
 
   // ---- 3. distinct (split, unit) pairs, their masks.  In sorted order,
   // position p is the first entry of its token in its (request, unit) run

@@ -86,6 +86,21 @@ def test_grouped_errors_and_duplicates():
     assert dp.err_flags() & (1 | 8)
 
 
+@pytest.mark.parametrize("spp", [48, 12])
+def test_grouped_two_requests_in_one_group(spp):
+    """Groups whose 8 tokens belong to two requests (the planner then sorts its
+    full 64-bit keys; single-request groups sort 32-bit keys): the tokens from
+    13 on become a second request that shares the first one's pages, so its
+    rows select the same logical units of an identical cache."""
+    p = _mb(37)
+    q_seq = p.q_seq.clone()
+    q_seq[13:] = torch.where(q_seq[13:] >= 0, torch.ones_like(q_seq[13:]), q_seq[13:])
+    p = dataclasses.replace(p, num_seqs=2, q_seq=q_seq, slots_per_split=spp,
+                            seq_lens=torch.cat([p.seq_lens, p.seq_lens]),
+                            page_table=torch.cat([p.page_table, p.page_table]))
+    _parity(p, out_dtype="f32")
+
+
 def test_grouped_three_runs_bitwise_identical():
     p = _mb(35)
     dp = DeviceProblem(p)
