@@ -140,21 +140,21 @@ __device__ __forceinline__ void bitonic_sort_e(uint64_t *k, int n) {
   __syncthreads();
 }
 
-// The same sort of 64-bit keys that share their top bits `hi` and whose low
-// 32 bits alone order them (all-ones low words only on invalid keys): run on
-// the 32-bit low words (half the compares, selects and exchanges), then
-// written back as 64-bit keys.
-template <int E>
-__device__ __forceinline__ void bitonic_sort_e32(uint64_t *k, int n, uint64_t hi) {
+// The same sort of 64-bit keys that map one-to-one, order-preserving, onto
+// 32-bit keys (narrow; invalid keys onto all-ones, which no valid key takes):
+// run on the 32-bit keys (half the compares, selects and exchanges), then
+// written back widened (wide).
+template <int E, typename Narrow, typename Wide>
+__device__ __forceinline__ void bitonic_sort_e32(uint64_t *k, int n, Narrow narrow, Wide wide) {
   uint32_t r[E];
   const int t = threadIdx.x, nt = blockDim.x;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < E; ++i) r[i] = (uint32_t)k[i * nt + t];
+  for (int i = 0; i < E; ++i) r[i] = narrow(k[i * nt + t]);
   bitonic_core<E, uint32_t>((uint32_t *)k, n, r);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < E; ++i) k[t * E + t + i] = r[i] == ~0u ? kInvalidKey : (hi | r[i]);
+  for (int i = 0; i < E; ++i) k[t * E + t + i] = r[i] == ~0u ? kInvalidKey : wide(r[i]);
   __syncthreads();
 }
 
@@ -174,13 +174,14 @@ __device__ __forceinline__ void bitonic_sort(uint64_t *k, int n) {
     default: bitonic_sort_e<16>(k, n); break;
   }
 }
-__device__ __forceinline__ void bitonic_sort32(uint64_t *k, int n, uint64_t hi) {
+template <typename Narrow, typename Wide>
+__device__ __forceinline__ void bitonic_sort32(uint64_t *k, int n, Narrow narrow, Wide wide) {
   switch (n / (int)blockDim.x) {
-    case 1: bitonic_sort_e32<1>(k, n, hi); break;
-    case 2: bitonic_sort_e32<2>(k, n, hi); break;
-    case 4: bitonic_sort_e32<4>(k, n, hi); break;
-    case 8: bitonic_sort_e32<8>(k, n, hi); break;
-    default: bitonic_sort_e32<16>(k, n, hi); break;
+    case 1: bitonic_sort_e32<1>(k, n, narrow, wide); break;
+    case 2: bitonic_sort_e32<2>(k, n, narrow, wide); break;
+    case 4: bitonic_sort_e32<4>(k, n, narrow, wide); break;
+    case 8: bitonic_sort_e32<8>(k, n, narrow, wide); break;
+    default: bitonic_sort_e32<16>(k, n, narrow, wide); break;
   }
 }
 
@@ -260,10 +261,13 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     if (b0 < 0) b0 = b;
     else if (b != b0) one_req = false;
   }
-  if (one_req && (int64_t)a.max_pages * a.page_size / a.unit_tokens <= 32767)
-    bitonic_sort32(keys, npow2, b0 < 0 ? 0ull : (uint64_t)b0 << 41);
-  else
+  if (one_req && (int64_t)a.max_pages * a.page_size / a.unit_tokens <= 32767) {
+    const uint64_t hi = b0 < 0 ? 0ull : (uint64_t)b0 << 41;
+    bitonic_sort32(keys, npow2, [](uint64_t x) { return (uint32_t)x; },
+                   [hi](uint32_t x) { return hi | x; });
+  } else {
     bitonic_sort(keys, npow2);
+  }
 
   // ---- 3. distinct (split, unit) pairs, their masks.  In sorted order,
   // position p is the first entry of its token in its (request, unit) run
@@ -376,7 +380,21 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     }
     keys[e] = key;
   }
-  bitonic_sort(keys, n2);
+  if (one_split) {
+    // split 0 throughout: (tiles:8 | tokens:8 | index:16) orders the keys as
+    // the 64-bit form does; the index is below 8 * 512
+    bitonic_sort32(keys, n2,
+                   [](uint64_t x) {
+                     return x == kInvalidKey ? ~0u
+                                             : (uint32_t)(((x >> 40) & 0xffu) << 24 | ((x >> 32) & 0xffu) << 16 |
+                                                          (x & 0xffffu));
+                   },
+                   [](uint32_t x) {
+                     return (uint64_t)(x >> 24) << 40 | (uint64_t)((x >> 16) & 0xffu) << 32 | (x & 0xffffu);
+                   });
+  } else {
+    bitonic_sort(keys, n2);
+  }
   const int sh2 = __builtin_ctz((unsigned)(n2 / NT));
 
   // ---- 5. final list: byte offset of the unit's first K/V row, mask, tiles
