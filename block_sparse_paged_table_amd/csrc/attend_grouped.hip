@@ -8,7 +8,9 @@
 // tiles; wave w owns tile w.  The union of the group's microblocks (built by
 // the planner, ordered by category) streams through LDS in batches of 8
 // units = 32 keys, double-buffered: the next batch's K/V is in flight in
-// registers while the current one is computed.  Per batch and active tile:
+// registers while the current one is computed, and the unit offsets of the
+// batch after it are read meanwhile, so each batch costs one round trip to
+// memory.  Per batch and active tile:
 //
 //   S^T = K . Q^T     f16 MFMA 16x16x32, FP32 accumulate (Q held in registers)
 //   mask              key i of unit b is visible to the row of token tau iff
