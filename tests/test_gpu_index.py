@@ -112,6 +112,20 @@ def test_index_tiny_chunks_many_requests_and_long_context():
     _check(ip, dev)
 
 
+@pytest.mark.parametrize("top_k", [1, 64])
+def test_index_topk16_limits(top_k):
+    """The 16-lanes-per-row top-k at its limits: rows of exactly 128 pages,
+    one slot and 64 slots (four result registers per lane), on sampled
+    tokens of one long request."""
+    ip = _small(47, ctx_lens=[16000], chunk_lens=[384], top_k=top_k, H=2)
+    assert ip.max_pages == 128
+    dev = DeviceIndexProblem(ip)
+    dev.run()
+    torch.cuda.synchronize()
+    err, exact = _check(ip, dev, tokens=[0, 5, 200, 383, 384])
+    assert err == 0 and exact > 0
+
+
 @pytest.mark.parametrize("ctx,chunk,top_k", [
     (9000, 200, 100),   # <= 128 pages, top_k > 64: one wave per row, 2 pages per lane
     (40000, 200, 20),   # 129 .. 512 pages: one wave per row, 8 pages per lane
