@@ -39,15 +39,16 @@ __device__ __forceinline__ f32x4 load_partial4(const void *base, int64_t off) {
   }
 }
 
-// Eight consecutive 16-bit partial elements (one 16-byte load) as FP32.
+// Eight consecutive 16-bit partial elements (one 16-byte word) as FP32.  The
+// words stay 16-bit in registers while in flight (4 VGPRs per split, so all
+// of a row's 16 splits fit) and are widened (exactly) where they are used.
 template <int IN>
-__device__ __forceinline__ void load_partial8(const void *base, int64_t off, f32x4 &lo, f32x4 &hi) {
+__device__ __forceinline__ void widen8(const u32x4 w, f32x4 &lo, f32x4 &hi) {
   if constexpr (IN == MSA_F16) {
-    const f16x8 h = __builtin_nontemporal_load((const f16x8 *)((const uint16_t *)base + off));
+    const f16x8 h = __builtin_bit_cast(f16x8, w);
     lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
     hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
   } else {
-    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)base + off));
     lo = f32x4{bf16_bits_to_f32(w[0] & 0xffffu), bf16_bits_to_f32(w[0] >> 16),
                bf16_bits_to_f32(w[1] & 0xffffu), bf16_bits_to_f32(w[1] >> 16)};
     hi = f32x4{bf16_bits_to_f32(w[2] & 0xffffu), bf16_bits_to_f32(w[2] >> 16),
@@ -94,28 +95,47 @@ __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ p
         for (int i = 0; i < B; ++i)
           l[i] = (s0 + i < S) ? plr[(int64_t)(s0 + i) * pl_split] : -INFINITY;
       }
-      f32x4 v[B][NV];
+      if constexpr (IN != MSA_F32 && NV % 2 == 0) {  // 16 bytes per 16-bit load
+        u32x4 raw[B][NV / 2];
 #pragma unroll
-      for (int i = 0; i < B; ++i)
-        if (l[i] != -INFINITY) {
-          if constexpr (IN != MSA_F32 && NV % 2 == 0) {  // 16 bytes per 16-bit load
+        for (int i = 0; i < B; ++i)
+          if (l[i] != -INFINITY) {
 #pragma unroll
-            for (int k = 0; k < NV; k += 2)
-              load_partial8<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k, v[i][k], v[i][k + 1]);
-          } else {
+            for (int k = 0; k < NV / 2; ++k)
+              raw[i][k] = __builtin_nontemporal_load(
+                  (const u32x4 *)((const uint16_t *)po + base + (int64_t)(s0 + i) * po_split + 8 * k));
+          }
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+          if (l[i] != -INFINITY) {
+            const float w = __builtin_amdgcn_exp2f((l[i] - M) * 1.4426950408889634f);
+            W += w;
+#pragma unroll
+            for (int k = 0; k < NV / 2; ++k) {
+              f32x4 lo, hi;
+              widen8<IN>(raw[i][k], lo, hi);
+              acc[2 * k] += w * lo;
+              acc[2 * k + 1] += w * hi;
+            }
+          }
+      } else {
+        f32x4 v[B][NV];
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+          if (l[i] != -INFINITY) {
 #pragma unroll
             for (int k = 0; k < NV; ++k)
               v[i][k] = load_partial4<IN>(po, base + (int64_t)(s0 + i) * po_split + 4 * k);
           }
-        }
 #pragma unroll
-      for (int i = 0; i < B; ++i)
-        if (l[i] != -INFINITY) {
-          const float w = __builtin_amdgcn_exp2f((l[i] - M) * 1.4426950408889634f);
-          W += w;
+        for (int i = 0; i < B; ++i)
+          if (l[i] != -INFINITY) {
+            const float w = __builtin_amdgcn_exp2f((l[i] - M) * 1.4426950408889634f);
+            W += w;
 #pragma unroll
-          for (int k = 0; k < NV; ++k) acc[k] += w * v[i][k];
-        }
+            for (int k = 0; k < NV; ++k) acc[k] += w * v[i][k];
+          }
+      }
     }
     const float inv = 1.0f / W;
 #pragma unroll
@@ -169,7 +189,8 @@ hipError_t launch_in(const void *po, int64_t po_split, int64_t po_row, const flo
   if constexpr (IN != MSA_F32) {  // 8 columns per thread: one 16-byte load per split
     if (dv % 8 == 0) {
       if (S <= 4) return launch_cb<8, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-      return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+      if (S <= 8) return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+      return launch_cb<8, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
     }
   }
   if (S <= 4) return launch_cb<4, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
