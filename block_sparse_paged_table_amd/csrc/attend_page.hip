@@ -112,6 +112,16 @@ __device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int,
   (f(std::integral_constant<int, Js>{}), ...);
 }
 
+// Four partial-output values as 16-bit words (RNE), two per dword.
+template <int PO> __device__ __forceinline__ u32x2 pack4_partial(f32x4 v) {
+  if constexpr (PO == MSA_F16) {
+    return u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+  } else {
+    return u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                 f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+  }
+}
+
 // ------------------------------------------------------------ page loading
 
 // F32 / BF16 / F16: K rows copied as-is (swizzled); V transposed to FP16
@@ -615,9 +625,29 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
         __builtin_nontemporal_store(va, (f32x4 *)(pa + 128 * k));
         __builtin_nontemporal_store(vb, (f32x4 *)(pb + 128 * k));
       }
-    } else {
+    } else if ((a.po_row_stride | a.po_split_stride) % 8 != 0) {
+      // 16-bit partials whose rows are only 8-byte aligned: 8 bytes per lane
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(dst, po_off + mt * 16, o[mt] * inv);
+    } else {
+      // 16-bit partials: 16 bytes per lane per store.  The lane groups of a
+      // row (grp 0-3, 4 columns each per tile) pair up, 0 with 1 and 2 with 3,
+      // through one row swap per word: the even group keeps tile 2k's words
+      // and takes its partner's, the odd group tile 2k+1's, so each lane holds
+      // 8 consecutive columns and a store covers 64 contiguous bytes of each
+      // of the 16 rows (4 stores per tile instead of 8).
+      uint16_t *const d16 = (uint16_t *)dst;
+      const int64_t rbase = po_off - grp * 4;  // the row's first element
+      const int colo = ((grp & 1) << 4) | ((grp >> 1) << 3);
+      const bool even = (grp & 1) == 0;
+#pragma unroll
+      for (int k = 0; k < MT / 2; ++k) {
+        const u32x2 w0 = pack4_partial<PO>(o[2 * k] * inv), w1 = pack4_partial<PO>(o[2 * k + 1] * inv);
+        const auto sx = __builtin_amdgcn_permlane16_swap(w0[0], w1[0], false, false);
+        const auto sy = __builtin_amdgcn_permlane16_swap(w0[1], w1[1], false, false);
+        const u32x4 v = even ? u32x4{w0[0], w0[1], sx[1], sy[1]} : u32x4{sx[0], sy[0], w1[0], w1[1]};
+        *(u32x4 *)(d16 + rbase + 32 * k + colo) = v;
+      }
     }
     float *ldst = (active && grp == 0) ? a.partial_lse + (int64_t)slot * a.pl_split_stride + row
                                        : dump + D + lane;

@@ -128,17 +128,22 @@ def test_fp32_output_and_bf16_output_agree():
     check_combined(p, out, lse, ref, "bf16")
 
 
-@pytest.mark.parametrize("qd,kd,d,pad", [("f32", "f32", 64, 32), ("e4m3", "nvfp4", 128, 4),
-                                         ("bf16", "bf16", 128, 12), ("e4m3", "e4m3", 64, 4)])
-def test_strided_partial_buffer(qd, kd, d, pad):
-    """Padded partial rows (row stride d + pad, so rows are not 128-byte aligned):
-    the whole-line stores of FP32 partials must land on each row's own bytes."""
+@pytest.mark.parametrize("qd,kd,d,pad,pd", [("f32", "f32", 64, 32, "f32"), ("e4m3", "nvfp4", 128, 4, "f32"),
+                                            ("bf16", "bf16", 128, 12, "f32"), ("e4m3", "e4m3", 64, 4, "f32"),
+                                            ("e4m3", "nvfp4", 128, 4, "f16"), ("bf16", "bf16", 64, 8, "bf16"),
+                                            ("e4m3", "e4m3", 128, 24, "f16")])
+def test_strided_partial_buffer(qd, kd, d, pad, pd):
+    """Padded partial rows (row stride d + pad, so rows are not 128-byte
+    aligned): the whole-line stores of FP32 partials and the 16-byte stores of
+    16-bit partials (8-byte-aligned rows take 8-byte stores) must land on each
+    row's own bytes."""
     p = _small(14, q_dtype=qd, kv_dtype=kd, d=d, Hq=8, Hkv=2)
-    dp = _run(p, po_row_pad=pad)
+    dp = _run(p, po_row_pad=pad, partial_dtype=pd)
     ref = oracle.prefill_rows(p)
     po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
-    check_partials(p, po, pl, ref)
-    check_combined(p, out, lse, ref, "f32")
+    check_partials(p, po, pl, ref, stored=pd)
+    if pd == "f32":
+        check_combined(p, out, lse, ref, "f32")
 
 
 def test_shared_selection_stride_zero():
