@@ -117,8 +117,7 @@ template <int PO> __device__ __forceinline__ u32x2 pack4_partial(f32x4 v) {
   if constexpr (PO == MSA_F16) {
     return u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
   } else {
-    return u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                 f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+    return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 

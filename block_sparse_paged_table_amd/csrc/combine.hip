@@ -149,8 +149,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ p
     if constexpr (OUT == MSA_F32) {
       *(f32x4 *)((float *)out + o) = a;
     } else if constexpr (OUT == MSA_BF16) {
-      uint32_t lo = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
-      uint32_t hi = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+      const uint32_t lo = pack_bf16x2(a[0], a[1]);
+      const uint32_t hi = pack_bf16x2(a[2], a[3]);
       *(u32x2 *)((uint16_t *)out + o) = u32x2{lo, hi};
     } else {
       *(u32x2 *)((uint16_t *)out + o) = u32x2{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3])};

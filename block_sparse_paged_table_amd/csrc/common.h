@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -117,6 +118,13 @@ __host__ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats as BF16 (round to nearest even; finite values), low half first:
+// one packed hardware conversion on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   f16x2 v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
@@ -132,8 +140,7 @@ __device__ __forceinline__ void store_partial4(void *base, int64_t off, f32x4 v)
     *(u32x2 *)((uint16_t *)base + off) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
   } else {
     *(u32x2 *)((uint16_t *)base + off) =
-        u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-              f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 
