@@ -635,17 +635,39 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
       // and takes its partner's, the odd group tile 2k+1's, so each lane holds
       // 8 consecutive columns and a store covers 64 contiguous bytes of each
       // of the 16 rows (4 stores per tile instead of 8).
-      uint16_t *const d16 = (uint16_t *)dst;
+      // Then, as for FP32 partials, lanes n and n + 8 of each 16-lane row swap
+      // one of each pair of 64-byte blocks, so a store writes whole 128-byte
+      // lines of 8 rows (blocks 2j, 2j+1 of rows 0-7, then of rows 8-15),
+      // non-temporally; addresses are byte offsets from partial_o (the
+      // scratch row's too).
       const int64_t rbase = po_off - grp * 4;  // the row's first element
       const int colo = ((grp & 1) << 4) | ((grp >> 1) << 3);
       const bool even = (grp & 1) == 0;
+      u32x4 v[MT / 2];
 #pragma unroll
       for (int k = 0; k < MT / 2; ++k) {
         const u32x2 w0 = pack4_partial<PO>(o[2 * k] * inv), w1 = pack4_partial<PO>(o[2 * k + 1] * inv);
         const auto sx = __builtin_amdgcn_permlane16_swap(w0[0], w1[0], false, false);
         const auto sy = __builtin_amdgcn_permlane16_swap(w0[1], w1[1], false, false);
-        const u32x4 v = even ? u32x4{w0[0], w0[1], sx[1], sy[1]} : u32x4{sx[0], sy[0], w1[0], w1[1]};
-        *(u32x4 *)(d16 + rbase + 32 * k + colo) = v;
+        v[k] = even ? u32x4{w0[0], w0[1], sx[1], sy[1]} : u32x4{sx[0], sy[0], w1[0], w1[1]};
+      }
+      uint8_t *const base = (uint8_t *)a.partial_o;
+      const int64_t own_off = ((uint8_t *)dst - base) + (rbase + colo) * 2;
+      const int64_t partner_off = (int64_t)(((uint64_t)swap_half_row((uint32_t)((uint64_t)own_off >> 32)) << 32) |
+                                            swap_half_row((uint32_t)own_off));
+      const bool lo_half = n < 8;
+      uint8_t *const pa = base + (lo_half ? own_off : partner_off + 64);
+      uint8_t *const pb = base + (lo_half ? partner_off : own_off + 64);
+#pragma unroll
+      for (int j = 0; j < MT / 4; ++j) {
+        u32x4 va, vb;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          va[w] = from_half_row<0xc>(v[2 * j][w], v[2 * j + 1][w]);
+          vb[w] = from_half_row<0x3>(v[2 * j + 1][w], v[2 * j][w]);
+        }
+        __builtin_nontemporal_store(va, (u32x4 *)(pa + 128 * j));
+        __builtin_nontemporal_store(vb, (u32x4 *)(pb + 128 * j));
       }
     }
     float *ldst = (active && grp == 0) ? a.partial_lse + (int64_t)slot * a.pl_split_stride + row
