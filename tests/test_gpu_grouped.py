@@ -191,3 +191,40 @@ def test_page4_small_chunk_workload():
     16 splits), every row against the oracle."""
     p = synth.make_page4_small_chunk(ctx_len=24240)
     _parity(p)
+
+
+@pytest.mark.parametrize("spp", [48, 12])
+def test_grouped_graph_capture_replays_match_eager(spp):
+    """Grouped plan + attention + combine captured in one HIP graph (kernels
+    only: the planner clears its counters with a kernel, not a memset node);
+    every replay, with eager work and clobbered outputs in between,
+    reproduces the eager results bit for bit, one split or split-k."""
+    p = dataclasses.replace(_mb(41), slots_per_split=spp)
+    dp = DeviceProblem(p)
+    dp.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dp.partial_lse, dp.partial_o, dp.out, dp.lse)]
+    err = dp.err_flags()
+    live = ref[0] > -float("inf")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dp.run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (dp.partial_o, dp.out, dp.lse, dp.partial_lse):
+            t.fill_(float(i + 1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.partial_lse, ref[0]), i
+        assert torch.equal(dp.partial_o[live], ref[1][live]), i
+        assert torch.equal(dp.out, ref[2]) and torch.equal(dp.lse, ref[3]), i
+        assert dp.err_flags() == err
+        dp.run()  # eager work between replays
+        torch.cuda.synchronize()

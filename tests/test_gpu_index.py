@@ -155,6 +155,39 @@ def test_index_deterministic():
         assert all(torch.equal(x, y) for x, y in zip(outs[0], o))
 
 
+def test_index_graph_capture_replays_match_eager():
+    """Page scores + top-k captured in one HIP graph (kernels only: the error
+    word is cleared by a kernel); every replay, with eager work and clobbered
+    outputs in between, reproduces the eager scores and selections."""
+    ip = _small(46)
+    dev = DeviceIndexProblem(ip)
+    dev.run()
+    torch.cuda.synchronize()
+    ref = (dev.scores.clone(), dev.sel_idx.clone(), dev.sel_mask.clone())
+    err = dev.err_flags()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dev.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dev.run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        dev.scores.fill_(float(i + 1))
+        dev.sel_idx.fill_(-7)
+        dev.sel_mask.fill_(3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(ref, (dev.scores, dev.sel_idx, dev.sel_mask))), i
+        assert dev.err_flags() == err
+        dev.run()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_index_error_rows():
     ip = _small(45)
     q_seq = ip.q_seq.numpy().copy()
