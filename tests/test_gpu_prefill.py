@@ -344,3 +344,31 @@ def test_full_size_config_sampled(cfg):
     po, pl, out, lse = gpu_rows(dp, toks)
     check_partials(p, po, pl, ref)
     check_combined(p, out, lse, ref, dp.out_dtype)
+
+
+@pytest.mark.parametrize("cfg,pd", [(2, "f16"), (2, "bf16"), (4, "bf16"), (1, "f16")])
+def test_full_size_16bit_partials(cfg, pd):
+    """16-bit partial storage at full size, in the launch configuration the
+    benchmark's partial-dtype variants time: every live partial is the
+    rounding of the same kernel's FP32 partial (whole tensor, bit for bit),
+    the LSEs are identical, and sampled rows match the oracle within the
+    storage-rounding floor."""
+    p = synth.make_config(cfg)
+    dp32 = _run(p)
+    live = dp32.partial_lse > -float("inf")
+    dt = torch.float16 if pd == "f16" else torch.bfloat16
+    ref16 = dp32.partial_o[live].to(dt)
+    lse32 = dp32.partial_lse.clone()
+    del dp32
+    torch.cuda.empty_cache()
+    dp = _run(p, partial_dtype=pd)
+    assert dp.partial_o.dtype == dt
+    assert torch.equal(dp.partial_lse, lse32)
+    assert torch.equal(dp.partial_o[live], ref16)
+    assert dp.err_flags() == 0
+    del ref16, lse32
+    toks = _sample_tokens(p, n=24)
+    keep = oracle.make_keep(p)
+    ref = oracle.prefill_rows(p, toks, keep=keep)
+    po, pl, out, lse = gpu_rows(dp, toks)
+    check_partials(p, po, pl, ref, stored=pd)
