@@ -160,11 +160,75 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
 
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = kScanTile / kScanThreads;  // lists per thread
+constexpr int kScanOneBlockMax = kScanThreads * 8;  // lists one workgroup scans alone
 
-// Exclusive scans of list sizes (-> list_off, entry offsets) and of work
-// units per list (-> unit_off), in three steps: per tile of kScanTile lists,
-// over the tile totals, then tile offsets added back.  With a single tile
-// the first step writes the final values.
+// Up to kScanOneBlockMax lists: one workgroup scans them all, PER lists per
+// thread -- inclusive scans within each wave by shuffles, the wave totals
+// through LDS behind a single barrier -- and writes the final offsets.
+template <int PER>
+__global__ void __launch_bounds__(kScanThreads) plan_scan_one(const PageArgs a) {
+  constexpr int NW = kScanThreads / 64;
+  __shared__ int32_t w_e[NW], w_u[NW];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t L = a.lay.num_lists;
+  const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
+  int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
+  int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
+  const int64_t i0 = (int64_t)t * PER;
+  int32_t c[PER], u[PER];
+  int32_t se = 0, su = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    // unconditional loads (clamped index; L >= 1), so that all of them are
+    // in flight at once instead of one branch and wait per list
+    const int32_t v = counts[min(i0 + k, L - 1)];
+    c[k] = i0 + k < L ? v : 0;
+    u[k] = (c[k] + a.chunk - 1) / a.chunk;
+    se += c[k];
+    su += u[k];
+  }
+  int32_t ie = se, iu = su;  // inclusive scans over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t ve = __shfl_up(ie, off), vu = __shfl_up(iu, off);
+    if (lane >= off) {
+      ie += ve;
+      iu += vu;
+    }
+  }
+  if (lane == 63) {
+    w_e[w] = ie;
+    w_u[w] = iu;
+  }
+  __syncthreads();
+  int32_t oe = 0, ou = 0;  // totals of the earlier waves
+  for (int k = 0; k < w; ++k) {
+    oe += w_e[k];
+    ou += w_u[k];
+  }
+  int32_t be = oe + ie - se, bu = ou + iu - su;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (i0 + k < L) {
+      list_off[i0 + k] = be;
+      unit_off[i0 + k] = bu;
+    }
+    be += c[k];
+    bu += u[k];
+  }
+  if (t == kScanThreads - 1) {
+    int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
+    list_off[L] = be;
+    unit_off[L] = bu;
+    meta[0] = bu;  // number of work units
+    meta[2] = be;  // number of entries
+  }
+}
+
+// More lists: exclusive scans of list sizes (-> list_off, entry offsets) and
+// of work units per list (-> unit_off), in three steps: per tile of
+// kScanTile lists, over the tile totals, then tile offsets added back.
+template <int PER>
 __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a) {
   __shared__ int32_t s_e[kScanThreads];
   __shared__ int32_t s_u[kScanThreads];
@@ -173,12 +237,13 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
   const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
-  const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)t * kScanPer;
-  int32_t c[kScanPer];
+  const int64_t i0 = (int64_t)blockIdx.x * (kScanThreads * PER) + (int64_t)t * PER;
+  int32_t c[PER];
   int32_t se = 0, su = 0;
 #pragma unroll
-  for (int k = 0; k < kScanPer; ++k) {
-    c[k] = i0 + k < L ? counts[i0 + k] : 0;
+  for (int k = 0; k < PER; ++k) {
+    const int32_t v = counts[min(i0 + k, L - 1)];
+    c[k] = i0 + k < L ? v : 0;
     se += c[k];
     su += (c[k] + a.chunk - 1) / a.chunk;
   }
@@ -195,7 +260,7 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
   }
   int32_t be = s_e[t] - se, bu = s_u[t] - su;
 #pragma unroll
-  for (int k = 0; k < kScanPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     if (i0 + k < L) {
       list_off[i0 + k] = be;
       unit_off[i0 + k] = bu;
@@ -312,9 +377,13 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
     else
       plan_count<false><<<count_blocks, kCountThreads, 0, s>>>(a);
   }
-  const int nt = (int)((L + kScanTile - 1) / kScanTile);
-  plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
-  if (nt > 1) {
+  if (L <= kScanTile) {
+    plan_scan_one<kScanPer><<<1, kScanThreads, 0, s>>>(a);
+  } else if (L <= kScanOneBlockMax) {
+    plan_scan_one<kScanOneBlockMax / kScanThreads><<<1, kScanThreads, 0, s>>>(a);
+  } else {
+    const int nt = (int)((L + kScanTile - 1) / kScanTile);
+    plan_scan_tiles<kScanPer><<<nt, kScanThreads, 0, s>>>(a);
     plan_scan_top<<<1, kScanThreads, 0, s>>>(a, nt);
     plan_scan_add<<<nt - 1, kScanThreads, 0, s>>>(a);
   }

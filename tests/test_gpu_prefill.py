@@ -75,14 +75,16 @@ def test_ordering_slices_bitwise_identical(Hq, Hkv, qd, kd):
     written partial, the combined output and the LSE are bitwise equal for any
     slice length, and match the oracle with many slices."""
     # a long context makes many (slice, page, head) lists: the plan's scan
-    # then runs over several tiles
+    # runs over several tiles (slices of 1 and 100 tokens, > 8192 lists), in
+    # one workgroup at 8 lists per thread (200, 300: 4097-8192 lists at
+    # 16 heads) or at 4 (one slice)
     p = _small(21, Hq=Hq, Hkv=Hkv, q_dtype=qd, kv_dtype=kd, ctx_lens=[0, 20000, 1000],
                chunk_lens=[700, 450, 600], num_slots=8)
     _full_parity(p, order_slice_tokens=1)
     ref = _run(p)
     live = ref.partial_lse > -float("inf")
     assert live.any() and not live.all()
-    for st in (1, 100, 300, 1 << 20):
+    for st in (1, 100, 200, 300, 1 << 20):
         dp = _run(p, order_slice_tokens=st)
         assert torch.equal(dp.partial_lse, ref.partial_lse), st
         assert torch.equal(dp.partial_o[live], ref.partial_o[live]), st
