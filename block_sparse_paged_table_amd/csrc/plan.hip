@@ -76,6 +76,12 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
   const int K = a.num_slots;
   int32_t *slot_list = (int32_t *)(a.ws + a.lay.slot_list) + idx * K;
   int32_t *slot_pos = (int32_t *)(a.ws + a.lay.slot_pos) + idx * K;
+  // rows of at most kRegSlots slots keep each slot's list (local index, -1:
+  // none) and its position in the workgroup's block in registers until the
+  // block offsets are known, and store the final position once
+  int lr[kRegSlots], pr[kRegSlots];
+#pragma unroll
+  for (int j = 0; j < kRegSlots; ++j) lr[j] = -1, pr[j] = 0;
   if (live) {
     const int r = (int)(idx / a.Hkv), g = (int)(idx - (int64_t)r * a.Hkv);
     const int32_t *sidx = a.sel_idx + r * a.sel_stride_tok + g * a.sel_stride_head;
@@ -83,8 +89,9 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
     uint32_t err = 0;
     const RowCtx c = row_ctx(a, r, err);
     const int bb = c.valid ? c.b : 0;  // an in-bounds table row for the loads below
-    // slot j: validate, find its list, claim a position (or mark the split empty)
-    auto visit = [&](int j, uint32_t mk, int u, bool dup, int pp) {
+    // slot j: validate, find its list, claim a position (or mark the split
+    // empty); returns the list (-1: none) and, in `pos`, the position claimed
+    auto visit = [&](int j, uint32_t mk, int u, bool dup, int pp, int &pos, bool store_pos) -> int {
       int list = -1;
       if (c.valid && mk) {
         if (u < 0 || u >= a.max_pages) {
@@ -100,11 +107,13 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
       }
       slot_list[j] = list >= 0 ? (int32_t)(lbase + list) : -1;
       if (list >= 0) {
-        slot_pos[j] = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[lbase + list], 1);
+        pos = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[lbase + list], 1);
+        if (store_pos) slot_pos[j] = pos;
       } else {
         float *pl = a.partial_lse + j * a.pl_split_stride + (int64_t)r * a.Hq + g * a.G;
         for (int h = 0; h < a.G; ++h) pl[h] = -INFINITY;
       }
+      return list;
     };
     if (K <= kRegSlots) {
       // every load of the row is issued before any is used; the duplicate
@@ -128,7 +137,7 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
           bool dup = false;
 #pragma unroll
           for (int jj = 0; jj < j; ++jj) dup |= (mk[jj] != 0u) && (uu[jj] == uu[j]);
-          visit(j, mk[j], uu[j], dup, pp[j]);
+          lr[j] = visit(j, mk[j], uu[j], dup, pp[j], pr[j], !LDS_HIST);
         }
       }
     } else {
@@ -138,7 +147,8 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
         bool dup = false;
         for (int jj = 0; jj < j; ++jj) dup |= (smask[jj] != 0) && (sidx[jj] == u);
         const int uc = (u >= 0 && u < a.max_pages) ? u : 0;
-        visit(j, mk, u, dup, a.page_table[bb * a.pt_stride + uc]);
+        int pos = 0;
+        visit(j, mk, u, dup, a.page_table[bb * a.pt_stride + uc], pos, true);
       }
     }
     if (err) atomicOr(a.err_flags, err);
@@ -150,11 +160,18 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
       if (n) hist[i] = atomicAdd(&counts[lbase + i], n);  // this workgroup's block of list i
     }
     __syncthreads();
-    if (live)
-      for (int j = 0; j < K; ++j) {
-        const int list = slot_list[j];
-        if (list >= 0) slot_pos[j] += hist[list - lbase];
+    if (live) {
+      if (K <= kRegSlots) {
+#pragma unroll
+        for (int j = 0; j < kRegSlots; ++j)
+          if (lr[j] >= 0) slot_pos[j] = pr[j] + hist[lr[j]];
+      } else {
+        for (int j = 0; j < K; ++j) {
+          const int list = slot_list[j];
+          if (list >= 0) slot_pos[j] += hist[list - lbase];
+        }
       }
+    }
   }
 }
 
