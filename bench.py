@@ -108,6 +108,10 @@ def main():
                     help="cache dtype variant of the Q8 workloads (e4m3: the Q8KV8 route)")
     ap.add_argument("--partial-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="partial_o storage (the workloads specify f32)")
+    ap.add_argument("--partial-layout", choices=["row", "split"], default="row",
+                    help="partial_o layout, through the ABI's split / row strides: "
+                         "[row][split][d] (each row's splits one contiguous run, which the "
+                         "combine reads in order) or [split][row][d]")
     ap.add_argument("--index", action="store_true",
                     help="time the paged prefill indexer (page scores + top-k) instead")
     ap.add_argument("--workload", choices=["page4_small_chunk"], default=None,
@@ -164,7 +168,8 @@ def main():
             (p0.total_q, p0.num_rows, p0.num_splits, p0.d_v), "input sets differ in shape"
     # one partial buffer / output shared by all sets (the biggest allocations)
     pd = args.partial_dtype
-    dps = [DeviceProblem(probs[0], order_slice_tokens=args.slice_tokens, partial_dtype=pd)]
+    dps = [DeviceProblem(probs[0], order_slice_tokens=args.slice_tokens, partial_dtype=pd,
+                         partial_layout=args.partial_layout)]
     for p in probs[1:]:
         dps.append(DeviceProblem(p, partial_o=dps[0].partial_o, partial_lse=dps[0].partial_lse,
                                  order_slice_tokens=args.slice_tokens, partial_dtype=pd))
@@ -213,6 +218,8 @@ def main():
     kv_bytes = int(kv_bytes * min(1.0, st["touched_kv_rows"] / cache_rows))  # touched units only
     pe = dp.partial_o.element_size()
     wname = p.name + ("" if pd == "f32" else f"+{pd}_partials")
+    if args.partial_layout == "split":
+        wname += "+split_major_partials"
     if args.slots_per_split:
         wname += f"+{p.num_splits}_splits"
     attn_bytes = pe * dv * st["nonempty"] + 4 * st["nonempty"] + tensor_bytes(dp.q) + kv_bytes
@@ -257,7 +264,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": mfma_dtype, "data": "synthetic",
         "config": {"workload": wname,
-                   "description": p.description, "partial_dtype": pd, "total_q": p.total_q,
+                   "description": p.description, "partial_dtype": pd, "partial_layout": args.partial_layout, "total_q": p.total_q,
                    "Hq": p.Hq, "Hkv": p.Hkv, "head_dim": p.d_qk, "page_size": p.page_size,
                    "slots": p.num_slots, "splits": p.num_splits, "input_sets": len(dps)},
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4),

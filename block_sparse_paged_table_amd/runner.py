@@ -28,7 +28,8 @@ class DeviceProblem:
 
     def __init__(self, p: Problem, device: str = "cuda", out_dtype: str = None,
                  partial_o: torch.Tensor = None, partial_lse: torch.Tensor = None,
-                 po_row_pad: int = 0, order_slice_tokens: int = 0, partial_dtype: str = "f32"):
+                 po_row_pad: int = 0, order_slice_tokens: int = 0, partial_dtype: str = "f32",
+                 partial_layout: str = "split"):
         self.p = p
         self.order_slice_tokens = order_slice_tokens
         self.partial_dtype = partial_dtype
@@ -56,7 +57,14 @@ class DeviceProblem:
         self.sel_idx = p.sel_idx.to(dev)
         self.sel_mask = p.sel_mask.to(dev)
         S, rows, dv = p.num_splits, p.num_rows, p.d_v
-        if partial_o is None:
+        if partial_o is None and partial_layout == "row":
+            # [row][split][d]: each row's splits form one contiguous run, which
+            # the combine then reads in order; viewed as [split][row][d]
+            partial_o = torch.empty((rows, S, dv + po_row_pad), dtype=OUT_TORCH[partial_dtype],
+                                    device=dev).permute(1, 0, 2)
+        elif partial_o is None:
+            if partial_layout != "split":
+                raise ValueError(f"partial_layout {partial_layout!r}: 'split' or 'row'")
             partial_o = torch.empty((S, rows, dv + po_row_pad), dtype=OUT_TORCH[partial_dtype],
                                     device=dev)
         if partial_lse is None:

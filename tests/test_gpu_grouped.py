@@ -228,3 +228,23 @@ def test_grouped_graph_capture_replays_match_eager(spp):
         assert dp.err_flags() == err
         dp.run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("spp", [48, 12])
+def test_grouped_row_major_partials(spp):
+    """Grouped route with partial_o laid out [row][split][d]: bit for bit the
+    split-major results, and the oracle's within tolerance."""
+    p = dataclasses.replace(_mb(43), slots_per_split=spp)
+    dp = DeviceProblem(p, partial_layout="row")
+    dp.run()
+    ref = DeviceProblem(p)
+    ref.run()
+    torch.cuda.synchronize()
+    live = ref.partial_lse > -float("inf")
+    assert torch.equal(dp.partial_lse, ref.partial_lse)
+    assert torch.equal(dp.partial_o[live], ref.partial_o[live])
+    assert torch.equal(dp.out, ref.out) and torch.equal(dp.lse, ref.lse)
+    oref = oracle.prefill_rows(p)
+    po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+    check_partials(p, po, pl, oref)
+    check_combined(p, out, lse, oref, dp.out_dtype)

@@ -374,3 +374,51 @@ def test_full_size_16bit_partials(cfg, pd):
     ref = oracle.prefill_rows(p, toks, keep=keep)
     po, pl, out, lse = gpu_rows(dp, toks)
     check_partials(p, po, pl, ref, stored=pd)
+
+
+@pytest.mark.parametrize("qd,kd,pd", [("e4m3", "nvfp4", "f32"), ("bf16", "bf16", "f16"),
+                                      ("e4m3", "e4m3", "bf16"), ("f32", "f32", "f32")])
+def test_row_major_partials(qd, kd, pd):
+    """partial_o laid out [row][split][d] (split stride d, row stride
+    splits * d): the same values as the split-major layout, bit for bit, and
+    the combine reads them through the same strides."""
+    p = _small(27, q_dtype=qd, kv_dtype=kd, Hq=8, Hkv=2, d=64 if qd == "f32" else 128)
+    dp = _run(p, partial_dtype=pd, partial_layout="row")
+    assert dp.partial_o.stride(0) == p.d_v and dp.partial_o.stride(1) == p.num_splits * p.d_v
+    ref = _run(p, partial_dtype=pd)
+    live = ref.partial_lse > -float("inf")
+    assert live.any() and not live.all()
+    assert torch.equal(dp.partial_lse, ref.partial_lse)
+    assert torch.equal(dp.partial_o[live], ref.partial_o[live])
+    assert torch.equal(dp.out, ref.out) and torch.equal(dp.lse, ref.lse)
+    assert dp.err_flags() == ref.err_flags()
+    if pd == "f32":
+        oref = oracle.prefill_rows(p)
+        po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
+        check_partials(p, po, pl, oref)
+        check_combined(p, out, lse, oref, dp.out_dtype)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_row_major_partials(cfg):
+    """The benchmark's partial layout at full size: every partial, the output
+    and the LSE equal the split-major run bit for bit; sampled rows against
+    the oracle."""
+    p = synth.make_config(cfg)
+    ref = _run(p)
+    live = ref.partial_lse > -float("inf")
+    ref_o = ref.partial_o[live].clone()
+    ref_l, ref_out, ref_lse = ref.partial_lse.clone(), ref.out.clone(), ref.lse.clone()
+    del ref
+    torch.cuda.empty_cache()
+    dp = _run(p, partial_layout="row")
+    assert torch.equal(dp.partial_lse, ref_l)
+    assert torch.equal(dp.partial_o[live], ref_o)
+    assert torch.equal(dp.out, ref_out) and torch.equal(dp.lse, ref_lse)
+    assert dp.err_flags() == 0
+    del ref_o
+    toks = _sample_tokens(p, n=16)
+    oref = oracle.prefill_rows(p, toks, keep=oracle.make_keep(p))
+    po, pl, out, lse = gpu_rows(dp, toks)
+    check_partials(p, po, pl, oref)
+    check_combined(p, out, lse, oref, dp.out_dtype)
