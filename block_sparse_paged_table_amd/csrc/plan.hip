@@ -245,8 +245,8 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_one(const PageArgs a) 
 // More lists: exclusive scans of list sizes (-> list_off, entry offsets) and
 // of work units per list (-> unit_off), in three steps: per tile of
 // kScanTile lists, over the tile totals, then tile offsets added back.
-template <int PER>
 __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a) {
+  constexpr int PER = kScanPer;
   __shared__ int32_t s_e[kScanThreads];
   __shared__ int32_t s_u[kScanThreads];
   const int t = threadIdx.x;
@@ -285,18 +285,10 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
     be += c[k];
     bu += (c[k] + a.chunk - 1) / a.chunk;
   }
-  if (t == kScanThreads - 1) {
-    if (gridDim.x == 1) {
-      int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
-      list_off[L] = s_e[t];
-      unit_off[L] = s_u[t];
-      meta[0] = s_u[t];  // number of work units
-      meta[2] = s_e[t];  // number of entries
-    } else {
-      int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
-      tiles[2 * blockIdx.x] = s_e[t];
-      tiles[2 * blockIdx.x + 1] = s_u[t];
-    }
+  if (t == kScanThreads - 1) {  // this tile's totals, for plan_scan_top
+    int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
+    tiles[2 * blockIdx.x] = s_e[t];
+    tiles[2 * blockIdx.x + 1] = s_u[t];
   }
 }
 
@@ -400,7 +392,7 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
     plan_scan_one<kScanOneBlockMax / kScanThreads><<<1, kScanThreads, 0, s>>>(a);
   } else {
     const int nt = (int)((L + kScanTile - 1) / kScanTile);
-    plan_scan_tiles<kScanPer><<<nt, kScanThreads, 0, s>>>(a);
+    plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
     plan_scan_top<<<1, kScanThreads, 0, s>>>(a, nt);
     plan_scan_add<<<nt - 1, kScanThreads, 0, s>>>(a);
   }
