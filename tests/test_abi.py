@@ -202,3 +202,24 @@ def test_index_validation_rejects(over):
     for fn in calls:  # every case is rejected on the host: nothing is launched
         assert fn(ctypes.byref(d), None) in (1, 2), fn
 
+
+
+@pytest.mark.parametrize("layout,pad", [("row", 0), ("split", 0), ("row", 8)])
+def test_partial_layouts_describe_their_strides(layout, pad):
+    """The device harness builds descriptors on the host: a row-major partial
+    buffer ([row][split][d]) is described by split stride d and row stride
+    splits * d; a split-major one by row stride d and split stride rows * d
+    (padded rows widen both); the workspace does not depend on the layout."""
+    from block_sparse_paged_table_amd import synth
+    from block_sparse_paged_table_amd.runner import DeviceProblem
+    p = synth.make_config(0)
+    dp = DeviceProblem(p, device="cpu", partial_layout=layout, po_row_pad=pad)
+    S, rows, w = p.num_splits, p.num_rows, p.d_v + pad
+    assert tuple(dp.partial_o.shape) == (S, rows, w)
+    if layout == "row":
+        assert (dp.desc.po_split_stride, dp.desc.po_row_stride) == (w, S * w)
+    else:
+        assert (dp.desc.po_split_stride, dp.desc.po_row_stride) == (rows * w, w)
+    assert dp.ws_bytes == DeviceProblem(p, device="cpu").ws_bytes
+    with pytest.raises(ValueError):
+        DeviceProblem(p, device="cpu", partial_layout="column")
