@@ -56,22 +56,27 @@ __device__ __forceinline__ RowCtx row_ctx(const PageArgs &a, int r, uint32_t &er
   return c;
 }
 
-constexpr int kCountThreads = 64;  // rows per plan_count workgroup (slice_rows is a multiple)
+// Rows per plan_count workgroup (slice_rows is a multiple of both): 64 keeps
+// many workgroups in flight; 256 when a slice has many lists, since every
+// workgroup clears and claims all of its slice's lists.
+constexpr int kCountThreads = 64;
+constexpr int kCountThreadsWide = 256;
+constexpr int kCountWideLists = 2048;  // lists per slice from which the wide form is used
 constexpr int kRegSlots = 16;      // rows with at most this many slots keep them in registers
 
-template <bool LDS_HIST>
-__global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
+template <bool LDS_HIST, int NT>
+__global__ void __launch_bounds__(NT) plan_count(const PageArgs a) {
   extern __shared__ int32_t hist[];
   const int64_t L = a.lists_per_slice;
   const int tid = threadIdx.x;
   // slice_rows is a multiple of the block size: one slice per workgroup
-  const int64_t lbase = ((int64_t)blockIdx.x * kCountThreads) / a.slice_rows * L;
+  const int64_t lbase = ((int64_t)blockIdx.x * NT) / a.slice_rows * L;
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
   if constexpr (LDS_HIST) {
-    for (int64_t i = tid; i < L; i += kCountThreads) hist[i] = 0;
+    for (int64_t i = tid; i < L; i += NT) hist[i] = 0;
     __syncthreads();
   }
-  const int64_t idx = (int64_t)blockIdx.x * kCountThreads + tid;
+  const int64_t idx = (int64_t)blockIdx.x * NT + tid;
   const bool live = idx < (int64_t)a.total_q * a.Hkv;
   const int K = a.num_slots;
   int32_t *slot_list = (int32_t *)(a.ws + a.lay.slot_list) + idx * K;
@@ -155,7 +160,7 @@ __global__ void __launch_bounds__(kCountThreads) plan_count(const PageArgs a) {
   }
   if constexpr (LDS_HIST) {
     __syncthreads();
-    for (int64_t i = tid; i < L; i += kCountThreads) {
+    for (int64_t i = tid; i < L; i += NT) {
       const int32_t n = hist[i];
       if (n) hist[i] = atomicAdd(&counts[lbase + i], n);  // this workgroup's block of list i
     }
@@ -379,12 +384,18 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   plan_zero<<<(unsigned)zero_blocks, 256, 0, s>>>(counts, L, a.err_flags);
   const int64_t rows = (int64_t)a.total_q * a.Hkv;
   const unsigned blocks = (unsigned)((rows + kPlanThreads - 1) / kPlanThreads);
-  const unsigned count_blocks = (unsigned)((rows + kCountThreads - 1) / kCountThreads);
-  if (count_blocks) {
-    if (a.lists_per_slice <= kMaxLdsLists)
-      plan_count<true><<<count_blocks, kCountThreads, (size_t)a.lists_per_slice * 4, s>>>(a);
-    else
-      plan_count<false><<<count_blocks, kCountThreads, 0, s>>>(a);
+  if (rows > 0) {
+    const size_t hist_bytes = (size_t)a.lists_per_slice * 4;
+    if (a.lists_per_slice > kMaxLdsLists) {
+      plan_count<false, kCountThreads><<<(unsigned)((rows + kCountThreads - 1) / kCountThreads),
+                                         kCountThreads, 0, s>>>(a);
+    } else if (a.lists_per_slice > kCountWideLists) {
+      plan_count<true, kCountThreadsWide><<<(unsigned)((rows + kCountThreadsWide - 1) / kCountThreadsWide),
+                                            kCountThreadsWide, hist_bytes, s>>>(a);
+    } else {
+      plan_count<true, kCountThreads><<<(unsigned)((rows + kCountThreads - 1) / kCountThreads),
+                                        kCountThreads, hist_bytes, s>>>(a);
+    }
   }
   if (L <= kScanTile) {
     plan_scan_one<kScanPer><<<1, kScanThreads, 0, s>>>(a);
