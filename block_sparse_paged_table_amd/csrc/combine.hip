@@ -57,14 +57,14 @@ __device__ __forceinline__ void widen8(const u32x4 w, f32x4 &lo, f32x4 &hi) {
 }
 
 template <int CPT, int B, int OUT, int IN>
-__global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ po, int64_t po_split,
+__global__ void __launch_bounds__(512) combine_kernel(const void *__restrict__ po, int64_t po_split,
                                                       int64_t po_row, const float *__restrict__ pl,
                                                       int64_t pl_split, int S, int64_t rows, int dv,
                                                       void *__restrict__ out, int64_t out_row,
                                                       float *__restrict__ lse_out) {
   constexpr int NV = CPT / 4;                   // 16-byte vectors per split and thread
   const int tpr = dv / CPT;                     // threads per row
-  const int rows_per_block = blockDim.x / tpr;  // host guarantees tpr <= 256
+  const int rows_per_block = blockDim.x / tpr;  // host guarantees tpr <= 256 (blocks of 512)
   const int tid = threadIdx.x;
   const int r_local = tid / tpr;
   const int cc = tid - r_local * tpr;
@@ -165,18 +165,18 @@ hipError_t launch_cb(const void *po, int64_t po_split, int64_t po_row, const flo
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
                      int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
   const int tpr = dv / CPT;  // <= 256 (head_dim_v <= 1024)
-  const int rpb = 256 / tpr;
+  const int rpb = 512 / tpr;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   if (blocks == 0) return hipSuccess;
   switch (out_dtype) {
     case MSA_F32:
-      combine_kernel<CPT, B, MSA_F32, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F32, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
     case MSA_BF16:
-      combine_kernel<CPT, B, MSA_BF16, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_BF16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
     default:
-      combine_kernel<CPT, B, MSA_F16, IN><<<(unsigned)blocks, 256, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
       break;
   }
   return hipGetLastError();
