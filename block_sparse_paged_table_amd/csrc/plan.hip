@@ -27,7 +27,7 @@
 namespace msa {
 namespace {
 
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 64;  // plan_fill: one (token, KV head) row per thread, many workgroups
 constexpr int kMaxLdsLists = 16384;  // lists an LDS histogram may hold (64 KiB)
 
 __global__ void plan_zero(int32_t *counts, int64_t n, uint32_t *err) {
