@@ -212,6 +212,34 @@ static double kv_value(const orc_problem *p, const double tab[16][256], int is_v
     return ((const double *)(is_v ? p->v : p->k))[base * dim + d];
 }
 
+/* The decoded K or V cache, [P][page][Hkv][dim] doubles: kv_value of every
+ * element, computed once per call so that the attention loops read plain
+ * values (the same values, so the arithmetic is unchanged).  F64 caches are
+ * used in place (*owned = 0). */
+static const double *decode_cache(const orc_problem *p, const double tab[16][256], int is_v,
+                                  int *owned)
+{
+    if (p->kv_fmt == ORC_FMT_F64) {
+        *owned = 0;
+        return (const double *)(is_v ? p->v : p->k);
+    }
+    int dim = is_v ? p->d_v : p->d_qk;
+    int64_t rows = (int64_t)p->num_phys_pages * p->page_size * p->Hkv;
+    double *out = (double *)malloc(sizeof(double) * (size_t)(rows * dim));
+    if (!out)
+        abort();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int g = (int)(r % p->Hkv);
+        int off = (int)((r / p->Hkv) % p->page_size);
+        int phys = (int)(r / ((int64_t)p->Hkv * p->page_size));
+        for (int d = 0; d < dim; ++d)
+            out[r * dim + d] = kv_value(p, tab, is_v, phys, off, g, d);
+    }
+    *owned = 1;
+    return out;
+}
+
 /* A visible key of one (row, KV head): absolute token position, the slot
  * that selected it, its physical page and offset. */
 typedef struct {
@@ -272,11 +300,12 @@ static int gather_visible(const orc_problem *p, int r, int g, vis_key *keys, uin
     return n;
 }
 
-/* Softmax of the keys [lo, hi) of `keys` for query (r, h):
- * writes o[d_v] (normalised, times v_scale) and returns lse, or -inf with
- * o = 0 when the set is empty.  `s` is scratch for the logits. */
-static double softmax_pv(const orc_problem *p, const double tab[16][256], int r, int h, int g,
-                         const vis_key *keys, const int *sel, int nsel, double *s, double *o)
+/* Softmax of the selected keys of `keys` for query (r, h) whose decoded
+ * vector is q[d_qk]: writes o[d_v] (normalised, times v_scale) and returns
+ * lse, or -inf with o = 0 when the set is empty.  kd / vd are the decoded
+ * caches; `s` is scratch for the logits. */
+static double softmax_pv(const orc_problem *p, const double *kd, const double *vd, const double *q,
+                         int g, const vis_key *keys, const int *sel, int nsel, double *s, double *o)
 {
     for (int c = 0; c < p->d_v; ++c)
         o[c] = 0.0;
@@ -286,9 +315,10 @@ static double softmax_pv(const orc_problem *p, const double tab[16][256], int r,
     double m = -INFINITY;
     for (int i = 0; i < nsel; ++i) {
         const vis_key *kk = &keys[sel[i]];
+        const double *k = kd + (((int64_t)kk->phys * p->page_size + kk->off) * p->Hkv + g) * p->d_qk;
         double dot = 0.0;
         for (int d = 0; d < p->d_qk; ++d)
-            dot += q_value(p, r, h, d) * kv_value(p, tab, 0, kk->phys, kk->off, g, d);
+            dot += q[d] * k[d];
         s[i] = scale * dot;
         if (s[i] > m)
             m = s[i];
@@ -296,10 +326,11 @@ static double softmax_pv(const orc_problem *p, const double tab[16][256], int r,
     double l = 0.0;
     for (int i = 0; i < nsel; ++i) {
         const vis_key *kk = &keys[sel[i]];
+        const double *v = vd + (((int64_t)kk->phys * p->page_size + kk->off) * p->Hkv + g) * p->d_v;
         double e = exp(s[i] - m);
         l += e;
         for (int c = 0; c < p->d_v; ++c)
-            o[c] += e * p->v_scale * kv_value(p, tab, 1, kk->phys, kk->off, g, c);
+            o[c] += e * p->v_scale * v[c];
     }
     for (int c = 0; c < p->d_v; ++c)
         o[c] /= l;
@@ -323,6 +354,9 @@ uint32_t orc_prefill_rows(const orc_problem *p, int n_req, const int32_t *row_to
     static double tab[16][256];
     if (p->kv_fmt == ORC_FMT_NVFP4)
         build_dequant_table(tab);
+    int k_owned, v_owned;
+    const double *kd = decode_cache(p, tab, 0, &k_owned);
+    const double *vd = decode_cache(p, tab, 1, &v_owned);
     const int S = p->num_slots / p->slots_per_split;
     const int G = p->Hq / p->Hkv;
     const int max_keys = p->num_slots * p->unit_tokens;
@@ -336,6 +370,7 @@ uint32_t orc_prefill_rows(const orc_problem *p, int n_req, const int32_t *row_to
         double *po = (double *)malloc(sizeof(double) * (size_t)S * p->d_v);
         double *pl = (double *)malloc(sizeof(double) * (size_t)S);
         double *tmp_o = (double *)malloc(sizeof(double) * (size_t)p->d_v);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)p->d_qk);
 #pragma omp for schedule(dynamic, 1)
         for (int i = 0; i < n_req; ++i) {
             int r = row_tokens[i];
@@ -346,13 +381,15 @@ uint32_t orc_prefill_rows(const orc_problem *p, int n_req, const int32_t *row_to
                 for (int hl = 0; hl < G; ++hl) {
                     int h = g * G + hl;
                     int64_t row = (int64_t)i * p->Hq + h;
+                    for (int d = 0; d < p->d_qk; ++d)
+                        qrow[d] = q_value(p, r, h, d);
                     /* per split: keys whose slot falls in the split */
                     for (int sp = 0; sp < S; ++sp) {
                         int nsel = 0;
                         for (int k = 0; k < n; ++k)
                             if (keys[k].slot / p->slots_per_split == sp)
                                 sel[nsel++] = k;
-                        pl[sp] = softmax_pv(p, tab, r, h, g, keys, sel, nsel, s,
+                        pl[sp] = softmax_pv(p, kd, vd, qrow, g, keys, sel, nsel, s,
                                             po + (int64_t)sp * p->d_v);
                     }
                     if (part_o)
@@ -370,7 +407,7 @@ uint32_t orc_prefill_rows(const orc_problem *p, int n_req, const int32_t *row_to
                     if (out1 || lse1) {
                         for (int k = 0; k < n; ++k)
                             sel[k] = k;
-                        double l1 = softmax_pv(p, tab, r, h, g, keys, sel, n, s, tmp_o);
+                        double l1 = softmax_pv(p, kd, vd, qrow, g, keys, sel, n, s, tmp_o);
                         if (out1)
                             memcpy(out1 + row * p->d_v, tmp_o, sizeof(double) * p->d_v);
                         if (lse1)
@@ -385,7 +422,12 @@ uint32_t orc_prefill_rows(const orc_problem *p, int n_req, const int32_t *row_to
         free(po);
         free(pl);
         free(tmp_o);
+        free(qrow);
     }
+    if (k_owned)
+        free((void *)kd);
+    if (v_owned)
+        free((void *)vd);
     return err_all;
 }
 
