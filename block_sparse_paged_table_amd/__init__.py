@@ -14,6 +14,7 @@ Functions (same names as the C entry points):
   msa_combine(partial_o, partial_lse, num_splits, num_rows, head_dim_v, out,
               lse=None, ...strides..., stream=None)
   msa_nvfp4_dequant_e4m3(codes, scales, out, stream=None)
+  msa_nvfp4_dequant_f16(codes, scales, out, stream=None)
   msa_device_supported(device) -> bool
 """
 from __future__ import annotations
@@ -29,7 +30,8 @@ __all__ = [
     "MsaError", "PrefillDesc", "IndexDesc", "library", "library_path", "msa_combine_ex",
     "msa_index_scores", "msa_index_topk", "msa_prefill_index",
     "msa_prefill_workspace_bytes", "msa_prefill_plan", "msa_prefill_attend",
-    "msa_sparse_prefill", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_device_supported",
+    "msa_sparse_prefill", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_nvfp4_dequant_f16",
+    "msa_device_supported", "msa_required_lds_bytes", "msa_sparse_prefill_workspace_bytes",
     "msa_abi_version",
 ]
 
@@ -120,10 +122,13 @@ _SIGNATURES = [
     ("msa_combine_ex", ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64,
                                       _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     ("msa_nvfp4_dequant_e4m3", ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p]),
+    ("msa_nvfp4_dequant_f16", ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p]),
     ("msa_index_scores", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
     ("msa_index_topk", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
     ("msa_prefill_index", ctypes.c_int, [ctypes.POINTER(IndexDesc), _c_p]),
     ("msa_device_supported", ctypes.c_int, [ctypes.c_int]),
+    ("msa_required_lds_bytes", ctypes.c_size_t, []),
+    ("msa_sparse_prefill_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(PrefillDesc)]),
     ("msa_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("msa_last_error", ctypes.c_char_p, []),
     ("msa_abi_version", ctypes.c_int, []),
@@ -256,6 +261,20 @@ def msa_prefill_index(desc: IndexDesc, stream=None):
 def msa_nvfp4_dequant_e4m3(codes, scales, out, stream=None):
     _check(library().msa_nvfp4_dequant_e4m3(_ptr(codes), _ptr(scales), _ptr(out), codes.numel(),
                                             _stream(stream)))
+
+
+def msa_nvfp4_dequant_f16(codes, scales, out, stream=None):
+    _check(library().msa_nvfp4_dequant_f16(_ptr(codes), _ptr(scales), _ptr(out), codes.numel(),
+                                           _stream(stream)))
+
+
+def msa_sparse_prefill_workspace_bytes(desc: PrefillDesc) -> int:
+    """Workspace bytes, or 0 if the descriptor is rejected."""
+    return library().msa_sparse_prefill_workspace_bytes(ctypes.byref(desc))
+
+
+def msa_required_lds_bytes() -> int:
+    return library().msa_required_lds_bytes()
 
 
 def msa_device_supported(device: int = 0) -> bool:

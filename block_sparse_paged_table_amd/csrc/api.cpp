@@ -45,6 +45,7 @@ int esize(int dt) {
 }
 
 constexpr int kPageRouteRowsPerUnit = 1024;  // (token, head) rows per work unit
+constexpr int kMaxDevices = 64;               // devices the per-device caches cover
 
 // Route of a descriptor (page selections), or -1.
 int page_route(const msa_prefill_desc *d) {
@@ -418,6 +419,11 @@ msa_status msa_prefill_workspace_bytes(const msa_prefill_desc *d, size_t *bytes)
   return ok();
 }
 
+size_t msa_sparse_prefill_workspace_bytes(const msa_prefill_desc *d) {
+  size_t bytes = 0;
+  return msa_prefill_workspace_bytes(d, &bytes) == MSA_OK ? bytes : 0;
+}
+
 msa_status msa_prefill_plan(const msa_prefill_desc *d, void *ws, size_t ws_bytes, void *stream) {
   Resolved r;
   msa_status s = resolve(d, &r);
@@ -505,15 +511,33 @@ msa_status msa_nvfp4_dequant_e4m3(const uint8_t *codes, const uint8_t *scales, u
   return hip_status(launch_nvfp4_dequant(codes, scales, out, n, (hipStream_t)stream), "dequant launch");
 }
 
+msa_status msa_nvfp4_dequant_f16(const uint8_t *codes, const uint8_t *scales, uint16_t *out,
+                                 int64_t n, void *stream) {
+  if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (!codes || !scales || !out) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(out, 2)) return fail(MSA_ERR_INVALID_ARG, "out must be 2-byte aligned");
+  return hip_status(launch_nvfp4_dequant_f16(codes, scales, out, n, (hipStream_t)stream),
+                    "dequant launch");
+}
+
+size_t msa_required_lds_bytes(void) {
+  const size_t sizes[] = {page_plan_lds_bytes(), page_attend_lds_bytes(), grouped_plan_lds_bytes(),
+                          grouped_attend_lds_bytes(), index_lds_bytes()};
+  size_t m = 0;
+  for (size_t x : sizes) m = std::max(m, x);
+  return m;
+}
+
 int msa_device_supported(int device) {
-  static std::atomic<int> cache[64];  // 0 unknown, 1 yes, 2 no
-  if (device < 0 || device >= 64) return 0;
+  static std::atomic<int> cache[kMaxDevices];  // 0 unknown, 1 yes, 2 no
+  if (device < 0 || device >= kMaxDevices) return 0;
   int c = cache[device].load();
   if (c) return c == 1;
   hipDeviceProp_t prop;
   int yes = 0;
   if (hipGetDeviceProperties(&prop, device) == hipSuccess)
-    yes = strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.sharedMemPerBlock >= 65536;
+    yes = strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.sharedMemPerBlock >= msa_required_lds_bytes();
   cache[device].store(yes ? 1 : 2);
   return yes;
 }

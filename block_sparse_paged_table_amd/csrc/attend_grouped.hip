@@ -296,6 +296,10 @@ __global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
 
 }  // namespace
 
+size_t grouped_attend_lds_bytes() {
+  return (size_t)(2 * (GGeom<256>::STAGE > GGeom<128>::STAGE ? GGeom<256>::STAGE : GGeom<128>::STAGE));
+}
+
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;
   dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv, (unsigned)a.num_splits);

@@ -308,21 +308,12 @@ __device__ __forceinline__ void load_page_nvfp4(const PageArgs &a, int phys, int
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const uint32_t scale = (vsf[kk] >> (8 * b)) & 0xffu;
-      // FP16 magnitude table, split into its low and high bytes
-      uint32_t lo[2], hi[2];
-      nvfp4_f16_tables(nvfp4_mag_table(scale), lo, hi);
-      const uint32_t flip = (scale & 0x80u) ? 0x80008000u : 0u;
+      const Nvfp4F16Tab tab = nvfp4_f16_tab((vsf[kk] >> (8 * b)) & 0xffu);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // 4 codes -> two FP16 pairs
-        const uint32_t sp = spread_nibbles((vcw[kk][b * 2 + (q >> 1)] >> (16 * (q & 1))) & 0xffffu);
-        const uint32_t sel = sp & 0x07070707u, sg = sp & 0x08080808u;
-        const uint32_t L = __builtin_amdgcn_perm(lo[1], lo[0], sel);
-        const uint32_t H = __builtin_amdgcn_perm(hi[1], hi[0], sel);
-        const uint32_t p01 = __builtin_amdgcn_perm(H, L, 0x05010400u) | ((sg & 0x8u) << 12) | ((sg & 0x800u) << 20);
-        const uint32_t p23 = __builtin_amdgcn_perm(H, L, 0x07030602u) | ((sg & 0x80000u) >> 4) | ((sg & 0x8000000u) << 4);
-        hw[kk][b * 8 + q * 2] = p01 ^ flip;
-        hw[kk][b * 8 + q * 2 + 1] = p23 ^ flip;
+        const u32x2 w = nvfp4_lookup4_f16(vcw[kk][b * 2 + (q >> 1)] >> (16 * (q & 1)), tab);
+        hw[kk][b * 8 + q * 2] = w[0];
+        hw[kk][b * 8 + q * 2 + 1] = w[1];
       }
     }
   // V^T rows dv, dv+1 get the (key 2kp, key 2kp+1) pairs
@@ -707,6 +698,17 @@ hipError_t launch_route(const PageArgs &a, hipStream_t s) {
 
 }  // namespace
 
+size_t page_attend_lds_bytes() {
+  constexpr int sizes[] = {Geom<kRouteF32, 64>::LDS,   Geom<kRouteF32, 128>::LDS,
+                           Geom<kRouteBF16, 64>::LDS,  Geom<kRouteBF16, 128>::LDS,
+                           Geom<kRouteF16, 64>::LDS,   Geom<kRouteF16, 128>::LDS,
+                           Geom<kRouteQ8KV4, 128>::LDS, Geom<kRouteQ8KV8, 64>::LDS,
+                           Geom<kRouteQ8KV8, 128>::LDS};
+  int m = 0;
+  for (int x : sizes) m = x > m ? x : m;
+  return (size_t)m;
+}
+
 hipError_t launch_page_attend(const PageArgs &a, hipStream_t s) {
   switch (a.route) {
     case kRouteF32:
@@ -723,12 +725,19 @@ hipError_t launch_page_attend(const PageArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Standalone device dequantisation (same routine the attention uses).
+// Standalone device dequantisation (the routines the attention uses for K
+// and for V).  Element i sits at position i % 4 of its 4-code word, so
+// every position of the lookups is exercised.
 namespace {
 __global__ void nvfp4_dequant_kernel(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
                                      int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = (uint8_t)nvfp4_to_e4m3(codes[i] & 15u, scales[i]);
+  if (i < n) out[i] = (uint8_t)nvfp4_to_e4m3(codes[i] & 15u, scales[i], (int)(i & 3));
+}
+__global__ void nvfp4_dequant_f16_kernel(const uint8_t *codes, const uint8_t *scales, uint16_t *out,
+                                         int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint16_t)nvfp4_to_f16(codes[i] & 15u, scales[i], (int)(i & 3));
 }
 }  // namespace
 
@@ -736,6 +745,13 @@ hipError_t launch_nvfp4_dequant(const uint8_t *codes, const uint8_t *scales, uin
                                 int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   nvfp4_dequant_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(codes, scales, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_dequant_f16(const uint8_t *codes, const uint8_t *scales, uint16_t *out,
+                                    int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  nvfp4_dequant_f16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(codes, scales, out, n);
   return hipGetLastError();
 }
 

@@ -187,7 +187,9 @@ hipError_t launch_in(const void *po, int64_t po_split, int64_t po_row, const flo
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
                      int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
   if constexpr (IN != MSA_F32) {  // 8 columns per thread: one 16-byte load per split
-    if (dv % 8 == 0) {
+    // (only where every row of every split starts 16-byte aligned; rows
+    // padded to a multiple of 4 elements only take the 8-byte path below)
+    if (dv % 8 == 0 && (po_row | po_split) % 8 == 0) {
       if (S <= 4) return launch_cb<8, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
       if (S <= 8) return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
       return launch_cb<8, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);

@@ -99,9 +99,47 @@ __device__ __forceinline__ uint32_t nvfp4_lookup4(uint32_t codes, u32x2 tab, uin
   return (mags | ((sp & 0x08080808u) << 4)) ^ sign_flip;
 }
 
-// Single-element form (standalone dequantisation entry point; same tables).
-__device__ __forceinline__ uint32_t nvfp4_to_e4m3(uint32_t code, uint32_t scale) {
-  return nvfp4_lookup4(code & 15u, nvfp4_mag_table(scale), (scale & 0x80u) ? 0x80808080u : 0u) & 0xffu;
+// Single element at position pos (0..3) of a 4-code word (standalone
+// dequantisation entry point; same tables and lookup as the attention).
+__device__ __forceinline__ uint32_t nvfp4_to_e4m3(uint32_t code, uint32_t scale, int pos) {
+  const uint32_t b4 = nvfp4_lookup4((code & 15u) << (4 * pos), nvfp4_mag_table(scale),
+                                    (scale & 0x80u) ? 0x80808080u : 0u);
+  return (b4 >> (8 * pos)) & 0xffu;
+}
+
+// The V side of the same dequantisation, straight to the FP16 operand of the
+// PV product (every E4M3 value is an FP16 value, so this is exact): a block's
+// eight FP16 magnitudes as byte-permute tables of their low and high bytes,
+// and the sign flip of a negative scale.
+struct Nvfp4F16Tab {
+  uint32_t lo[2], hi[2], flip;
+};
+
+__device__ __forceinline__ Nvfp4F16Tab nvfp4_f16_tab(uint32_t scale) {
+  Nvfp4F16Tab t;
+  nvfp4_f16_tables(nvfp4_mag_table(scale), t.lo, t.hi);
+  t.flip = (scale & 0x80u) ? 0x80008000u : 0u;
+  return t;
+}
+
+// Four elements sharing one block scale (codes in the low 16 bits of
+// `codes`, element i in bits 4i..4i+3) as FP16: word 0 holds elements 0 (low
+// half) and 1, word 1 elements 2 and 3.  A code's sign bit becomes the FP16
+// sign (XOR the scale's), which also signs the zeros.
+__device__ __forceinline__ u32x2 nvfp4_lookup4_f16(uint32_t codes, const Nvfp4F16Tab &t) {
+  const uint32_t sp = spread_nibbles(codes & 0xffffu);
+  const uint32_t sel = sp & 0x07070707u, sg = sp & 0x08080808u;
+  const uint32_t L = __builtin_amdgcn_perm(t.lo[1], t.lo[0], sel);
+  const uint32_t H = __builtin_amdgcn_perm(t.hi[1], t.hi[0], sel);
+  const uint32_t p01 = __builtin_amdgcn_perm(H, L, 0x05010400u) | ((sg & 0x8u) << 12) | ((sg & 0x800u) << 20);
+  const uint32_t p23 = __builtin_amdgcn_perm(H, L, 0x07030602u) | ((sg & 0x80000u) >> 4) | ((sg & 0x8000000u) << 4);
+  return u32x2{p01 ^ t.flip, p23 ^ t.flip};
+}
+
+// Single element at position pos (0..3) as FP16 bits (standalone entry point).
+__device__ __forceinline__ uint32_t nvfp4_to_f16(uint32_t code, uint32_t scale, int pos) {
+  const u32x2 w = nvfp4_lookup4_f16((code & 15u) << (4 * pos), nvfp4_f16_tab(scale));
+  return (w[pos >> 1] >> (16 * (pos & 1))) & 0xffffu;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -375,6 +375,16 @@ __global__ void k_index_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
 
+// Static LDS of k_index_scores<D> (its __shared__ arrays).
+template <int D> constexpr size_t index_scores_lds() {
+  using Gm = IGeom<D>;
+  return 2 * (size_t)Gm::PAGE_BYTES + (size_t)Gm::ITQ * (IPC + 1) * 4 + 4 * (size_t)Gm::ITQ * 4 + 4 * 4;
+}
+
+size_t index_lds_bytes() {
+  return index_scores_lds<128>() > index_scores_lds<64>() ? index_scores_lds<128>() : index_scores_lds<64>();
+}
+
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t s) {
   if (a.err_flags) k_index_zero<<<1, 1, 0, s>>>(a.err_flags);
   if (a.total_q == 0) return hipGetLastError();

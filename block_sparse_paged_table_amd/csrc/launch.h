@@ -53,7 +53,16 @@ hipError_t launch_combine(const void *po, int32_t po_dtype, int64_t po_split, in
                           const float *pl, int64_t pl_split, int32_t S, int64_t rows, int32_t dv,
                           void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s);
 
+// Largest LDS (static + dynamic) one workgroup of each kernel family needs.
+size_t page_plan_lds_bytes();
+size_t page_attend_lds_bytes();
+size_t grouped_plan_lds_bytes();
+size_t grouped_attend_lds_bytes();
+size_t index_lds_bytes();
+
 hipError_t launch_nvfp4_dequant(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
                                 int64_t n, hipStream_t s);
+hipError_t launch_nvfp4_dequant_f16(const uint8_t *codes, const uint8_t *scales, uint16_t *out,
+                                    int64_t n, hipStream_t s);
 
 }  // namespace msa

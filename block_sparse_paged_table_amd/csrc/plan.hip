@@ -377,6 +377,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a) {
 
 }  // namespace
 
+size_t page_plan_lds_bytes() { return (size_t)kMaxLdsLists * 4; }  // plan_count's histogram
+
 hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
   const int64_t L = a.lay.num_lists;  // all slices

@@ -1,10 +1,14 @@
 // Planner of the grouped microblock route (1Cat-vLLM PR 387, section
-// "Purpose": a deterministic GPU planner maps the logical selections through
-// the paged cache, groups blocks by active-row category and validates
-// request, visibility, logical-page, tail and physical-page bounds; PR 1236,
-// section "Purpose": a group of eight rows holds at most 8 x 513
-// microblocks and the plan order depends only on category and logical
-// owner).
+// "Purpose"; 1Cat-vLLM PR 1236, section "Purpose").  It turns each group's
+// logical selections into the list of physical 4-token units the attention
+// kernel loads once for all rows of the group.  On the GPU and
+// deterministically, it drops any selection it cannot honour (a padding
+// row, a request id outside the batch, a unit past the request's table row
+// or its tail, a table entry outside the cache) and flags it, and it orders
+// the resulting units by which row tiles use them, so a tile with nothing in
+// a batch skips it.  The union of a group is bounded by its 8 rows times
+// their slots, and the order of the list is a function of the categories
+// and logical units alone, never of scheduling.
 //
 // One workgroup per (group of kGroupTokens consecutive query tokens, KV head):
 //   1. every (token, slot) selection becomes a 64-bit key
@@ -449,6 +453,14 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
 __global__ void gplan_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
+
+// Dynamic key array (sort size + one slot per thread) plus the static wave
+// counters, at the largest sort: 8 tokens x 512 slots.
+size_t grouped_plan_lds_bytes() {
+  size_t n = 1;
+  while (n < (size_t)kGroupTokens * 512 || n < (size_t)kGPlanThreadsFew) n <<= 1;
+  return (n + kGPlanThreadsFew) * 8 + 16 * (kGPlanThreadsFew / 64) * 4;
+}
 
 hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s) {
   gplan_zero<<<1, 1, 0, s>>>(a.err_flags);

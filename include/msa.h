@@ -179,9 +179,17 @@ typedef struct msa_prefill_desc {
     int32_t partial_dtype;
 } msa_prefill_desc;
 
-/* Workspace needed by msa_prefill_plan/_attend for this problem (bytes).
- * Depends only on host-side fields. */
+/* Workspace needed by msa_prefill_plan/_attend for this problem (bytes),
+ * so that a caller sizes it up front (MiniMax-AI/MSA PR 21, section "Place
+ * the partials by memory locality domain": the workspace object is sized
+ * once with a required-bytes query and may serve several layers run in order
+ * on one stream).  Depends only on host-side fields; nothing is launched.
+ * Returns the descriptor's validation status; *bytes is written on MSA_OK. */
 msa_status msa_prefill_workspace_bytes(const msa_prefill_desc *d, size_t *bytes);
+
+/* The same query in the one-value form: the workspace bytes, or 0 when the
+ * descriptor is rejected (msa_last_error() then says why). */
+size_t msa_sparse_prefill_workspace_bytes(const msa_prefill_desc *d);
 
 /* Step 1: build the work plan in `workspace` from the selections: the
  * inverted index of queries per (request, logical page, KV head) for page
@@ -299,9 +307,29 @@ msa_status msa_prefill_index(const msa_index_desc *d, void *stream);
 msa_status msa_nvfp4_dequant_e4m3(const uint8_t *codes, const uint8_t *scales, uint8_t *out,
                                   int64_t n, void *stream);
 
-/* 1 iff `device` is a gfx950 GPU with the LDS the kernels need, else 0.
- * The result is cached per device. */
+/* The V-side form of the same dequantisation: the attention's PV product
+ * takes the dequantised value as FP16, converted straight from the code and
+ * the scale through FP16 tables (section "Build the prefill for SM107": the
+ * product is exact in FP16, so the FP16 value equals the E4M3 rounding, and
+ * the same bits must come out).
+ * out[i] = FP16 bits of E4M3(code codes[i] & 15 x scale scales[i]); n
+ * elements, out 2-byte aligned.  Only the low nibble of codes[i] is read.
+ * Element i is looked up at position i % 4 of a 4-code word, as the kernel
+ * does for the four codes of a 16-bit group. */
+msa_status msa_nvfp4_dequant_f16(const uint8_t *codes, const uint8_t *scales, uint16_t *out,
+                                 int64_t n, void *stream);
+
+/* Per-device capability query (1Cat-vLLM PR 1236, section "Purpose": the
+ * build reports, per device and cached, whether it has a kernel image for
+ * the device and enough shared memory for its kernels).  1 iff `device` is a
+ * gfx950 GPU whose LDS per workgroup is at least msa_required_lds_bytes(),
+ * else 0 (also for a device index that does not exist).  The result is
+ * cached per device. */
 int msa_device_supported(int device);
+
+/* LDS per workgroup (bytes, static + dynamic) that the largest kernel of
+ * this build needs: the FP32 page-route attention at head_dim 128. */
+size_t msa_required_lds_bytes(void);
 
 const char *msa_status_str(msa_status s);
 

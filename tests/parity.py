@@ -8,9 +8,11 @@ Tolerances (written here, used by every GPU test):
   * BF16 / FP16 storage: relative L2 <= 1e-3 and max abs <= 2e-3 on FP32
     partials and on the FP32 combine; |d lse| <= 1e-4 (logits are exact
     products accumulated in FP32, |logit| < 20).
-  * E4M3 Q / NVFP4 KV: the oracle consumes the identical E4M3 operands;
-    relative L2 <= 5e-3 and max abs <= 5e-3 on partials and combine;
-    |d lse| <= 1e-4.
+  * E4M3 Q / NVFP4 or E4M3 KV: the oracle consumes the identical E4M3
+    operands; relative L2 <= 5e-3 and max abs <= 2e-3 on partials and
+    combine (the max-abs bound of the 16-bit inputs, applied to the FP8
+    path too; every row of the full 16K-token and chunked-batch layers
+    measures below 6e-4); |d lse| <= 1e-4.
   * 16-bit outputs of the combine are compared bit for bit with the
     round-to-nearest-even conversion of the GPU's own FP32 combine; end to
     end, ||gpu - ref|| <= ||round(ref) - ref|| + tol * ||ref||.
@@ -32,7 +34,7 @@ TOL = {
     "f32": dict(rel_l2=1e-5, max_abs=1e-5, lse=1e-5),
     "bf16": dict(rel_l2=1e-3, max_abs=2e-3, lse=1e-4),
     "f16": dict(rel_l2=1e-3, max_abs=2e-3, lse=1e-4),
-    "e4m3": dict(rel_l2=5e-3, max_abs=5e-3, lse=1e-4),
+    "e4m3": dict(rel_l2=5e-3, max_abs=2e-3, lse=1e-4),
 }
 
 

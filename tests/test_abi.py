@@ -223,3 +223,67 @@ def test_partial_layouts_describe_their_strides(layout, pad):
     assert dp.ws_bytes == DeviceProblem(p, device="cpu").ws_bytes
     with pytest.raises(ValueError):
         DeviceProblem(p, device="cpu", partial_layout="column")
+
+
+def _kernel_lds_of_library():
+    """{kernel symbol: group_segment_fixed_size} of every gfx950 kernel in
+    lib/libmsa.so, read from the code objects' metadata notes: the library's
+    .hip_fatbin section holds one offload bundle per source file."""
+    import shutil
+    import subprocess
+    import tempfile
+    tools = {t: shutil.which(t) or os.path.join("/opt/rocm/llvm/bin", t)
+             for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf")}
+    if not all(os.path.exists(p) for p in tools.values()):
+        pytest.skip("ROCm LLVM tools not found")
+    out = {}
+    with tempfile.TemporaryDirectory() as td:
+        fat = os.path.join(td, "fat.bin")
+        subprocess.check_call([tools["llvm-objcopy"], "-O", "binary", "--only-section=.hip_fatbin",
+                               msa.library_path, fat])
+        data = open(fat, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        starts, i = [], data.find(magic)
+        while i >= 0:
+            starts.append(i)
+            i = data.find(magic, i + 1)
+        assert starts, "no offload bundle in libmsa.so"
+        for k, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+            bundle, co = os.path.join(td, f"b{k}.bin"), os.path.join(td, f"b{k}.co")
+            open(bundle, "wb").write(data[a:b])
+            subprocess.check_call([tools["clang-offload-bundler"], "--type=o", "--unbundle",
+                                   "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                                   f"--input={bundle}", f"--output={co}"])
+            notes = subprocess.check_output([tools["llvm-readelf"], "--notes", co], text=True)
+            lds = None
+            for line in notes.splitlines():
+                line = line.strip()
+                if line.startswith(".group_segment_fixed_size:"):
+                    lds = int(line.split(":")[1])
+                elif line.startswith(".name:") and lds is not None:
+                    out[line.split(":", 1)[1].strip()] = lds
+                    lds = None
+    return out
+
+
+def test_required_lds_covers_every_compiled_kernel():
+    """msa_device_supported compares the device's LDS with
+    msa_required_lds_bytes(): it must cover the static LDS of every kernel
+    the build compiled, and equal the largest one (the FP32 page-route
+    attention at head_dim 128, 135,232 bytes; the planners' dynamic LDS is
+    smaller)."""
+    lds = _kernel_lds_of_library()
+    attend = {k: v for k, v in lds.items() if "k1_page_attend" in k}
+    assert len(attend) >= 9 and any("k_grouped_attend" in k for k in lds)
+    need = msa.msa_required_lds_bytes()
+    assert max(lds.values()) <= need
+    assert need == max(attend.values()) == 135232
+
+
+def test_workspace_query_one_value_form():
+    """msa_sparse_prefill_workspace_bytes: the workspace size, or 0 for a
+    rejected descriptor."""
+    d = _desc()
+    assert msa.msa_sparse_prefill_workspace_bytes(d) == msa.msa_prefill_workspace_bytes(d)
+    assert msa.msa_sparse_prefill_workspace_bytes(_desc(q=0)) == 0
+    assert msa.library().msa_last_error().decode()

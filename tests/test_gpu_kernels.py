@@ -18,20 +18,51 @@ def test_device_supported():
     assert msa.msa_device_supported(0)
 
 
-def test_nvfp4_dequant_exhaustive_bitexact():
-    """All 16 codes x 254 finite E4M3 scales, bit for bit (signed zeros,
-    saturation beyond 448 included) against the oracle's exact rounding."""
+def _all_finite_pairs():
+    """All 16 codes x 254 finite E4M3 scales, each pair repeated four times in
+    a row so that element i = 4 * pair + pos reaches the device lookups at
+    every position pos of a 4-code word."""
     scales = np.array([s for s in range(256) if s not in (0x7F, 0xFF)], np.uint8)
     cc, ss = np.meshgrid(np.arange(16, dtype=np.uint8), scales, indexing="ij")
-    ref = oracle.nvfp4_dequant(cc, ss).ravel()
-    codes = torch.from_numpy(cc.ravel().copy()).cuda()
-    sc = torch.from_numpy(ss.ravel().copy()).cuda()
+    return np.repeat(cc.ravel(), 4), np.repeat(ss.ravel(), 4)
+
+
+def test_nvfp4_dequant_exhaustive_bitexact():
+    """K side (E4M3 operand of the QK product): all 4064 finite (code, scale)
+    pairs at every lookup position, bit for bit (signed zeros, saturation
+    beyond 448 included) against the oracle's exact rounding."""
+    cc, ss = _all_finite_pairs()
+    ref = oracle.nvfp4_dequant(cc, ss)
+    codes = torch.from_numpy(cc.copy()).cuda()
+    sc = torch.from_numpy(ss.copy()).cuda()
     out = torch.empty_like(codes)
     msa.msa_nvfp4_dequant_e4m3(codes, sc, out)
     got = out.cpu().numpy()
     bad = np.nonzero(got != ref)[0]
-    assert len(bad) == 0, [(int(cc.ravel()[i]), int(ss.ravel()[i]), int(got[i]), int(ref[i]))
+    assert len(bad) == 0, [(int(cc[i]), int(ss[i]), i % 4, int(got[i]), int(ref[i]))
                            for i in bad[:10]]
+
+
+def test_nvfp4_dequant_f16_exhaustive_bitexact():
+    """V side (FP16 operand of the PV product, converted through the FP16
+    tables the attention kernel uses): all 4064 finite (code, scale) pairs at
+    every lookup position equal the oracle's E4M3 rounding widened to FP16,
+    bit for bit (signed zeros and saturation included)."""
+    cc, ss = _all_finite_pairs()
+    ref = oracle.e4m3_decode(oracle.nvfp4_dequant(cc, ss)).astype(np.float16).view(np.uint16)
+    codes = torch.from_numpy(cc.copy()).cuda()
+    sc = torch.from_numpy(ss.copy()).cuda()
+    out = torch.empty(codes.shape, dtype=torch.int16, device="cuda")
+    msa.msa_nvfp4_dequant_f16(codes, sc, out)
+    got = out.cpu().numpy().view(np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert len(bad) == 0, [(int(cc[i]), int(ss[i]), i % 4, hex(got[i]), hex(ref[i]))
+                           for i in bad[:10]]
+    # the K-side bytes decode to the same values
+    k8 = torch.empty_like(codes)
+    msa.msa_nvfp4_dequant_e4m3(codes, sc, k8)
+    kv = oracle.e4m3_decode(k8.cpu().numpy()).astype(np.float16).view(np.uint16)
+    assert np.array_equal(kv, got)
 
 
 @pytest.mark.parametrize("S,rows,dv", [(1, 333, 128), (3, 1000, 64), (16, 4099, 128),

@@ -91,6 +91,20 @@ def test_ordering_slices_bitwise_identical(Hq, Hkv, qd, kd):
         assert torch.equal(dp.out, ref.out) and torch.equal(dp.lse, ref.lse), st
 
 
+def _check_own_combine(p, po, pl, out, lse):
+    """The GPU combine of the GPU's own (widened) partials equals the oracle's
+    combine of the same values at FP32-combine accuracy."""
+    po = np.where(np.isfinite(pl)[..., None], po, 0.0)  # empty splits' rows are unspecified
+    own_out, own_lse = oracle.combine(po.reshape(-1, p.num_splits, p.d_v).transpose(1, 0, 2),
+                                      pl.reshape(-1, p.num_splits).T)
+    own_out = own_out.reshape(out.shape)
+    own_lse = own_lse.reshape(lse.shape)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(own_lse))
+    fin = np.isfinite(own_lse)
+    assert rel_l2(out, own_out) <= 1e-5 and np.abs(out - own_out).max() <= 1e-5
+    assert np.abs(lse[fin] - own_lse[fin]).max() <= 1e-5
+
+
 @pytest.mark.parametrize("qd,kd", [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "nvfp4"),
                                    ("e4m3", "e4m3")])
 @pytest.mark.parametrize("pd", ["f16", "bf16"])
@@ -104,15 +118,7 @@ def test_16bit_partials(qd, kd, pd):
     ref = oracle.prefill_rows(p)
     po, pl, out, lse = gpu_rows(dp, np.arange(p.total_q))
     check_partials(p, po, pl, ref, stored=pd)
-    po = np.where(np.isfinite(pl)[..., None], po, 0.0)  # empty splits' rows are unspecified
-    own_out, own_lse = oracle.combine(po.reshape(-1, p.num_splits, p.d_v).transpose(1, 0, 2),
-                                      pl.reshape(-1, p.num_splits).T)
-    own_out = own_out.reshape(out.shape)
-    own_lse = own_lse.reshape(lse.shape)
-    assert np.array_equal(np.isneginf(lse), np.isneginf(own_lse))
-    fin = np.isfinite(own_lse)
-    assert rel_l2(out, own_out) <= 1e-5 and np.abs(out - own_out).max() <= 1e-5
-    assert np.abs(lse[fin] - own_lse[fin]).max() <= 1e-5
+    _check_own_combine(p, po, pl, out, lse)
     # same kernel, FP32 partials: the 16-bit ones are their rounding
     dp32 = _run(p)
     live = dp32.partial_lse > -float("inf")
@@ -146,6 +152,11 @@ def test_strided_partial_buffer(qd, kd, d, pad, pd):
     check_partials(p, po, pl, ref, stored=pd)
     if pd == "f32":
         check_combined(p, out, lse, ref, "f32")
+    else:
+        # the combine reads the padded 16-bit rows through the same strides
+        # (rows 8-byte aligned only when the pad is not a multiple of 8):
+        # equal to the oracle's combine of the GPU's own widened partials
+        _check_own_combine(p, po, pl, out, lse)
 
 
 def test_shared_selection_stride_zero():
