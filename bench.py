@@ -62,12 +62,135 @@ def workload_stats(p):
     sel = (sm != 0) & (si >= 0) & (si < n_units) & seq_ok[:, None, None]
     ukey = (seq.astype(np.int64)[:, None, None] * p.Hkv + np.arange(p.Hkv)[None, :, None]) * n_units + si
     touched_rows = int(np.unique(ukey[sel]).size) * p.unit_tokens
+    # microblock route: every (8-token group, KV head, split) loads each
+    # distinct unit its rows selected in that split once (K and V rows)
+    gathered = 0
+    if p.unit_tokens != p.page_size:
+        kvrow = p.k_cache.element_size() * p.d_qk + p.v_cache.element_size() * p.d_v
+        T = si.shape[0]
+        grp = np.arange(T) // 8
+        split = np.arange(p.num_slots) // p.slots_per_split
+        gkey = ((grp[:, None, None] * p.Hkv + np.arange(p.Hkv)[None, :, None]) * p.num_splits
+                + split[None, None, :]) * (n_units + 1) + si
+        gathered = int(np.unique(gkey[sel & (vis > 0)]).size) * p.unit_tokens * kvrow
     return dict(n_visible=n_vis, nonempty=nonempty, touched_kv_rows=touched_rows,
+                gathered_kv_bytes=gathered,
                 flops=4.0 * p.d_qk * n_vis if p.d_qk == p.d_v else 2.0 * (p.d_qk + p.d_v) * n_vis)
 
 
 def tensor_bytes(t):
     return t.numel() * t.element_size()
+
+
+def _calib_lib():
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_paged_table_amd", "lib", "libmsa_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with `python -m block_sparse_paged_table_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+    lib.calib_read.argtypes = [P, I64, P, I32, I32, P]
+    lib.calib_write.argtypes = [P, I64, I32, U32, I32, P]
+    lib.calib_gather.argtypes = [P, I64, P, I64, P, I32, I32, P]
+    lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
+    lib.calib_chunk_bytes.restype = I64
+    return lib
+
+
+def measure_ceilings(reps=5, buf_gib=4, pool_sweep=False):
+    """Best rates this GPU reaches for the access patterns the kernels use
+    (probes of libmsa_calib.so, timed with HIP events on the launch stream,
+    median of `reps`): a streaming read and a streaming write of a 4 GiB
+    buffer, and a gather of 4 KiB microblock units (two 2 KiB runs 8 KiB
+    apart) from a 32 MiB K/V pool that stays in the Infinity Cache."""
+    import torch
+    lib = _calib_lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nbytes = buf_gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    grids = (256 * 8, 256 * 32)
+    sink = torch.zeros(max(grids) * 4, dtype=torch.int32, device="cuda")
+    grid = grids[0]
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            assert fn() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    out = {}
+    variants = {}
+    # writes: grid-stride / chunked non-temporal / chunked write-back
+    for g in grids:
+        for mode, name in ((0, "stride_nt"), (1, "chunk_nt"), (2, "chunk_wb")):
+            nb = nbytes if mode == 0 else lib.calib_chunk_bytes(nbytes, g, 4)
+            fn = lambda: lib.calib_write(buf.data_ptr(), nbytes, g, 7, mode, sp)
+            timed(fn)
+            variants[f"write_{name}_g{g}"] = round(nb / (timed(fn) * 1e-3) / 1e9, 1)
+    for g in grids:
+        for mode, name in ((0, "stride_nt"), (1, "chunk_nt")):
+            nb = nbytes if mode == 0 else lib.calib_chunk_bytes(nbytes, g, 8)
+            fn = lambda: lib.calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), g, mode, sp)
+            variants[f"read_{name}_g{g}"] = round(nb / (timed(fn) * 1e-3) / 1e9, 1)
+    out["hbm_write_gbs"] = max(v for k, v in variants.items() if k.startswith("write"))
+    out["hbm_read_gbs"] = max(v for k, v in variants.items() if k.startswith("read"))
+    out["variants"] = variants
+    del buf
+    rng = np.random.default_rng(9)
+    n_units = 1 << 20                           # 4 GiB of 4 KiB units
+
+    def gather(pool_mib, upis):
+        pool_blocks = pool_mib * 64             # 16 KiB blocks (16 K rows + 16 V rows)
+        pool = torch.randint(0, 255, (pool_blocks * 16384,), dtype=torch.uint8, device="cuda")
+        units = torch.from_numpy(rng.integers(0, pool_blocks * 4, n_units).astype(np.int32)).cuda()
+        res = {}
+        for upi in upis:
+            ms = timed(lambda: lib.calib_gather(pool.data_ptr(), pool.numel(), units.data_ptr(),
+                                                n_units, sink.data_ptr(), grid, upi, sp))
+            res[upi] = n_units * 4096 / (ms * 1e-3) / 1e9
+        return res
+
+    # the grouped route's K/V cache size class: 32 MiB (Infinity-Cache resident)
+    res = gather(32, (2, 4, 8))
+    for upi, gbs in res.items():
+        out[f"gather_4k_upi{upi}_gbs"] = round(gbs, 1)
+    out["gather_4k_gbs"] = round(max(res.values()), 1)
+    if pool_sweep:  # where the gather rate comes from: L2-, cache- or HBM-resident pools
+        out["gather_4k_by_pool_mib"] = {m: round(max(gather(m, (4, 8)).values()), 1)
+                                        for m in (2, 8, 32, 128, 1024)}
+    out["method"] = ("libmsa_calib.so probes, median of %d launches, best variant: 16-byte "
+                     "read / write of %d GiB (grid-stride or one chunk per workgroup, %s "
+                     "workgroups; writes non-temporal or write-back); 4 KiB-unit gather from a "
+                     "32 MiB pool, %d units, 2/4/8 units in flight per 256-thread workgroup, "
+                     "%d workgroups" % (reps, buf_gib, "/".join(map(str, grids)), n_units, grid))
+    return out
+
+
+def cpu_info():
+    """Host the CPU baseline ran on: model, logical CPUs and affinity mask."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = sorted(os.sched_getaffinity(0))
+    ranges, start = [], None
+    for i, c in enumerate(aff):
+        if start is None:
+            start = c
+        if i + 1 == len(aff) or aff[i + 1] != c + 1:
+            ranges.append(f"{start}-{c}" if c != start else f"{c}")
+            start = None
+    return dict(cpu_model=model, nproc=os.cpu_count(), affinity=",".join(ranges))
 
 
 KERNEL_SOURCES = {"k1_page_attend": "attend_page.hip", "combine_kernel": "combine.hip",
@@ -102,7 +225,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4,
                     help="rotated input sets (4: the queries and caches of the set in use "
                          "are not left in the 256 MB Infinity Cache by the previous steps)")
-    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens for the CPU oracle leg")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens for the CPU oracle leg (0: the whole layer)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kv-dtype", choices=["nvfp4", "e4m3"], default=None,
                     help="cache dtype variant of the Q8 workloads (e4m3: the Q8KV8 route)")
@@ -124,7 +248,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure the ceilings (HBM read, HBM write, cache-resident "
+                         "4 KiB gather) and print them as one JSON line")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the live ceiling measurement of the normal run")
     args = ap.parse_args()
+    if args.calibrate:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(measure_ceilings(pool_sweep=True)), flush=True)
+        return
     if args.copy_calibration:
         import torch
         n = args.copy_calibration * (1 << 20) // 4
@@ -200,13 +334,21 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    # per-kernel times: median of the K launches (the mean beside it)
+    t_plan = [e[0].elapsed_time(e[1]) for e in ev]
+    t_attn = [e[1].elapsed_time(e[2]) for e in ev]
+    t_comb = [e[2].elapsed_time(e[3]) for e in ev]
+    plan_ms, attn_ms, comb_ms = (float(np.median(t)) for t in (t_plan, t_attn, t_comb))
+    step_ms = float(np.median([e[0].elapsed_time(e[3]) for e in ev]))
+    means = {k: round(float(np.mean(t)), 4) for k, t in
+             (("plan", t_plan), ("attention", t_attn), ("combine", t_comb))}
     ms_per_step = wall * 1e3 / K
-    log(f"plan {plan_ms:.3f} ms, attention {attn_ms:.3f} ms, combine {comb_ms:.3f} ms, "
+    log(f"plan {plan_ms:.3f} ms, attention {attn_ms:.3f} ms, combine {comb_ms:.3f} ms (medians), "
         f"step(events) {step_ms:.3f} ms, step(wall) {ms_per_step:.3f} ms")
+    ceil = None
+    if not args.no_ceilings:
+        log("measuring the read / write / gather ceilings")
+        ceil = measure_ceilings()
 
     # algorithmic bytes per launch
     p, dp = p0, dps[0]
@@ -229,31 +371,51 @@ def main():
     comb_gbs = comb_bytes / (comb_ms * 1e-3) / 1e9
     mfma_dtype = {"e4m3": "fp8", "bf16": "bf16", "f16": "f16", "f32": "f32"}[p.q_dtype]
     dominant = "attention" if attn_ms >= comb_ms else "combine"
-    if dominant == "attention":
-        kname = "k1_page_attend" if p.unit_tokens == p.page_size else "k_grouped_attend"
-        roof = dict(kernel=kname, bound="hbm", achieved=round(attn_gbs, 1),
+    grouped = p.unit_tokens != p.page_size
+    # the grouped route gathers its units' K/V rows from a cache that stays on
+    # chip: its binding ceiling is the cache-resident gather, not HBM
+    gather_bytes = st["gathered_kv_bytes"]
+    gather_gbs = gather_bytes / (attn_ms * 1e-3) / 1e9
+    if dominant == "attention" and grouped:
+        peak = ceil["gather_4k_gbs"] if ceil else None
+        roof = dict(kernel="k_grouped_attend", bound="gather", achieved=round(gather_gbs, 1),
+                    peak=peak, unit="GB/s", frac=round(gather_gbs / peak, 4) if peak else None,
+                    peak_source="measured 4 KiB-unit gather ceiling (Infinity-Cache resident)",
+                    traffic=recorded_traffic("k_grouped_attend", wname), alg_bytes=gather_bytes,
+                    hbm_alg_bytes=attn_bytes,
+                    mfma_frac=round(attn_tflops / MFMA_PEAK_TFLOPS[mfma_dtype], 4))
+    elif dominant == "attention":
+        roof = dict(kernel="k1_page_attend", bound="hbm", achieved=round(attn_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4),
-                    traffic=recorded_traffic(kname, wname), alg_bytes=attn_bytes)
+                    traffic=recorded_traffic("k1_page_attend", wname), alg_bytes=attn_bytes)
+        if ceil:  # its bytes are almost all partial writes
+            roof.update(ceiling=ceil["hbm_write_gbs"], ceiling_kind="measured HBM write",
+                        frac_of_ceiling=round(attn_gbs / ceil["hbm_write_gbs"], 4))
     else:
         roof = dict(kernel="combine_kernel", bound="hbm", achieved=round(comb_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(comb_gbs / HBM_PEAK_GBS, 4),
                     traffic=recorded_traffic("combine_kernel", wname), alg_bytes=comb_bytes)
+        if ceil:
+            roof.update(ceiling=ceil["hbm_read_gbs"], ceiling_kind="measured HBM read",
+                        frac_of_ceiling=round(comb_gbs / ceil["hbm_read_gbs"], 4))
 
     cpu = None
     if not args.no_cpu:
         import oracle
-        n = min(args.cpu_sample, p.total_q)
+        n = min(args.cpu_sample, p.total_q) if args.cpu_sample > 0 else p.total_q
         toks = np.linspace(0, p.total_q - 1, n).astype(np.int32)
         keep = oracle.make_keep(p)
         sub = workload_stats_subset(p, toks)
         log(f"CPU oracle on {n} tokens")
         t = time.perf_counter()
-        oracle.prefill_rows(p, toks, want_partials=True, want_single_pass=False, keep=keep)
+        # the layer's result: every split's partial and their combine, per row
+        oracle.prefill_rows(p, toks, want_partials=False, want_single_pass=False, keep=keep)
         dt = time.perf_counter() - t
         cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        what = "the whole layer" if n == p.total_q else f"{n} of {p.total_q} query tokens (evenly spaced)"
         cpu = dict(value=round(sub / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
-                   sample=f"{n} of {p.total_q} query tokens (evenly spaced), all heads and slots; "
-                          f"{dt:.2f} s, FP64 C oracle, OpenMP")
+                   sample=f"{what}: all heads and slots, partials + combine; {dt:.2f} s, "
+                          f"FP64 C oracle, OpenMP", seconds=round(dt, 2), **cpu_info())
 
     res = {
         "metric": "sparse-prefill attn TFLOP/s over selected tokens + combine HBM GB/s, 1 GPU",
@@ -268,13 +430,17 @@ def main():
                    "Hq": p.Hq, "Hkv": p.Hkv, "head_dim": p.d_qk, "page_size": p.page_size,
                    "slots": p.num_slots, "splits": p.num_splits, "input_sets": len(dps)},
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4),
-                       "combine": round(comb_ms, 4)},
+                       "combine": round(comb_ms, 4), "stat": "median of the timed steps",
+                       "mean": means},
+        "ceilings": ceil,
         "attention": {"tflops": round(attn_tflops, 2),
                       "mfma_frac": round(attn_tflops / MFMA_PEAK_TFLOPS[mfma_dtype], 4),
                       "hbm_gbs": round(attn_gbs, 1), "alg_bytes": attn_bytes,
+                      "gathered_kv_gbs": round(gather_gbs, 1) if grouped else None,
                       "flops": st["flops"], "visible_keys": st["n_visible"]},
         "combine": {"gbs": round(comb_gbs, 1), "hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                     "alg_bytes": comb_bytes,
+                    "read_ceiling_frac": round(comb_gbs / ceil["hbm_read_gbs"], 4) if ceil else None,
                     "traffic": recorded_traffic("combine_kernel", wname)},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -17,6 +17,10 @@ OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "plan.hip", "attend_page.hip", "combine.hip", "plan_grouped.hip",
            "attend_grouped.hip", "index.hip"]
+# measurement probes of the benchmark (HBM read / write, cache-resident gather):
+# a library of their own, never loaded by the attention path
+CALIB_SOURCES = ["calibrate.hip"]
+CALIB_LIB = os.path.join(LIBDIR, "libmsa_calib.so")
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 # Packed-FP32 instructions are disabled: ordinary float code only.
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
@@ -37,19 +41,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

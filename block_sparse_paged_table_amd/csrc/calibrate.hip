@@ -1,0 +1,180 @@
+// Measurement probes for the roofline ceilings the benchmark reports
+// (libmsa_calib.so; not part of the attention library).  Each probe is the
+// simplest kernel that moves bytes in one pattern as fast as this GPU
+// allows, so a kernel's achieved rate can be read against what its own
+// access pattern can reach, not only against the 8 TB/s HBM peak:
+//
+//   calib_read    streaming read of a large buffer (16-byte non-temporal
+//                 loads, every workgroup striding through the array; a
+//                 checksum per workgroup keeps the loads alive)
+//   calib_write   streaming write of a large buffer (16-byte non-temporal
+//                 stores)
+//   calib_gather  gather of 4 KiB units -- two 2 KiB runs 8 KiB apart, the
+//                 K and V rows of one 4-token microblock in a K/V-interleaved
+//                 cache of 16-token blocks -- named by a list of unit ids
+//                 into a pool small enough to stay in the Infinity Cache:
+//                 the ceiling of the grouped microblock route's K/V gather.
+//                 Each workgroup keeps UPI units (UPI * 4 KiB) in flight.
+//
+// All indexing is bounded by the sizes passed in; every kernel exits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t wave_xor(uint32_t x) {
+  for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
+  return x;
+}
+
+__global__ void __launch_bounds__(kThreads) k_read(const u32x4 *__restrict__ src, int64_t n16,
+                                                   uint32_t *__restrict__ sink) {
+  constexpr int U = 8;  // independent loads in flight per thread
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  // one word per wave, so no load above can be dropped
+  acc = wave_xor(acc);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
+}
+
+// The same read with each workgroup owning one contiguous chunk of the
+// array, U consecutive 4 KiB blocks per iteration.
+__global__ void __launch_bounds__(kThreads) k_read_chunk(const u32x4 *__restrict__ src, int64_t n16,
+                                                         uint32_t *__restrict__ sink) {
+  constexpr int U = 8;
+  const int64_t per = (n16 / gridDim.x) / (U * kThreads) * (U * kThreads);  // whole iterations
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  uint32_t acc = 0;
+  for (int64_t i = lo + threadIdx.x; i < lo + per; i += U * kThreads) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  acc = wave_xor(acc);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
+}
+
+__global__ void __launch_bounds__(kThreads) k_write(u32x4 *__restrict__ dst, int64_t n16, uint32_t seed) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+    const uint32_t x = (uint32_t)i ^ seed;
+    __builtin_nontemporal_store(u32x4{x, x + 1u, x + 2u, x + 3u}, dst + i);
+  }
+}
+
+// Write with each workgroup owning one contiguous chunk, U 4 KiB blocks per
+// iteration; TEMPORAL selects ordinary (write-back) stores.
+template <bool TEMPORAL>
+__global__ void __launch_bounds__(kThreads) k_write_chunk(u32x4 *__restrict__ dst, int64_t n16, uint32_t seed) {
+  constexpr int U = 4;
+  const int64_t per = (n16 / gridDim.x) / (U * kThreads) * (U * kThreads);
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  for (int64_t i = lo + threadIdx.x; i < lo + per; i += U * kThreads) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t x = (uint32_t)(i + u * kThreads) ^ seed;
+      const u32x4 v = u32x4{x, x + 1u, x + 2u, x + 3u};
+      if constexpr (TEMPORAL) dst[i + u * kThreads] = v;
+      else __builtin_nontemporal_store(v, dst + i + u * kThreads);
+    }
+  }
+}
+
+// Unit u of the pool: 16-byte chunks [u4 + c] for c < 128 (K half) and
+// [u4 + 512 + c] for c < 128 (V half), u4 = (u / 4) * 1024 + (u % 4) * 128
+// in 16-byte units -- block b = u / 4 holds 16 K rows then 16 V rows of 512
+// bytes each, unit u % 4 covers 4 rows of each.  Thread t of a workgroup
+// loads chunk t % 128 of half t / 128 of each of its UPI units.
+template <int UPI>
+__global__ void __launch_bounds__(kThreads) k_gather(const u32x4 *__restrict__ pool, int64_t pool16,
+                                                     const int32_t *__restrict__ units, int64_t n_units,
+                                                     uint32_t *__restrict__ sink) {
+  const int half = threadIdx.x >> 7, c = threadIdx.x & 127;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * UPI; base < n_units; base += (int64_t)gridDim.x * UPI) {
+    int64_t off[UPI];
+#pragma unroll
+    for (int k = 0; k < UPI; ++k) {
+      const int64_t j = base + k;
+      const int64_t u = j < n_units ? units[j] : -1;
+      const int64_t o = (u / 4) * 1024 + (u % 4) * 128 + half * 512 + c;
+      off[k] = (u >= 0 && o < pool16) ? o : -1;
+    }
+    u32x4 v[UPI];
+#pragma unroll
+    for (int k = 0; k < UPI; ++k) v[k] = off[k] >= 0 ? pool[off[k]] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < UPI; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  acc = wave_xor(acc);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// sink: one uint32 per wave (4 * grid words).  mode 0: grid-stride
+// addressing; mode 1: one contiguous chunk per workgroup (the chunked form
+// covers the largest multiple of grid * 32 KiB; the caller counts those
+// bytes: calib_chunk_bytes).
+int calib_read(const void *src, int64_t bytes, uint32_t *sink, int grid, int mode, void *stream) {
+  if (!src || !sink || bytes < 16 || grid < 1 || mode < 0 || mode > 1) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (mode == 0) k_read<<<grid, kThreads, 0, s>>>((const u32x4 *)src, bytes / 16, sink);
+  else k_read_chunk<<<grid, kThreads, 0, s>>>((const u32x4 *)src, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// mode 0: grid-stride non-temporal; 1: chunked non-temporal; 2: chunked
+// write-back.
+int calib_write(void *dst, int64_t bytes, int grid, uint32_t seed, int mode, void *stream) {
+  if (!dst || bytes < 16 || grid < 1 || mode < 0 || mode > 2) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (mode == 0) k_write<<<grid, kThreads, 0, s>>>((u32x4 *)dst, bytes / 16, seed);
+  else if (mode == 1) k_write_chunk<false><<<grid, kThreads, 0, s>>>((u32x4 *)dst, bytes / 16, seed);
+  else k_write_chunk<true><<<grid, kThreads, 0, s>>>((u32x4 *)dst, bytes / 16, seed);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Bytes a chunked read (per 8 blocks of 4 KiB) or write (4 blocks) covers.
+int64_t calib_chunk_bytes(int64_t bytes, int grid, int blocks_per_iter) {
+  const int64_t it = (int64_t)blocks_per_iter * kThreads;
+  return ((bytes / 16) / grid) / it * it * grid * 16;
+}
+
+// units_per_iter: 1, 2, 4 or 8 units in flight per workgroup.
+int calib_gather(const void *pool, int64_t pool_bytes, const int32_t *units, int64_t n_units,
+                 uint32_t *sink, int grid, int units_per_iter, void *stream) {
+  if (!pool || !units || !sink || grid < 1 || n_units < 1 || pool_bytes < 16) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  const int64_t p16 = pool_bytes / 16;
+  switch (units_per_iter) {
+    case 1: k_gather<1><<<grid, kThreads, 0, s>>>((const u32x4 *)pool, p16, units, n_units, sink); break;
+    case 2: k_gather<2><<<grid, kThreads, 0, s>>>((const u32x4 *)pool, p16, units, n_units, sink); break;
+    case 4: k_gather<4><<<grid, kThreads, 0, s>>>((const u32x4 *)pool, p16, units, n_units, sink); break;
+    case 8: k_gather<8><<<grid, kThreads, 0, s>>>((const u32x4 *)pool, p16, units, n_units, sink); break;
+    default: return 1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"
