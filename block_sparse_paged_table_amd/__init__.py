@@ -11,6 +11,7 @@ Functions (same names as the C entry points):
   msa_prefill_plan(desc, workspace, stream=None)
   msa_prefill_attend(desc, workspace, stream=None)
   msa_sparse_prefill(desc, workspace, stream=None)
+  msa_sparse_prefill_noalloc(desc, stream=None)
   msa_combine(partial_o, partial_lse, num_splits, num_rows, head_dim_v, out,
               lse=None, ...strides..., stream=None)
   msa_nvfp4_dequant_e4m3(codes, scales, out, stream=None)
@@ -30,7 +31,7 @@ __all__ = [
     "MsaError", "PrefillDesc", "IndexDesc", "library", "library_path", "msa_combine_ex",
     "msa_index_scores", "msa_index_topk", "msa_prefill_index",
     "msa_prefill_workspace_bytes", "msa_prefill_plan", "msa_prefill_attend",
-    "msa_sparse_prefill", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_nvfp4_dequant_f16",
+    "msa_sparse_prefill", "msa_sparse_prefill_noalloc", "msa_noalloc_scratch_bytes", "msa_combine", "msa_nvfp4_dequant_e4m3", "msa_nvfp4_dequant_f16",
     "msa_device_supported", "msa_required_lds_bytes", "msa_sparse_prefill_workspace_bytes",
     "msa_abi_version",
 ]
@@ -117,6 +118,8 @@ _SIGNATURES = [
     ("msa_prefill_plan", ctypes.c_int, [ctypes.POINTER(PrefillDesc), _c_p, ctypes.c_size_t, _c_p]),
     ("msa_prefill_attend", ctypes.c_int, [ctypes.POINTER(PrefillDesc), _c_p, ctypes.c_size_t, _c_p]),
     ("msa_sparse_prefill", ctypes.c_int, [ctypes.POINTER(PrefillDesc), _c_p, ctypes.c_size_t, _c_p]),
+    ("msa_sparse_prefill_noalloc", ctypes.c_int, [ctypes.POINTER(PrefillDesc), _c_p]),
+    ("msa_noalloc_scratch_bytes", ctypes.c_size_t, []),
     ("msa_combine", ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i32,
                                    _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     ("msa_combine_ex", ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_i64,
@@ -202,6 +205,16 @@ def msa_prefill_attend(desc: PrefillDesc, workspace, stream=None):
 def msa_sparse_prefill(desc: PrefillDesc, workspace, stream=None):
     p, n = _ws(workspace)
     _check(library().msa_sparse_prefill(ctypes.byref(desc), p, n, _stream(stream)))
+
+
+def msa_sparse_prefill_noalloc(desc: PrefillDesc, stream=None):
+    """msa_sparse_prefill on the library's fixed per-device scratch (no
+    workspace argument, nothing allocated); calls on one GPU must not overlap."""
+    _check(library().msa_sparse_prefill_noalloc(ctypes.byref(desc), _stream(stream)))
+
+
+def msa_noalloc_scratch_bytes() -> int:
+    return library().msa_noalloc_scratch_bytes()
 
 
 def _combine_args(partial_o, partial_lse, out, po_split_stride, po_row_stride, pl_split_stride,

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "grouped.h"
 #include "launch.h"
@@ -406,6 +407,44 @@ msa_status resolve_index(const msa_index_desc *d, bool need_topk, IndexArgs *r) 
   return MSA_OK;
 }
 
+// ---- fixed device scratch of msa_sparse_prefill_noalloc
+//
+// The no-allocation entry point's workspace: one file-scope device array,
+// of which every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+
+msa_status scratch_of_current_device(void **addr);
+
+}  // namespace
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+msa_status scratch_of_current_device(void **addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +486,32 @@ msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *ws, size_t ws_byt
   if (s != MSA_OK) return s;
   return msa_prefill_attend(d, ws, ws_bytes, stream);
 }
+
+msa_status msa_sparse_prefill_noalloc(const msa_prefill_desc *d, void *stream) {
+  Resolved r;
+  msa_status s = resolve(d, &r);
+  if (s != MSA_OK) return s;
+  const size_t need = r.ws_bytes();
+  if (need > kNoAllocScratchBytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "problem needs %zu bytes of workspace, above the fixed %zu-byte scratch of the "
+                "no-allocation entry point (use msa_sparse_prefill with a caller workspace)",
+                need, kNoAllocScratchBytes);
+  void *ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != MSA_OK) return s;
+  if ((s = bind_workspace(&r, d, ws, kNoAllocScratchBytes)) != MSA_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  if (r.grouped) {
+    hipError_t e = launch_grouped_plan(r.ga, st);
+    if (e == hipSuccess) e = launch_grouped_attend(r.ga, st);
+    return hip_status(e, "prefill launch");
+  }
+  hipError_t e = launch_page_plan(r.pa, st);
+  if (e == hipSuccess) e = launch_page_attend(r.pa, st);
+  return hip_status(e, "prefill launch");
+}
+
+size_t msa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 msa_status msa_combine_ex(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
                           const float *pl, int64_t pl_split, int32_t num_splits, int64_t num_rows,

@@ -10,7 +10,7 @@ import torch
 from . import (MSA_BF16, MSA_E4M3, MSA_F16, MSA_F32, MSA_NVFP4, IndexDesc, PrefillDesc,
                msa_combine_ex, msa_index_scores, msa_index_topk, msa_prefill_index,
                msa_prefill_attend, msa_prefill_plan, msa_prefill_workspace_bytes,
-               msa_sparse_prefill)
+               msa_sparse_prefill, msa_sparse_prefill_noalloc)
 from .synth import Problem
 
 DTYPE_CODE = {"f32": MSA_F32, "bf16": MSA_BF16, "f16": MSA_F16, "e4m3": MSA_E4M3,
@@ -125,6 +125,9 @@ class DeviceProblem:
 
     def prefill(self, stream=None):
         msa_sparse_prefill(self.desc, self.workspace, stream)
+
+    def prefill_noalloc(self, stream=None):
+        msa_sparse_prefill_noalloc(self.desc, stream)
 
     def combine(self, stream=None, lse: bool = True):
         p = self.p

@@ -211,6 +211,30 @@ msa_status msa_sparse_prefill(const msa_prefill_desc *d, void *workspace, size_t
                               void *stream);
 
 /*
+ * msa_sparse_prefill without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The plan lives in a fixed scratch
+ * array of msa_noalloc_scratch_bytes() bytes (32 MiB) inside the library:
+ * every GPU holds its own copy from the first call on that device until the
+ * process ends, and its address is resolved once per device on that first
+ * call.  Nothing is allocated per call and the results are the same as
+ * msa_sparse_prefill's.
+ *   - A problem whose workspace (msa_prefill_workspace_bytes) exceeds the
+ *     scratch returns MSA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued
+ *     (every page-selection workload up to ~4x a 16K-token, 32-head layer
+ *     fits; microblock chunks up to 2048 tokens at 512 slots).
+ *   - The scratch keeps the last call's contents; the plan step clears what
+ *     it needs (counters, error word) with kernels of its own.
+ *   - All calls on one GPU share its scratch: calls that overlap in time on
+ *     one GPU (different streams, or threads) race and give wrong results.
+ *     Serialise them, or use msa_sparse_prefill with separate workspaces.
+ */
+msa_status msa_sparse_prefill_noalloc(const msa_prefill_desc *d, void *stream);
+
+/* Size of the fixed scratch of msa_sparse_prefill_noalloc, in bytes. */
+size_t msa_noalloc_scratch_bytes(void);
+
+/*
  * LSE combine over a flat list of rows (MiniMax-AI/MSA PR 21, section
  * "Combine"): for each row, M = max_s lse_s; if M = -inf the output row is
  * +0 and lse = -inf; else w_s = exp(lse_s - M),

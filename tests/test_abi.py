@@ -287,3 +287,17 @@ def test_workspace_query_one_value_form():
     assert msa.msa_sparse_prefill_workspace_bytes(d) == msa.msa_prefill_workspace_bytes(d)
     assert msa.msa_sparse_prefill_workspace_bytes(_desc(q=0)) == 0
     assert msa.library().msa_last_error().decode()
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_before_launch():
+    """msa_sparse_prefill_noalloc checks the workspace the descriptor needs
+    against its fixed scratch on the host, before touching the device."""
+    lib = msa.library()
+    assert msa.msa_noalloc_scratch_bytes() == 32 << 20
+    big = _desc(total_q=8192, num_slots=512, sel_stride_tok=512, sel_stride_head=512,
+                **{k: v for k, v in _MICROBLOCK.items() if k not in ("total_q", "num_slots",
+                                                                     "sel_stride_tok", "sel_stride_head")})
+    assert msa.msa_prefill_workspace_bytes(big) > msa.msa_noalloc_scratch_bytes()
+    assert lib.msa_sparse_prefill_noalloc(ctypes.byref(big), None) == 3  # WORKSPACE_TOO_SMALL
+    assert b"scratch" in lib.msa_last_error()
+    assert lib.msa_sparse_prefill_noalloc(ctypes.byref(_desc(q=0)), None) == 1
