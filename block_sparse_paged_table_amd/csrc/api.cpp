@@ -73,6 +73,8 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   if (G > 8) return fail(MSA_ERR_UNSUPPORTED, "microblock route: at most 8 query heads per KV head");
   if (d->num_seqs >= (1 << 16) || (int64_t)d->max_pages * d->page_size / 4 >= (1ll << 24))
     return fail(MSA_ERR_UNSUPPORTED, "microblock route: too many requests or units");
+  if (d->page_size > 128 || d->num_phys_pages >= (1 << 27))
+    return fail(MSA_ERR_UNSUPPORTED, "microblock route: page_size <= 128 and fewer than 2^27 pages");
   if (!aligned(d->q, 16) || (d->q_stride_tok * 2) % 16 || (d->q_stride_head * 2) % 16 ||
       d->q_stride_head < 0 || d->q_stride_tok < 0)
     return fail(MSA_ERR_INVALID_ARG, "q must be 16-byte aligned with 16-byte aligned strides");

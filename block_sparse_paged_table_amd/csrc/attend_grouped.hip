@@ -1,315 +1,414 @@
 // Attention step of the grouped microblock route (1Cat-vLLM PR 387, section
 // "Purpose": eight adjacent query rows share one load of their overlapping
-// sparse K/V blocks while each row keeps its exact 4-bit mask; inactive row
-// tiles are skipped), written for gfx950.
+// sparse K/V blocks while each row keeps its exact 4-bit mask), written for
+// gfx950.
 //
 // One workgroup per (group of 8 query tokens, KV head, split).  The group's
 // G query heads per token make 8*G (token, head) rows, cut into 16-row
-// tiles; wave w owns tile w.  The union of the group's microblocks (built by
-// the planner, ordered by category) streams through LDS in batches of 8
-// units = 32 keys, double-buffered: the next batch's K/V is in flight in
-// registers while the current one is computed, and the unit offsets of the
-// batch after it are read meanwhile, so each batch costs one round trip to
-// memory.  Per batch and active tile:
+// tiles; wave w owns tile w.  Consecutive groups run on one XCD, and the
+// planner lists each split's units in ascending order, so the groups an XCD
+// runs together walk the K/V cache in step and mostly hit its L2.
 //
-//   S^T = K . Q^T     f16 MFMA 16x16x32, FP32 accumulate (Q held in registers)
-//   mask              key i of unit b is visible to the row of token tau iff
-//                     bit 4*tau + i of the unit's mask word is set (the planner
-//                     already folded the causal and tail rules into it)
-//   online softmax    running max / sums per row, rescaling O when the max
-//                     grows
-//   O^T += V^T . P^T  f16 MFMA, P in FP16, V^T built in LDS at load time
+// The workgroup first copies its split's unit list (8 bytes per unit: page,
+// unit in the page, mask) into LDS.  The units then stream through an LDS
+// ring of NST stages of 16 keys (4 units) each, loaded straight from the
+// cache into LDS (global_load_lds: no register staging, no LDS stores): wave
+// w loads unit w of a stage, its K rows then its V rows.  Loads run NST - 1
+// stages ahead of the stage being computed, and one barrier per stage both
+// publishes a landed stage and frees the slot the next loads reuse.  Inside
+// the loop the only memory accesses are these counted loads and LDS
+// traffic: a scalar or vector load there would make every later wait also
+// wait for the loads in flight.  K rows are stored as they are in the cache with a per-row XOR
+// swizzle of their 16-byte chunks (the 16 rows of one MFMA read fall in 16
+// different bank groups); V rows likewise, read back transposed.  Per stage
+// and active tile:
 //
-// A tile none of whose rows selected any unit of the batch skips it (the
-// wave-uniform test uses the units' active-tile bits).  Each split (the
-// units whose first slot for a row lies in that split's slot range) is an
-// independent softmax: partial_o = O / l * v_scale and lse = m + ln l (or
-// -inf with zeros for a row that sees nothing in the split).
+//   S^T = K . Q^T      f16 MFMA 16x16x32, FP32 accumulate (K rows from LDS,
+//                      Q rows held in registers)
+//   mask               key i of unit b is visible to the row of token tau iff
+//                      bit 4*tau + i of the unit's mask word is set (the
+//                      planner folded the causal and tail rules into it)
+//   online softmax     running max / sums per row, rescaling O when the max
+//                      grows
+//   O^T += V^T . P^T   f16 MFMA 16x16x16: the V^T operand comes from the
+//                      untransposed V rows through the gfx950 transposing LDS
+//                      read (ds_read_b64_tr_b16), and the S^T accumulator of
+//                      a lane already holds its P^T operand (keys 4q..4q+3 of
+//                      its row)
+//
+// A tile none of whose rows selected any unit of a stage skips it.  Each
+// split is an independent softmax: partial_o = O / l * v_scale and lse =
+// m + ln l (or -inf with zeros for a row that sees nothing in the split).
+#include <type_traits>
+
 #include "grouped.h"
 
 namespace msa {
 namespace {
 
-constexpr int GT = 256;  // threads per workgroup
-constexpr int BK = 32;   // keys per batch
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int GT = 256;             // threads per workgroup
+constexpr int SK = 16;              // keys per stage
+constexpr int UPS = SK / 4;         // units per stage = waves per workgroup
+static_assert(UPS * kWave == GT, "one unit per wave and stage");
+
+typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kListCap = kGroupTokens * 512;  // units a group's split may hold
 
 template <int D> struct GGeom {
-  static constexpr int RB = D * 2;            // K row bytes (FP16)
-  static constexpr int CPR = RB / 16;         // 16-byte chunks per K row
-  static constexpr int LANE_CH = CPR / 4;     // chunks of a Q/K row one lane holds
-  static constexpr int K_BYTES = BK * RB;
-  static constexpr int V_BYTES = D * BK * 2;  // V^T: [D][32 keys] FP16
-  static constexpr int STAGE = K_BYTES + V_BYTES + 2 * kGUnitsPerBatch * 4;
-  static constexpr int KLD = BK * CPR / GT;   // K chunks per thread per batch
-  static constexpr int VDB = D / 16;          // dims per thread in the V load
-  static constexpr int VLD = VDB * 2 / 16;    // 16-byte chunks per key per thread
-  static_assert(KLD >= 1 && VLD >= 1, "head_dim 128 or 256");
+  static constexpr int RB = D * 2;                  // K / V row bytes (FP16)
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int LANE_CH = CPR / 4;           // chunks of a Q/K row one lane holds
+  static constexpr int K_BYTES = SK * RB;           // one stage's K rows
+  static constexpr int STAGE = 2 * K_BYTES;         // K rows, then V rows
+  static constexpr int NST = D == 256 ? 3 : 4;      // ring stages
+  static constexpr int RING = NST * STAGE;
+  static constexpr int LDS = RING + kListCap * 8;   // ring + the split's unit list
+  static constexpr int ROWS_PER_LOAD = 1024 / RB;   // rows one 1 KiB wave load covers
+  static constexpr int LPP = 4 / ROWS_PER_LOAD;     // wave loads per unit and part (K or V)
+  static constexpr int LOADS = 2 * LPP;             // wave loads per stage
+  static constexpr int MT = D / 16;
+  static_assert(ROWS_PER_LOAD * RB == 1024 && LPP >= 1, "head_dim 128 or 256");
+  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
 };
 
-// Key (0..31 in the batch) carried by A-operand row m of key tile t (0, 1):
-// the two tiles interleave so a lane's 8 S^T registers are 8 consecutive keys.
-__device__ __forceinline__ int gkey_of(int t, int m) { return (m >> 2) * 8 + t * 4 + (m & 3); }
-__device__ __forceinline__ int grow_of_key(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
-template <int D> __device__ __forceinline__ int gk_off(int key, int c) {
-  return key * GGeom<D>::RB + ((c ^ grow_of_key(key)) << 4);
+// Byte offset of 16-byte chunk c of K row r (r < 16) / V row r in a stage.
+template <int D> __device__ __forceinline__ int gk_off(int r, int c) {
+  return r * GGeom<D>::RB + ((c ^ (r & 15)) << 4);
 }
-// V^T row dv: the batch's 32 keys, 4 chunks of 8 keys, XOR-swizzled.
-__device__ __forceinline__ int gvt_off(int dv, int c) { return dv * 64 + ((c ^ ((dv >> 2) & 3)) << 4); }
+template <int D> __device__ __forceinline__ int gv_off(int r, int c) {
+  return GGeom<D>::K_BYTES + r * GGeom<D>::RB + ((c ^ ((r & 7) << 1)) << 4);
+}
 
-template <typename T> __device__ __forceinline__ T gld(const void *p) { return *(const T *)p; }
+// s_waitcnt with vmcnt(n) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
-template <int D> struct BatchRegs {
-  u32x4 k[GGeom<D>::KLD];
-  u32x4 v[2][GGeom<D>::VLD];
-  uint32_t mask, tiles;
+// One 16-byte load per lane straight into LDS (global_load_lds_dwordx4):
+// lane i reads base + voff (base a wave-uniform 64-bit address, voff this
+// lane's 32-bit offset) and writes LDS bytes [lds + 16 i, lds + 16 i + 16);
+// M0 holds the LDS address, with the one wait state its write needs before
+// the load.  It is issued from asm so that the compiler, which cannot tell
+// which LDS bytes such a load writes, adds no wait for it before every later
+// LDS read: the kernel counts these loads itself (vmcnt) and publishes a
+// stage with a barrier.  No register is written: the data goes to LDS.
+__device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(lds), "v"(voff), "s"(base)
+                   : "memory");
+}
+
+// Workgroup barrier that waits for nothing by itself (the waits are explicit)
+// and that the compiler may not move memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Per-lane constants of the stage loop, computed once.
+template <int D> struct LaneOffsets {
+  uint32_t k[GGeom<D>::LANE_CH];  // K fragment c of row n (QK operand), from the slot
+  uint32_t v[8];                  // V^T fragment of dims tile mt (mt & 7; +256 B for mt >= 8)
+  uint32_t dk[GGeom<D>::LPP];     // DMA source offsets in the unit, K rows
+  uint32_t dv[GGeom<D>::LPP];     //   and V rows
 };
 
-// Byte offset (within the K / V caches) of unit u of the group's list, or -1
-// past the end of the list.
-__device__ __forceinline__ int64_t unit_off(const uint4 *list, int count, int u) {
-  if (u >= count) return -1;
-  const uint2 e = *(const uint2 *)&list[u];
-  return (int64_t)((uint64_t)e.x | ((uint64_t)e.y << 32));
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(const GroupArgs &a, int w) {
+  using Gm = GGeom<D>;
+  LaneOffsets<D> L;
+  const int lane = threadIdx.x & 63, n = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < Gm::LANE_CH; ++c) L.k[c] = gk_off<D>(n, gq * Gm::LANE_CH + c);
+  // transposed V read: lane (gq, r, c) addresses row 4 gq + r at dims
+  // 16 mt + 4c .. +3, i.e. chunk 2 mt + c / 2, half c % 2; with the row's XOR
+  // swizzle 2 t (t = row & 7), chunk (2 mt + c/2) ^ 2t = 2 (mt ^ t) + c/2
+  const int vr = gq * 4 + ((lane >> 2) & 3), vc = lane & 3;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    L.v[j] = Gm::K_BYTES + vr * Gm::RB + ((((j ^ (vr & 7)) << 1) + (vc >> 1)) << 4) + (vc & 1) * 8;
+#pragma unroll
+  for (int h = 0; h < Gm::LPP; ++h) {
+    const int r = w * 4 + h * Gm::ROWS_PER_LOAD + lane / Gm::CPR, pos = lane % Gm::CPR;
+    L.dk[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ (r & 15)) << 4);
+    L.dv[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ ((r & 7) << 1)) << 4);
+  }
+  return L;
 }
 
-// Unit offsets (and the batch's mask / active-tile words) of this thread's
-// chunks of batch beta.  They are fetched one batch ahead of the K / V loads
-// that use them: a wait between an offset and its data load would also wait
-// for every data load issued before it, one round trip each.
-template <int D> struct BatchOffs {
-  int64_t k[GGeom<D>::KLD];
-  int64_t v;
-  uint32_t mask, tiles;
-};
+// Issue this wave's part of one stage: the K and V rows of the unit at byte
+// offset `uoff` of the caches, straight into the stage's LDS slot.  A unit
+// past the end of the run is zero-filled instead (its mask is 0, so it adds
+// nothing; zeros keep the masked products finite).
 template <int D>
-__device__ __forceinline__ void fetch_offs(const uint4 *list, int count, int beta, BatchOffs<D> &o) {
+__device__ __forceinline__ void issue_stage(const GroupArgs &a, uint8_t *slot, int w, int64_t uoff, bool real,
+                                            const LaneOffsets<D> &L) {
   using Gm = GGeom<D>;
-  const int tid = threadIdx.x;
-  const int u0 = beta * kGUnitsPerBatch;
+  const int lane = threadIdx.x & 63;
+  if (!real) {
 #pragma unroll
-  for (int it = 0; it < Gm::KLD; ++it) {
-    const int key = (it * GT + tid) / Gm::CPR;
-    o.k[it] = unit_off(list, count, u0 + (key >> 2));
+    for (int h = 0; h < Gm::LPP; ++h) {
+      const int r0 = w * 4 + h * Gm::ROWS_PER_LOAD;
+      *(u32x4 *)(slot + r0 * Gm::RB + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4 *)(slot + Gm::K_BYTES + r0 * Gm::RB + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
   }
-  o.v = unit_off(list, count, u0 + ((tid & 15) >> 1));
-  o.mask = o.tiles = 0u;
-  if (tid < kGUnitsPerBatch && u0 + tid < count) {
-    const uint2 e = *(const uint2 *)((const uint32_t *)&list[u0 + tid] + 2);
-    o.mask = e.x;
-    o.tiles = e.y;
-  }
+  const uint8_t *kb = a.k_cache + uoff;
+  const uint8_t *vb = a.v_cache + uoff;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t *)slot);
+#pragma unroll
+  for (int h = 0; h < Gm::LPP; ++h)
+    lds_dma16(kb, L.dk[h], lds + (w * 4 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
+#pragma unroll
+  for (int h = 0; h < Gm::LPP; ++h)
+    lds_dma16(vb, L.dv[h], lds + Gm::K_BYTES + (w * 4 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
 }
 
-// The K and V chunks of this thread for the batch whose offsets are `o`.
-template <int D>
-__device__ __forceinline__ void load_batch(const GroupArgs &a, const BatchOffs<D> &o, BatchRegs<D> &r) {
-  using Gm = GGeom<D>;
-  const int tid = threadIdx.x;
-  const int kp = tid & 15, db = tid >> 4;  // V: key pair, block of D/16 dims
-#pragma unroll
-  for (int it = 0; it < Gm::KLD; ++it) {
-    const int q = it * GT + tid, key = q / Gm::CPR, c = q % Gm::CPR;
-    r.k[it] = o.k[it] >= 0 ? gld<u32x4>(a.k_cache + o.k[it] + (key & 3) * a.kv_stride_tok + c * 16)
-                           : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int c = 0; c < Gm::VLD; ++c)
-      r.v[kk][c] = o.v >= 0 ? gld<u32x4>(a.v_cache + o.v + ((2 * kp + kk) & 3) * a.kv_stride_tok +
-                                         db * Gm::VDB * 2 + c * 16)
-                            : u32x4{0u, 0u, 0u, 0u};
-  r.mask = o.mask;
-  r.tiles = o.tiles;
-}
-
-template <int D>
-__device__ __forceinline__ void store_batch(uint8_t *st, const BatchRegs<D> &r) {
-  using Gm = GGeom<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < Gm::KLD; ++it) {
-    const int q = it * GT + tid, key = q / Gm::CPR, c = q % Gm::CPR;
-    *(u32x4 *)(st + gk_off<D>(key, c)) = r.k[it];
-  }
-  uint8_t *sv = st + Gm::K_BYTES;
-  const int kp = tid & 15, db = tid >> 4;
-#pragma unroll
-  for (int c = 0; c < Gm::VLD; ++c)
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int dv = db * Gm::VDB + c * 8 + w * 2 + hh;
-        const uint32_t b0 = hh ? (r.v[0][c][w] >> 16) : (r.v[0][c][w] & 0xffffu);
-        const uint32_t b1 = hh ? (r.v[1][c][w] >> 16) : (r.v[1][c][w] & 0xffffu);
-        *(uint32_t *)(sv + gvt_off(dv, kp >> 2) + ((kp & 3) << 2)) = b0 | (b1 << 16);
-      }
-  uint32_t *meta = (uint32_t *)(st + Gm::K_BYTES + Gm::V_BYTES);
-  if (tid < kGUnitsPerBatch) {
-    meta[tid] = r.mask;
-    meta[kGUnitsPerBatch + tid] = r.tiles;
-  }
-}
+// A row's running max may lag its true max by up to 2^kLag (log2 units)
+// before O is rescaled: P = 2^(s - m) then stays below 2^kLag, well inside
+// FP16, and the rescale of the 64 accumulators runs only when a logit
+// exceeds the running max by more than that.
+constexpr float kLag = 8.0f;
 
 // PO: dtype of partial_o (MSA_F32, MSA_BF16 or MSA_F16).
 template <int D, int PO>
-__global__ void __launch_bounds__(GT, 2) k_grouped_attend(const GroupArgs a) {
+__global__ void __launch_bounds__(GT, 2)
+    k_grouped_attend(const GroupArgs a, const uint2 *__restrict__ lists, const int *__restrict__ split_offs) {
   using Gm = GGeom<D>;
-  constexpr int MT = D / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Gm::STAGE];
-  const int grp = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
+  constexpr int MT = Gm::MT, NST = Gm::NST;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Gm::RING];
+  __shared__ uint2 sList[kListCap];  // the split's units: {page << 5 | unit in page, mask32}
+
+  // ---- work item; consecutive groups on one XCD (workgroups are dealt to
+  // the 8 XCDs round-robin, and the grid's x size is a multiple of 8)
+  const int per_xcd = (a.num_groups + 7) >> 3;
+  const int grp = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (grp >= a.num_groups) return;  // the whole workgroup, before any barrier
+  const int g = blockIdx.y, split = blockIdx.z;
   const int64_t li = (int64_t)g * a.num_groups + grp;
-  const int *soff = (const int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1) + split;
-  const int count = soff[1] - soff[0];
-  const uint4 *list = (const uint4 *)(a.ws + a.lay.lists) + li * a.list_cap + soff[0];
-  const int nb = (count + kGUnitsPerBatch - 1) / kGUnitsPerBatch;
+  const int *soff = split_offs + li * (a.num_splits + 1) + split;
+  const int first = soff[0];
+  const int count = soff[1] - first;
+  const uint2 *list = lists + li * a.list_cap + first;
+  const int nst = (count + UPS - 1) / UPS;  // stages
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, gl = lane >> 4;
+  const int n = lane & 15, gq = lane >> 4;
   const int G = a.G;
   const int rows = kGroupTokens * G;
-  const bool has_tile = wave * 16 < rows;  // wave-uniform
+  // row tile of this wave, rotated by group so that the waves left without
+  // a tile (fewer than 64 rows) are not always on the same SIMD
+  const int tile = (wave + (blockIdx.x >> 3)) & 3;
+  const bool has_tile = tile * 16 < rows;  // wave-uniform
 
   // this lane's row: (token tau of the group, query head h)
-  const int rho = wave * 16 + n;
+  const int rho = tile * 16 + n;
   const int tau = rho / G;
   const int tok = grp * kGroupTokens + tau;
   const bool active = rho < rows && tok < a.total_q;
   const int h = g * G + (active ? rho - tau * G : 0);
   const int tok_c = active ? tok : 0;
+  const int mshift = 4 * tau;
+  // mask bits of the tokens whose rows meet this wave's tile
+  uint32_t tilemask = 0u;
+  if (has_tile) {
+    const int t0 = (tile * 16) / G, t1 = min((tile * 16 + 15) / G, kGroupTokens - 1);
+    for (int t = t0; t <= t1; ++t) tilemask |= 0xfu << (4 * t);
+  }
 
+  const LaneOffsets<D> L = lane_offsets<D>(a, wave);
+  // byte offset in the K / V caches of unit u of the run (an LDS read of its
+  // list entry, wave-uniform)
+  const int64_t head_off = (int64_t)g * a.kv_stride_head;
+  auto unit_off = [&](int u) {
+    const uint32_t e = __builtin_amdgcn_readfirstlane(sList[u].x);
+    return (int64_t)(e >> 5) * a.kv_stride_page + (int64_t)((e & 31u) * 4) * a.kv_stride_tok + head_off;
+  };
+
+  // ---- prologue: the run's list into LDS, Q into registers, then the
+  // first NST - 1 stages in flight.  The loop below issues no memory access
+  // but the counted K/V loads, LDS traffic and its output stores.
+  {  // every load first, then the stores (one round trip, not one per entry)
+    constexpr int PER = kListCap / GT;
+    uint2 e[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * GT;
+      if (i < count) e[k] = list[i];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * GT;
+      if (i < count) sList[i] = e[k];
+    }
+  }
   u32x4 qreg[Gm::LANE_CH];
   {
     const uint8_t *qp = (const uint8_t *)a.q +
-                        ((int64_t)tok_c * a.q_stride_tok + (int64_t)h * a.q_stride_head) * 2 + gl * (Gm::RB / 4);
+                        ((int64_t)tok_c * a.q_stride_tok + (int64_t)h * a.q_stride_head) * 2 + gq * (Gm::RB / 4);
 #pragma unroll
-    for (int c = 0; c < Gm::LANE_CH; ++c) qreg[c] = gld<u32x4>(qp + c * 16);
+    for (int c = 0; c < Gm::LANE_CH; ++c) qreg[c] = *(const u32x4 *)(qp + c * 16);
   }
   f32x4 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f, lp = 0.0f;
   const float sc = a.scale_log2;
-
-  BatchRegs<D> br;
-  BatchOffs<D> bo;  // offsets of the next batch to load
-  if (nb > 0) {
-    fetch_offs<D>(list, count, 0, bo);
-    load_batch<D>(a, bo, br);
-    fetch_offs<D>(list, count, 1, bo);
-    store_batch<D>(smem, br);
-  }
-  __syncthreads();
-
-  for (int beta = 0; beta < nb; ++beta) {
-    if (beta + 1 < nb) {
-      load_batch<D>(a, bo, br);                     // batch beta + 1
-      fetch_offs<D>(list, count, beta + 2, bo);     // offsets of batch beta + 2
-    }
-    const uint8_t *st = smem + (beta & 1) * Gm::STAGE;
-    const uint32_t *meta = (const uint32_t *)(st + Gm::K_BYTES + Gm::V_BYTES);
-    uint32_t tiles = 0;
+  wait_vm_lgkm0<0>();  // Q and the list, read and stored
+  stage_barrier();
 #pragma unroll
-    for (int b = 0; b < kGUnitsPerBatch; ++b) tiles |= meta[kGUnitsPerBatch + b];
-    if (has_tile && ((tiles >> wave) & 1u)) {
+  for (int s = 0; s < NST - 1; ++s) {
+    const int u = UPS * s + wave;
+    if (s < nst) issue_stage<D>(a, smem + s * Gm::STAGE, wave, u < count ? unit_off(u) : 0, u < count, L);
+  }
+
+  // One stage: J (compile time) is its ring slot.
+  auto stage = [&](auto J_, const int beta) {
 #pragma clang fp contract(off)
-      // ---- S^T = K Q^T for the batch's 32 keys
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    constexpr int J = decltype(J_)::value;
+    // loads this wave issued after stage beta's: stages beta+1 .. beta+NST-2
+    // that exist and hold a real unit of this wave (loads retire in order)
+    int newer = 0;
 #pragma unroll
-      for (int c = 0; c < Gm::LANE_CH; ++c)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 kr = *(const u32x4 *)(st + gk_off<D>(gkey_of(t, n), gl * Gm::LANE_CH + c));
-          acc[t] = mfma_f16(kr, qreg[c], acc[t]);
-        }
-      // ---- exact masks: lane holds keys 8*gl + 4*t + i = unit 2*gl + t, bit i
-      const uint32_t mu[2] = {meta[2 * gl], meta[2 * gl + 1]};
-      float mb = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool vis = active && ((mu[t] >> (4 * tau + i)) & 1u);
-          const float x = vis ? acc[t][i] * sc : -INFINITY;
-          acc[t][i] = x;
-          mb = fmaxf(mb, x);
-        }
-      mb = quarter_reduce<true>(mb);
-      const float mn = fmaxf(m, mb);
-      // ---- rescale when some row's running max grew
-      if (__any(mn > m)) {
-        const float alpha = (mn > m) ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn)) : 1.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
-        l *= alpha;
-        lp *= alpha;
-        m = mn;
-      }
-      // ---- P (0 for masked keys), sums, FP16 pairs
-      uint32_t pk[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = (acc[t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(acc[t][i] - m);
-          l += p[i];
-        }
-        pk[2 * t] = pack_f16x2(p[0], p[1]);
-        pk[2 * t + 1] = pack_f16x2(p[2], p[3]);
-        lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2 * t]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
-        lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2 * t + 1]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
-      }
-      // ---- O^T += V^T P^T (one 32-key step)
-      const u32x4 pf = {pk[0], pk[1], pk[2], pk[3]};
-      const uint8_t *sv = st + Gm::K_BYTES;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 vf = *(const u32x4 *)(sv + gvt_off(mt * 16 + n, gl));
-        o[mt] = mfma_f16(vf, pf, o[mt]);
-      }
+    for (int s = 1; s <= NST - 2; ++s)
+      newer += (beta + s < nst && UPS * (beta + s) + wave < count) ? Gm::LOADS : 0;
+    if (newer == 0) wait_vm_lgkm0<0>();
+    else if (newer == Gm::LOADS) wait_vm_lgkm0<Gm::LOADS>();
+    else wait_vm_lgkm0<2 * Gm::LOADS>();
+    stage_barrier();  // stage beta landed for every wave; slot of beta - 1 free
+    {
+      const int s = beta + NST - 1, u = UPS * s + wave;
+      if (s < nst)
+        issue_stage<D>(a, smem + ((J + NST - 1) % NST) * Gm::STAGE, wave, u < count ? unit_off(u) : 0,
+                       u < count, L);
     }
-    if (beta + 1 < nb) store_batch<D>(smem + ((beta + 1) & 1) * Gm::STAGE, br);
-    __syncthreads();
+    const uint8_t *st = smem + J * Gm::STAGE;
+    // this lane group's unit of the stage, and whether any unit of the stage
+    // has a token of this wave's tile
+    const int ug = UPS * beta + gq;
+    const uint32_t mask = ug < count ? sList[ug].y : 0u;
+    if (!has_tile || !__any((mask & tilemask) != 0u)) return;
+    // ---- every LDS operand of the stage is requested up front: the K
+    // fragments of S^T = K Q^T and the V^T fragments of the PV product (lane n
+    // receives V rows 4gq .. 4gq+3 at dim 16 mt + n), so the PV products can
+    // start as soon as P is ready
+    u32x4 kf[Gm::LANE_CH];
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) kf[c] = *(const u32x4 *)(st + L.k[c]);
+    i16x4 vt[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(st + L.v[mt & 7] + (mt & 8) * 32));
+    __asm__ volatile("" ::: "memory");
+    // ---- S^T for the stage's 16 keys (lane: keys 4gq..4gq+3 of row n), the
+    // contraction split over four accumulators to shorten the chain of
+    // dependent products
+    f32x4 ac[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Gm::LANE_CH; ++c) ac[c & 3] = mfma_f16(kf[c], qreg[c], ac[c & 3]);
+    const f32x4 acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
+    // ---- exact masks: key i of this lane group's unit gq
+    const uint32_t bits = active ? (mask >> mshift) & 0xfu : 0u;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = ((bits >> i) & 1u) ? acc[i] * sc : -INFINITY;
+    float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mb = quarter_reduce<true>(mb);
+    // ---- raise the running max only when a logit passes it by kLag
+    const bool up = mb > m + kLag;  // also when m is still -inf and mb is not
+    if (__any(up)) {
+      const float alpha = up ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mb)) : 1.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      l *= alpha;
+      lp *= alpha;
+      m = up ? mb : m;
+    }
+    // ---- P = 2^(s - m) < 2^kLag (0 for masked keys and for rows with no
+    // key yet), sums, FP16 operand
+    const float ms = (m == -INFINITY) ? 0.0f : m;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(x[i] - ms);
+      l += p[i];
+    }
+    const uint32_t pk0 = pack_f16x2(p[0], p[1]), pk1 = pack_f16x2(p[2], p[3]);
+    lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk0), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
+    lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk1), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
+    const f16x4v pf = __builtin_bit_cast(f16x4v, u32x2{pk0, pk1});
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4v, vt[mt]), pf, o[mt], 0, 0, 0);
+  };
+
+  for (int beta0 = 0; beta0 < nst; beta0 += NST) {
+    stage(std::integral_constant<int, 0>{}, beta0);
+    if (beta0 + 1 < nst) stage(std::integral_constant<int, 1>{}, beta0 + 1);
+    if (beta0 + 2 < nst) stage(std::integral_constant<int, 2 % NST>{}, beta0 + 2);
+    if constexpr (NST > 3) {
+      if (beta0 + 3 < nst) stage(std::integral_constant<int, 3 % NST>{}, beta0 + 3);
+    }
   }
 
-  // ---- epilogue: row n of the tile, columns 16*mt + 4*gl + [0,4)
+  // ---- epilogue: row n of the tile, columns 16*mt + 4*gq + [0,4).  The
+  // output is (O / lp) * v_scale with a true division: when one key carries
+  // all the weight, O = p v exactly and lp = p, so the row is v * v_scale
+  // bit for bit whatever P's scale.
   if (!has_tile || !active) return;
   l = quarter_reduce<false>(l);
   lp = quarter_reduce<false>(lp);
   const int64_t row = (int64_t)tok * a.Hq + h;
-  const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + gl * 4;
+  const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + gq * 4;
   float *lse_dst = a.partial_lse + (int64_t)split * a.pl_split_stride + row;
   if (l > 0.0f) {
-    const float inv = a.v_scale / lp;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, o[mt] * inv);
-    if (gl == 0) *lse_dst = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (o[mt][i] / lp) * a.v_scale;
+      store_partial4<PO>(a.partial_o, off + mt * 16, r);
+    }
+    if (gq == 0) *lse_dst = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
   } else {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) store_partial4<PO>(a.partial_o, off + mt * 16, f32x4{0.f, 0.f, 0.f, 0.f});
-    if (gl == 0) *lse_dst = -INFINITY;
+    if (gq == 0) *lse_dst = -INFINITY;
   }
 }
 
 }  // namespace
 
 size_t grouped_attend_lds_bytes() {
-  return (size_t)(2 * (GGeom<256>::STAGE > GGeom<128>::STAGE ? GGeom<256>::STAGE : GGeom<128>::STAGE));
+  return (size_t)(GGeom<256>::LDS > GGeom<128>::LDS ? GGeom<256>::LDS : GGeom<128>::LDS);
 }
+static_assert(kListCap >= kGroupTokens * 512, "the list must hold 8 tokens x 512 slots");
 
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;
-  dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv, (unsigned)a.num_splits);
+  dim3 grid((unsigned)((a.num_groups + 7) / 8 * 8), (unsigned)a.Hkv, (unsigned)a.num_splits);
+  const uint2 *lists = (const uint2 *)(a.ws + a.lay.lists);
+  const int *soffs = (const int *)(a.ws + a.lay.split_off);
   switch ((a.D == 256 ? 8 : 0) + a.po_dtype) {
-    case 8 + MSA_F32: k_grouped_attend<256, MSA_F32><<<grid, GT, 0, s>>>(a); break;
-    case 8 + MSA_BF16: k_grouped_attend<256, MSA_BF16><<<grid, GT, 0, s>>>(a); break;
-    case 8 + MSA_F16: k_grouped_attend<256, MSA_F16><<<grid, GT, 0, s>>>(a); break;
-    case MSA_BF16: k_grouped_attend<128, MSA_BF16><<<grid, GT, 0, s>>>(a); break;
-    case MSA_F16: k_grouped_attend<128, MSA_F16><<<grid, GT, 0, s>>>(a); break;
-    default: k_grouped_attend<128, MSA_F32><<<grid, GT, 0, s>>>(a); break;
+    case 8 + MSA_F32: k_grouped_attend<256, MSA_F32><<<grid, GT, 0, s>>>(a, lists, soffs); break;
+    case 8 + MSA_BF16: k_grouped_attend<256, MSA_BF16><<<grid, GT, 0, s>>>(a, lists, soffs); break;
+    case 8 + MSA_F16: k_grouped_attend<256, MSA_F16><<<grid, GT, 0, s>>>(a, lists, soffs); break;
+    case MSA_BF16: k_grouped_attend<128, MSA_BF16><<<grid, GT, 0, s>>>(a, lists, soffs); break;
+    case MSA_F16: k_grouped_attend<128, MSA_F16><<<grid, GT, 0, s>>>(a, lists, soffs); break;
+    default: k_grouped_attend<128, MSA_F32><<<grid, GT, 0, s>>>(a, lists, soffs); break;
   }
   return hipGetLastError();
 }

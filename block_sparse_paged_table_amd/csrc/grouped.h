@@ -8,12 +8,13 @@ namespace msa {
 constexpr int kGroupTokens = 8;        // adjacent query tokens per group
 constexpr int kGPlanThreads = 256;       // planner workgroup, many groups
 constexpr int kGPlanThreadsFew = 1024;  // planner workgroup when groups are few
-constexpr int kGUnitsPerBatch = 8;     // microblocks per attention batch (32 keys)
 
 // Workspace of the grouped route.  Per (KV head, group): a list of up to
-// list_cap entries {K/V byte offset (lo, hi), mask32, active row tiles},
-// ordered by split, and the num_splits + 1 offsets of the splits' runs in it
-// (split s owns entries [split_off[s], split_off[s + 1])).
+// list_cap 8-byte entries {physical page << 5 | unit index in the page,
+// mask32 (4 visible-token bits per token of the group)}, ordered by split
+// and, within a split, by unit; and the num_splits + 1 offsets of the
+// splits' runs in it (split s owns entries [split_off[s], split_off[s + 1])).
+// `stage` is the planner's own scratch (16 bytes per candidate unit).
 struct GroupLayout {
   size_t meta, split_off, stage, lists, total;
 };
@@ -24,7 +25,7 @@ __host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, in
   L.meta = off;   off = align_up(off + 64 * 4, 256);
   L.split_off = off; off = align_up(off + (size_t)num_lists * (num_splits + 1) * 4, 256);
   L.stage = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
-  L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
+  L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 8, 256);
   L.total = off;
   return L;
 }

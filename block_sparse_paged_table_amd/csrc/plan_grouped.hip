@@ -4,11 +4,11 @@
 // kernel loads once for all rows of the group.  On the GPU and
 // deterministically, it drops any selection it cannot honour (a padding
 // row, a request id outside the batch, a unit past the request's table row
-// or its tail, a table entry outside the cache) and flags it, and it orders
-// the resulting units by which row tiles use them, so a tile with nothing in
-// a batch skips it.  The union of a group is bounded by its 8 rows times
-// their slots, and the order of the list is a function of the categories
-// and logical units alone, never of scheduling.
+// or its tail, a table entry outside the cache) and flags it.  Each unit
+// carries the row tiles that use it, so a tile with nothing in a batch of
+// units skips it.  The union of a group is bounded by its 8 rows times their
+// slots, and the order of the list is a function of the splits and the
+// logical units alone, never of scheduling.
 //
 // One workgroup per (group of kGroupTokens consecutive query tokens, KV head):
 //   1. every (token, slot) selection becomes a 64-bit key
@@ -22,12 +22,12 @@
 //      request, unit) gets a 32-bit mask, 4 visible-token bits per token of
 //      the group; units no row sees are dropped; the physical page is looked
 //      up and checked;
-//   4. the union is sorted again by (split, active row tiles, active tokens,
-//      request, unit) so each split's units are contiguous and consecutive
-//      units share their category, letting whole row tiles skip a batch;
-//   5. the group's list is written: {K/V row offset of the unit's first
-//      token in bytes (low, high), mask32, active tiles} per unit, and the
-//      offsets of the splits' runs in it.
+//   4. the union is ordered by (split, request, unit): each split's units
+//      are contiguous, and within a split the units ascend, so the groups an
+//      XCD runs together walk the cache in step and share its L2;
+//   5. the group's list is written, 8 bytes per unit: its physical page and
+//      its index inside the page (page << 5 | unit), and its mask32; then
+//      the offsets of the splits' runs in the list.
 #include "grouped.h"
 
 namespace msa {
@@ -343,7 +343,7 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   const int64_t li = (int64_t)g * a.num_groups + grp;
   const int64_t list_base = li * a.list_cap;
   uint4 *stage = (uint4 *)(a.ws + a.lay.stage) + list_base;
-  uint4 *out = (uint4 *)(a.ws + a.lay.lists) + list_base;
+  uint2 *out = (uint2 *)(a.ws + a.lay.lists) + list_base;
   int total = 0;
   for (int i = 0; i < per; ++i) {
     const Lead L = analyze(i * NT + threadIdx.x);
@@ -363,43 +363,28 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   }
   __syncthreads();
 
-  // ---- 4. category keys: (split, tiles, tokens, index in the staged order)
-  const int G = a.G;
+  // ---- 4. list order: (split, request, unit).  The staged order is already
+  // (request, unit) with each unit's split; units are kept in that order
+  // inside each split, so the groups running together on one XCD sweep the
+  // cache in the same direction and share its L2 (their unions overlap).
   int n2 = NT;  // the union is usually far smaller than npow2
   while (n2 < total) n2 <<= 1;
-  for (int e = threadIdx.x; e < n2; e += NT) {
-    uint64_t key = kInvalidKey;
-    if (e < total) {
-      const uint4 st = stage[e];
-      const uint32_t m32 = st.z;
-      uint32_t toks = 0, tiles = 0;
-#pragma unroll
-      for (int tau = 0; tau < kGroupTokens; ++tau)
-        if ((m32 >> (4 * tau)) & 0xfu) {
-          toks |= 1u << tau;
-          const int r0 = tau * G, r1 = tau * G + G - 1;  // rows of this token
-          tiles |= (1u << (r0 >> 4)) | (1u << (r1 >> 4));
-        }
-      key = ((uint64_t)st.w << 48) | ((uint64_t)tiles << 40) | ((uint64_t)toks << 32) | (uint64_t)e;
-    }
-    keys[e] = key;
-  }
-  if (one_split) {
-    // split 0 throughout: (tiles:8 | tokens:8 | index:16) orders the keys as
-    // the 64-bit form does; the index is below 8 * 512
+  if (!one_split) {
+    // (split:10 | staged index:16) sorts on 32 bits (index < 8 * 512)
+    for (int e = threadIdx.x; e < n2; e += NT)
+      keys[e] = e < total ? ((uint64_t)stage[e].w << 48) | (uint64_t)e : kInvalidKey;
     bitonic_sort32(keys, n2,
                    [](uint64_t x) {
-                     return x == kInvalidKey ? ~0u
-                                             : (uint32_t)(((x >> 40) & 0xffu) << 24 | ((x >> 32) & 0xffu) << 16 |
-                                                          (x & 0xffffu));
+                     return x == kInvalidKey ? ~0u : (uint32_t)((x >> 48) << 16 | (x & 0xffffu));
                    },
-                   [](uint32_t x) {
-                     return (uint64_t)(x >> 24) << 40 | (uint64_t)((x >> 16) & 0xffu) << 32 | (x & 0xffffu);
-                   });
-  } else {
-    bitonic_sort(keys, n2);
+                   [](uint32_t x) { return (uint64_t)(x >> 16) << 48 | (x & 0xffffu); });
   }
   const int sh2 = __builtin_ctz((unsigned)(n2 / NT));
+  if (one_split) {  // already in order: written in the sorted (padded) layout
+    __syncthreads();
+    for (int e = threadIdx.x; e < n2; e += NT) keys[e + (e >> sh2)] = e < total ? (uint64_t)e : kInvalidKey;
+    __syncthreads();
+  }
 
   // ---- 5. final list: byte offset of the unit's first K/V row, mask, tiles
   // (four entries per thread in flight: their page-table loads overlap)
@@ -423,16 +408,13 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
       const int e = e0 + i * NT;
       if (e >= total) continue;
       const uint64_t unit_id = (uint64_t)st[i].x | ((uint64_t)st[i].y << 32);
-      const int t0 = (int)(unit_id & 0xffffffu) * a.unit_tokens;
-      uint4 r;
+      const int upp = a.page_size / a.unit_tokens;  // units per page
+      uint2 r;
       if (phys[i] < 0 || phys[i] >= a.num_phys_pages) {
         err |= MSA_ERRF_PHYS_RANGE;
-        r = make_uint4(0u, 0u, 0u, 0u);  // mask 0: contributes nothing
+        r = make_uint2(0u, 0u);  // mask 0: contributes nothing
       } else {
-        const int64_t off = (int64_t)phys[i] * a.kv_stride_page +
-                            (int64_t)(t0 % a.page_size) * a.kv_stride_tok + (int64_t)g * a.kv_stride_head;
-        r = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), st[i].z,
-                       (uint32_t)(ck[i] >> 40) & 0xffu);
+        r = make_uint2(((uint32_t)phys[i] << 5) | (uint32_t)((int)(unit_id & 0xffffffu) % upp), st[i].z);
       }
       out[e] = r;
     }
