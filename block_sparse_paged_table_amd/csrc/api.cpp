@@ -45,7 +45,7 @@ int esize(int dt) {
   }
 }
 
-constexpr int kPageRouteRowsPerUnit = 1024;  // (token, head) rows per work unit
+constexpr int kPageRouteRowsPerUnit = 1024;  // (token, head) rows per work unit (at most)
 constexpr int kMaxDevices = 64;               // devices the per-device caches cover
 
 // Route of a descriptor (page selections), or -1.
@@ -272,8 +272,8 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
 
   // Ordering slices: the plan keeps one list per (slice, KV head, request,
   // logical page), so units come out slice by slice (one KV head after the
-  // other) and the workgroups an XCD runs at one time read the queries of
-  // one slice and head group only.  Automatic
+  // other) and the workgroups in flight at one time read the queries of one
+  // slice and head group only.  Automatic
   // size: none while all queries fit in 16 MiB (their re-reads then hit the
   // caches anyway); else ~512 KiB of queries per slice, but enough tokens
   // that an average page list of a slice still fills one unit.
@@ -295,9 +295,9 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
   }
   r.slice_rows = (int32_t)slice_rows;
   r.lists_per_slice = (int32_t)L;
-  r.lay = page_layout(n_slices * L, NS);
   // every unit holds >= 1 entry: units <= entries/chunk + non-empty lists
   r.max_units = NS / r.chunk + std::min(n_slices * L, NS);
+  r.lay = page_layout(n_slices * L, NS, r.max_units);
   return MSA_OK;
 }
 

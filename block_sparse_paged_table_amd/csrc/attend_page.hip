@@ -340,30 +340,19 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
   float *sRed = (float *)(smem + Gm::K_BYTES + Gm::V_BYTES);
   PlanEntry *sEnt = (PlanEntry *)(smem + Gm::K_BYTES + Gm::V_BYTES + 64);
 
-  // ---- work unit (XCD-aware: consecutive units stay on one XCD's L2)
-  const int32_t *meta = (const int32_t *)(a.ws + a.lay.meta);
-  const int num_units = meta[0];
-  const int per_xcd = (num_units + 7) >> 3;
-  const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int unit = (bid & 7) * per_xcd + (bid >> 3);
+  // ---- work unit.  Units go to the XCDs round robin (workgroup i runs on
+  // XCD i mod 8): their sizes vary with the request (a long chunk's pages
+  // carry many more queries), and contiguous unit ranges per XCD left some
+  // XCDs with several times the work of others.  The slice ordering of the
+  // units still keeps the queries all XCDs read at one time to one slice.
+  // The unit's record is read before the unit count (both loads in flight at
+  // once): the grid never exceeds the record array, whose tail past the
+  // count is simply not used.
+  const int unit = blockIdx.x;
+  const PageUnit wu = ((const PageUnit *)(a.ws + a.lay.units))[unit];
+  const int num_units = ((const int32_t *)(a.ws + a.lay.meta))[0];
   if (unit >= num_units) return;
-  const int32_t *unit_off = (const int32_t *)(a.ws + a.lay.unit_off);
-  const int32_t *list_off = (const int32_t *)(a.ws + a.lay.list_off);
-  int lo = 0, hi = (int)a.lay.num_lists;  // unit_off[lo] <= unit < unit_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (unit_off[mid] <= unit) lo = mid; else hi = mid;
-  }
-  const int list = lo;  // (slice, KV head, request, logical page)
-  const int chunk_i = unit - unit_off[list];
-  const int e_begin = list_off[list] + chunk_i * a.chunk;
-  const int e_count = min(a.chunk, list_off[list + 1] - e_begin);
-  const int pl = list % a.lists_per_slice;
-  const int u = pl % a.max_pages;
-  const int b = (pl / a.max_pages) % a.num_seqs;
-  const int g = pl / (a.max_pages * a.num_seqs);
-  const int phys = a.page_table[b * a.pt_stride + u];
+  const int e_begin = wu.e_begin, e_count = wu.e_count, g = wu.g, phys = wu.phys;
 
   // ---- the unit's entries -> LDS (so the tile loop issues no dependent
   // global loads behind its own stores: vmcnt counts loads and stores alike)
@@ -682,7 +671,7 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
 
 template <int ROUTE, int D>
 hipError_t launch_route(const PageArgs &a, hipStream_t s) {
-  const int64_t grid = (a.max_units + 7) / 8 * 8;
+  const int64_t grid = a.max_units;
   if (grid == 0) return hipSuccess;
   if constexpr (ROUTE == kRouteF32) {  // FP32 partials only (checked on the host)
     k1_page_attend<ROUTE, D, MSA_F32><<<(unsigned)grid, THREADS, 0, s>>>(a);

@@ -191,20 +191,28 @@ struct PlanEntry {
   int32_t limit;      // min(q_pos, seq_len - 1) - page_start, in [0, page)
 };
 
+// One work unit of the page route, as the plan writes it: a chunk of one
+// list's entries and the list's physical page and KV head.
+struct PageUnit {
+  int32_t e_begin, e_count, phys, g;
+};
+
 struct PageLayout {
   int64_t num_lists;     // slices * num_seqs * max_pages * Hkv
   int64_t num_sel;       // total_q * Hkv * num_slots
-  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, meta, dump, tiles, total;
+  int64_t max_units;     // bound on the work units
+  size_t counts, list_off, unit_off, slot_list, slot_pos, entries, units, meta, dump, tiles, total;
 };
 
 constexpr int kScanTile = 4096;  // lists per block of the plan's scan
 
 __host__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel) {
+__host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel, int64_t max_units) {
   PageLayout L;
   L.num_lists = num_lists;
   L.num_sel = num_sel;
+  L.max_units = max_units;
   size_t off = 0;
   L.meta = off;      off = align_up(off + 64 * 4, 256);
   L.dump = off;      off = align_up(off + 1024 * 4, 256);  // scratch for masked-off stores
@@ -214,7 +222,8 @@ __host__ inline PageLayout page_layout(int64_t num_lists, int64_t num_sel) {
   L.slot_list = off; off = align_up(off + (size_t)num_sel * 4, 256);
   L.slot_pos = off;  off = align_up(off + (size_t)num_sel * 4, 256);
   L.entries = off;   off = align_up(off + (size_t)num_sel * sizeof(PlanEntry), 256);
-  L.tiles = off;     off = align_up(off + (size_t)((num_lists + kScanTile - 1) / kScanTile + 1) * 8, 256);
+  L.units = off;     off = align_up(off + (size_t)max_units * sizeof(PageUnit), 256);
+  L.tiles = off;     off = align_up(off + (size_t)((num_lists + kScanTile - 1) / kScanTile + 1) * 4 * 8, 256);
   L.total = off;
   return L;
 }

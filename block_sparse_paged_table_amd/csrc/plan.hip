@@ -9,16 +9,18 @@
 //                position inside its (slice, KV head, request, logical page)
 //                list.  Slices are runs of slice_rows (token, KV head) rows;
 //                listing them outermost makes the work units come out slice
-//                by slice, so the units running together on one XCD re-read
-//                the queries of one slice only (they stay in its L2).
+//                by slice, so the units running together re-read the
+//                queries of one slice only (they stay in the L2s).
 //                A workgroup first counts into an LDS histogram, then claims
 //                its block of each list with one global atomic per list, so
 //                the global counters see one atomic per (workgroup, list)
 //                instead of one per selection.
 //   plan_scan  : exclusive scans of list sizes and of work units (lists cut
-//                into chunks of `chunk` entries), tile by tile
+//                evenly into units of at most `chunk` entries, numbered by
+//                size class, largest first), tile by tile
 //   plan_fill  : scatter (token, slot, visible limit) entries to their
-//                positions (no atomics)
+//                positions (no atomics), and write one record per work unit
+//                (its entries, physical page and KV head)
 //
 // Entry order inside a list depends on atomics, but every (token, slot)
 // partial is computed on its own, so the results do not depend on it.
@@ -184,76 +186,128 @@ constexpr int kScanThreads = 1024;
 constexpr int kScanPer = kScanTile / kScanThreads;  // lists per thread
 constexpr int kScanOneBlockMax = kScanThreads * 8;  // lists one workgroup scans alone
 
+// With a single ordering slice (all queries fit in the caches, so there is
+// no query locality to keep), work units are numbered by size class, largest
+// first, and by list within a class: the workgroups dispatched last then run
+// the shortest units instead of, say, the own pages of the last request,
+// which would otherwise end the kernel long after the rest.  With several
+// slices the units stay in list (slice) order.  A list of n entries makes
+// ceil(n / chunk) units of n / units entries each; its class is 0 for units
+// of at least chunk/2 entries, 1 for chunk/4, 2 for chunk/8, else 3.
+constexpr int kSizeClasses = 4;
+__device__ __forceinline__ int units_of(int32_t n, int chunk) { return (n + chunk - 1) / chunk; }
+__device__ __forceinline__ int size_class(const PageArgs &a, int32_t n) {
+  if (a.lay.num_lists != a.lists_per_slice) return 0;
+  const int32_t s = n / max(1, units_of(n, a.chunk));  // entries per unit (rounded down)
+  return 2 * s >= a.chunk ? 0 : (4 * s >= a.chunk ? 1 : (8 * s >= a.chunk ? 2 : 3));
+}
+
+// Per-class unit counts of one thread's lists, and its running offsets.
+struct ClassCounts {
+  int32_t v[kSizeClasses];
+};
+
 // Up to kScanOneBlockMax lists: one workgroup scans them all, PER lists per
 // thread -- inclusive scans within each wave by shuffles, the wave totals
-// through LDS behind a single barrier -- and writes the final offsets.
+// through LDS behind a single barrier -- and writes the final offsets:
+// list_off (entries) in list order, unit_off (the list's first unit) in
+// (size class, list) order.
 template <int PER>
 __global__ void __launch_bounds__(kScanThreads) plan_scan_one(const PageArgs a) {
   constexpr int NW = kScanThreads / 64;
-  __shared__ int32_t w_e[NW], w_u[NW];
+  constexpr int NC = kSizeClasses;
+  __shared__ int32_t w_e[NW], w_u[NC][NW];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t L = a.lay.num_lists;
   const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
   const int64_t i0 = (int64_t)t * PER;
-  int32_t c[PER], u[PER];
-  int32_t se = 0, su = 0;
+  int32_t c[PER];
+  int32_t se = 0;
+  ClassCounts su = {};
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     // unconditional loads (clamped index; L >= 1), so that all of them are
     // in flight at once instead of one branch and wait per list
     const int32_t v = counts[min(i0 + k, L - 1)];
     c[k] = i0 + k < L ? v : 0;
-    u[k] = (c[k] + a.chunk - 1) / a.chunk;
     se += c[k];
-    su += u[k];
+    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) su.v[q] += q == cl ? u : 0;
   }
-  int32_t ie = se, iu = su;  // inclusive scans over the wave's lanes
+  int32_t ie = se;  // inclusive scans over the wave's lanes
+  ClassCounts iu = su;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int32_t ve = __shfl_up(ie, off), vu = __shfl_up(iu, off);
+    const int32_t ve = __shfl_up(ie, off);
+    ClassCounts vu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) vu.v[q] = __shfl_up(iu.v[q], off);
     if (lane >= off) {
       ie += ve;
-      iu += vu;
+#pragma unroll
+      for (int q = 0; q < NC; ++q) iu.v[q] += vu.v[q];
     }
   }
   if (lane == 63) {
     w_e[w] = ie;
-    w_u[w] = iu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) w_u[q][w] = iu.v[q];
   }
   __syncthreads();
-  int32_t oe = 0, ou = 0;  // totals of the earlier waves
-  for (int k = 0; k < w; ++k) {
-    oe += w_e[k];
-    ou += w_u[k];
+  int32_t oe = 0;  // totals of the earlier waves
+  ClassCounts ou = {}, tot = {};
+  for (int k = 0; k < NW; ++k) {
+    if (k < w) oe += w_e[k];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      ou.v[q] += k < w ? w_u[q][k] : 0;
+      tot.v[q] += w_u[q][k];
+    }
   }
-  int32_t be = oe + ie - se, bu = ou + iu - su;
+  int32_t be = oe + ie - se;
+  ClassCounts bu;
+  int32_t base = 0;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    bu.v[q] = base + ou.v[q] + iu.v[q] - su.v[q];
+    base += tot.v[q];
+  }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
+    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+    int32_t uo = bu.v[0];
+#pragma unroll
+    for (int q = 1; q < NC; ++q) uo = q == cl ? bu.v[q] : uo;
     if (i0 + k < L) {
       list_off[i0 + k] = be;
-      unit_off[i0 + k] = bu;
+      unit_off[i0 + k] = uo;
     }
     be += c[k];
-    bu += u[k];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) bu.v[q] += q == cl ? u : 0;
   }
   if (t == kScanThreads - 1) {
     int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
     list_off[L] = be;
-    unit_off[L] = bu;
-    meta[0] = bu;  // number of work units
-    meta[2] = be;  // number of entries
+    meta[0] = base;  // number of work units
+    meta[2] = be;    // number of entries
   }
 }
 
-// More lists: exclusive scans of list sizes (-> list_off, entry offsets) and
-// of work units per list (-> unit_off), in three steps: per tile of
-// kScanTile lists, over the tile totals, then tile offsets added back.
+// More lists: the same offsets in three steps -- per tile of kScanTile lists
+// (offsets within the tile, per class), over the tile totals (tile offsets
+// per class, class bases), then the tile offsets added back.  Per tile, the
+// tiles array holds 1 + kSizeClasses words: entries, then units per class.
+constexpr int kTileWords = 1 + kSizeClasses;
+
 __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a) {
   constexpr int PER = kScanPer;
+  constexpr int NC = kSizeClasses;
   __shared__ int32_t s_e[kScanThreads];
-  __shared__ int32_t s_u[kScanThreads];
+  __shared__ int32_t s_u[NC][kScanThreads];
   const int t = threadIdx.x;
   const int64_t L = a.lay.num_lists;
   const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
@@ -261,99 +315,178 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
   const int64_t i0 = (int64_t)blockIdx.x * (kScanThreads * PER) + (int64_t)t * PER;
   int32_t c[PER];
-  int32_t se = 0, su = 0;
+  int32_t se = 0;
+  ClassCounts su = {};
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int32_t v = counts[min(i0 + k, L - 1)];
     c[k] = i0 + k < L ? v : 0;
     se += c[k];
-    su += (c[k] + a.chunk - 1) / a.chunk;
+    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) su.v[q] += q == cl ? u : 0;
   }
   s_e[t] = se;
-  s_u[t] = su;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) s_u[q][t] = su.v[q];
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {
     const int32_t ve = t >= off ? s_e[t - off] : 0;
-    const int32_t vu = t >= off ? s_u[t - off] : 0;
+    ClassCounts vu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) vu.v[q] = t >= off ? s_u[q][t - off] : 0;
     __syncthreads();
     s_e[t] += ve;
-    s_u[t] += vu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) s_u[q][t] += vu.v[q];
     __syncthreads();
   }
-  int32_t be = s_e[t] - se, bu = s_u[t] - su;
+  int32_t be = s_e[t] - se;
+  ClassCounts bu;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) bu.v[q] = s_u[q][t] - su.v[q];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
+    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+    int32_t uo = bu.v[0];
+#pragma unroll
+    for (int q = 1; q < NC; ++q) uo = q == cl ? bu.v[q] : uo;
     if (i0 + k < L) {
       list_off[i0 + k] = be;
-      unit_off[i0 + k] = bu;
+      unit_off[i0 + k] = uo;
     }
     be += c[k];
-    bu += (c[k] + a.chunk - 1) / a.chunk;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) bu.v[q] += q == cl ? u : 0;
   }
   if (t == kScanThreads - 1) {  // this tile's totals, for plan_scan_top
-    int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
-    tiles[2 * blockIdx.x] = s_e[t];
-    tiles[2 * blockIdx.x + 1] = s_u[t];
+    int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles) + (int64_t)blockIdx.x * kTileWords;
+    tiles[0] = s_e[t];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) tiles[1 + q] = s_u[q][t];
   }
 }
 
 __global__ void __launch_bounds__(kScanThreads) plan_scan_top(const PageArgs a, int nt) {
+  constexpr int NC = kSizeClasses;
   __shared__ int32_t s_e[kScanThreads];
-  __shared__ int32_t s_u[kScanThreads];
+  __shared__ int32_t s_u[NC][kScanThreads];
   const int t = threadIdx.x;
   int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles);
   const int per = (nt + kScanThreads - 1) / kScanThreads;
   const int j0 = min(nt, t * per), j1 = min(nt, j0 + per);
-  int32_t se = 0, su = 0;
+  int32_t se = 0;
+  ClassCounts su = {};
   for (int j = j0; j < j1; ++j) {
-    se += tiles[2 * j];
-    su += tiles[2 * j + 1];
+    se += tiles[j * kTileWords];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) su.v[q] += tiles[j * kTileWords + 1 + q];
   }
   s_e[t] = se;
-  s_u[t] = su;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) s_u[q][t] = su.v[q];
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {
     const int32_t ve = t >= off ? s_e[t - off] : 0;
-    const int32_t vu = t >= off ? s_u[t - off] : 0;
+    ClassCounts vu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) vu.v[q] = t >= off ? s_u[q][t - off] : 0;
     __syncthreads();
     s_e[t] += ve;
-    s_u[t] += vu;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) s_u[q][t] += vu.v[q];
     __syncthreads();
   }
-  int32_t be = s_e[t] - se, bu = s_u[t] - su;
+  // class q's units start after all units of the classes before it
+  ClassCounts base;
+  int32_t total = 0;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    base.v[q] = total;
+    total += s_u[q][kScanThreads - 1];
+  }
+  int32_t be = s_e[t] - se;
+  ClassCounts bu;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) bu.v[q] = base.v[q] + s_u[q][t] - su.v[q];
   for (int j = j0; j < j1; ++j) {  // totals -> exclusive offsets, in place
-    const int32_t e = tiles[2 * j], u = tiles[2 * j + 1];
-    tiles[2 * j] = be;
-    tiles[2 * j + 1] = bu;
+    int32_t *tj = tiles + j * kTileWords;
+    const int32_t e = tj[0];
+    tj[0] = be;
     be += e;
-    bu += u;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int32_t u = tj[1 + q];
+      tj[1 + q] = bu.v[q];
+      bu.v[q] += u;
+    }
   }
   if (t == kScanThreads - 1) {
     const int64_t L = a.lay.num_lists;
     int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
     ((int32_t *)(a.ws + a.lay.list_off))[L] = s_e[t];
-    ((int32_t *)(a.ws + a.lay.unit_off))[L] = s_u[t];
-    meta[0] = s_u[t];
+    meta[0] = total;
     meta[2] = s_e[t];
   }
 }
 
 __global__ void __launch_bounds__(kScanThreads) plan_scan_add(const PageArgs a) {
-  const int tile = blockIdx.x + 1;  // tile 0 has offset 0
-  const int32_t *tiles = (const int32_t *)(a.ws + a.lay.tiles);
-  const int32_t oe = tiles[2 * tile], ou = tiles[2 * tile + 1];
+  const int tile = blockIdx.x;
+  const int32_t *tiles = (const int32_t *)(a.ws + a.lay.tiles) + (int64_t)tile * kTileWords;
+  const int32_t oe = tiles[0];
+  ClassCounts ou;
+#pragma unroll
+  for (int q = 0; q < kSizeClasses; ++q) ou.v[q] = tiles[1 + q];
+  const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
   const int64_t L = a.lay.num_lists;
   const int64_t i0 = (int64_t)tile * kScanTile;
   for (int k = threadIdx.x; k < kScanTile; k += kScanThreads)
     if (i0 + k < L) {
+      const int cl = size_class(a, counts[i0 + k]);
+      int32_t o = ou.v[0];
+#pragma unroll
+      for (int q = 1; q < kSizeClasses; ++q) o = q == cl ? ou.v[q] : o;
       list_off[i0 + k] += oe;
-      unit_off[i0 + k] += ou;
+      unit_off[i0 + k] += o;
     }
 }
 
-__global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a) {
+// The work units of list l: its entries split evenly into units of at most
+// a.chunk entries (from unit_off[l] on), each with the list's physical page
+// (in range: a list exists only for a valid page) and KV head, so that the
+// attention kernel reads one record per unit.
+__device__ __forceinline__ void write_units(const PageArgs &a, int64_t l) {
+  if (l >= a.lay.num_lists) return;
+  const int32_t *list_off = (const int32_t *)(a.ws + a.lay.list_off);
+  const int32_t *unit_off = (const int32_t *)(a.ws + a.lay.unit_off);
+  const int32_t lo = list_off[l], n = list_off[l + 1] - lo;
+  if (n == 0) return;
+  const int32_t u0 = unit_off[l];
+  const int pl = (int)(l % a.lists_per_slice);
+  const int u = pl % a.max_pages;
+  const int b = (pl / a.max_pages) % a.num_seqs;
+  PageUnit w;
+  w.g = pl / (a.max_pages * a.num_seqs);
+  w.phys = a.page_table[b * a.pt_stride + u];
+  PageUnit *units = (PageUnit *)(a.ws + a.lay.units) + u0;
+  const int32_t nu = (n + a.chunk - 1) / a.chunk;  // the list's entries split evenly
+  for (int32_t c = 0; c < nu; ++c) {
+    const int32_t b0 = (int32_t)((int64_t)c * n / nu), b1 = (int32_t)((int64_t)(c + 1) * n / nu);
+    w.e_begin = lo + b0;
+    w.e_count = b1 - b0;
+    units[c] = w;
+  }
+}
+
+// Blocks [0, fill_blocks): one (token, KV head) row per thread, its entries
+// into the lists; the blocks after them: one list per thread, its units.
+__global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a, int fill_blocks) {
+  if ((int)blockIdx.x >= fill_blocks) {
+    write_units(a, (int64_t)(blockIdx.x - fill_blocks) * kPlanThreads + threadIdx.x);
+    return;
+  }
   const int64_t idx = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
   if (idx >= (int64_t)a.total_q * a.Hkv) return;
   const int r = (int)(idx / a.Hkv), g = (int)(idx - (int64_t)r * a.Hkv);
@@ -407,9 +540,10 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
     const int nt = (int)((L + kScanTile - 1) / kScanTile);
     plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
     plan_scan_top<<<1, kScanThreads, 0, s>>>(a, nt);
-    plan_scan_add<<<nt - 1, kScanThreads, 0, s>>>(a);
+    plan_scan_add<<<nt, kScanThreads, 0, s>>>(a);
   }
-  if (blocks) plan_fill<<<blocks, kPlanThreads, 0, s>>>(a);
+  const int64_t list_blocks = (L + kPlanThreads - 1) / kPlanThreads;
+  plan_fill<<<(unsigned)(blocks + list_blocks), kPlanThreads, 0, s>>>(a, (int)blocks);
   return hipGetLastError();
 }
 
