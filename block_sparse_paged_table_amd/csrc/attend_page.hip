@@ -443,6 +443,23 @@ __global__ void __launch_bounds__(THREADS, (Geom<ROUTE, D>::LDS <= 53 * 1024 ? 3
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (Gm::QB == 1 && Gm::LANE_CH == 2) {
+      // FP8 rows of 128: a lane's 32 bytes of each K row against its 32 bytes
+      // of the Q row, one K = 128 MFMA per key tile; the fragments of four
+      // key tiles are read before their MFMAs
+#pragma unroll
+      for (int t0 = 0; t0 < NT; t0 += 4) {
+        u32x4 kf[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            kf[t][c] = *(const u32x4 *)(sK + k_off<ROUTE, D>(key_of<ROUTE>(t0 + t, n), grp * 2 + c));
+        if constexpr (kPipelineLds) __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t0 + t] = mfma_fp8_k128(kf[t][0], kf[t][1], qb[J][0], qb[J][1], acc[t0 + t]);
+      }
+    } else
 #pragma unroll
     for (int c = 0; c < Gm::LANE_CH; ++c) {
       // all of this chunk's K fragments are read before its MFMAs (the empty

@@ -42,6 +42,18 @@ __device__ __forceinline__ f32x4 mfma_fp8(u32x2 a, u32x2 b, f32x4 c) {
                                                     __builtin_bit_cast(long, b), c, 0, 0, 0);
 }
 
+// FP8 x FP8 over K = 128 (gfx950 v_mfma_f32_16x16x128_f8f6f4; E4M3 both
+// sides, no block scales): each lane brings 32 bytes of its A row and 32
+// bytes of its B column.  The contraction pairs byte j of lane (m, group)
+// with byte j of lane (n, group), so any placement of the K elements that A
+// and B share gives the full dot product.
+__device__ __forceinline__ f32x4 mfma_fp8_k128(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

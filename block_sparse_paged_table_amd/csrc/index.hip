@@ -3,8 +3,8 @@
 // the page's max -- for every (query, head) row, then a top-k over the row),
 // written for gfx950.
 //
-// k_index_scores: one workgroup per (128 query tokens, head, chunk of 16
-// logical pages).  The 128 Q rows live in registers (16 per wave); each page
+// k_index_scores: one workgroup per (64 query tokens, head, chunk of 16
+// logical pages).  The 64 Q rows live in registers (16 per wave); each page
 // of the chunk that some row of the tile can see is copied into LDS
 // (double-buffered, the next page's loads in flight while the current one is
 // scored), and every wave computes S^T = K Q^T for its 16 rows with FP8 MFMA
@@ -22,7 +22,11 @@
 namespace msa {
 namespace {
 
-constexpr int ITQ_WAVES = 8;  // waves per workgroup (16 query rows each)
+// 4 waves per workgroup (64 query tokens): against 8, each page load is
+// shared by half the rows, but twice as many workgroups share the GPU and
+// four fit on a CU (0.133 vs 0.145 ms on the 16K-token, 2-head workload;
+// 16-page chunks, as 32, beat 8 and 4)
+constexpr int ITQ_WAVES = 4;  // waves per workgroup (16 query rows each)
 constexpr int IPC = 16;     // logical pages per workgroup
 constexpr int IPAGE = 128;  // tokens per page
 
@@ -182,14 +186,25 @@ __global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a
       f32x4 acc[IPAGE / 16];
 #pragma unroll
       for (int t = 0; t < IPAGE / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < Gm::LANE_CH; ++c)
+      if constexpr (Gm::LANE_CH == 2) {
+        // d = 128: the lane's 32 bytes of a K row against its 32 bytes of the
+        // Q row, one K = 128 MFMA per key tile
 #pragma unroll
         for (int t = 0; t < IPAGE / 16; ++t) {
-          const u32x4 k4 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * Gm::LANE_CH + c));
-          acc[t] = mfma_fp8(u32x2{k4[0], k4[1]}, u32x2{qr[c][0], qr[c][1]}, acc[t]);
-          acc[t] = mfma_fp8(u32x2{k4[2], k4[3]}, u32x2{qr[c][2], qr[c][3]}, acc[t]);
+          const u32x4 k0 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * 2));
+          const u32x4 k1 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * 2 + 1));
+          acc[t] = mfma_fp8_k128(k0, k1, qr[0], qr[1], acc[t]);
         }
+      } else {
+#pragma unroll
+        for (int c = 0; c < Gm::LANE_CH; ++c)
+#pragma unroll
+          for (int t = 0; t < IPAGE / 16; ++t) {
+            const u32x4 k4 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * Gm::LANE_CH + c));
+            acc[t] = mfma_fp8(u32x2{k4[0], k4[1]}, u32x2{qr[c][0], qr[c][1]}, acc[t]);
+            acc[t] = mfma_fp8(u32x2{k4[2], k4[3]}, u32x2{qr[c][2], qr[c][3]}, acc[t]);
+          }
+      }
       // ---- max over the keys this row sees
       const int jabs = j0 + jj;
       const int vis_to = (my_b == cb) ? my_last - jabs * IPAGE : -1;  // last visible in-page key
