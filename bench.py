@@ -238,6 +238,8 @@ def main():
                          "combine reads in order) or [split][row][d]")
     ap.add_argument("--index", action="store_true",
                     help="time the paged prefill indexer (page scores + top-k) instead")
+    ap.add_argument("--index-workload", choices=["16k", "short_batch"], default="16k",
+                    help="indexer workload: the 16K-token request, or 8 short chunks over long contexts")
     ap.add_argument("--workload", choices=["page4_small_chunk"], default=None,
                     help="a named workload instead of --config (page4_small_chunk: 48 rows, "
                          "512 microblocks per row in splits, the split-k microblock route)")
@@ -464,7 +466,10 @@ def bench_index(args):
     from block_sparse_paged_table_amd.runner import DeviceIndexProblem
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    ips = [synth.make_index_problem(seed=2000 + 100 * i) for i in range(args.sets)]
+    if args.index_workload == "short_batch":
+        ips = [synth.make_index_short_batch(seed=2004 + 100 * i) for i in range(args.sets)]
+    else:
+        ips = [synth.make_index_problem(seed=2000 + 100 * i) for i in range(args.sets)]
     devs = [DeviceIndexProblem(ip) for ip in ips]
     ip = ips[0]
     for i in range(args.warmup):

@@ -4,7 +4,7 @@
 // written for gfx950.
 //
 // k_index_scores: one workgroup per (64 query tokens, head, chunk of 16
-// logical pages).  The 64 Q rows live in registers (16 per wave); each page
+// logical pages, or 8 or 4 when that grid would not fill the GPU).  The 64 Q rows live in registers (16 per wave); each page
 // of the chunk that some row of the tile can see is copied into LDS
 // (double-buffered, the next page's loads in flight while the current one is
 // scored), and every wave computes S^T = K Q^T for its 16 rows with FP8 MFMA
@@ -27,7 +27,16 @@ namespace {
 // four fit on a CU (0.133 vs 0.145 ms on the 16K-token, 2-head workload;
 // 16-page chunks, as 32, beat 8 and 4)
 constexpr int ITQ_WAVES = 4;  // waves per workgroup (16 query rows each)
-constexpr int IPC = 16;     // logical pages per workgroup
+// Logical pages per workgroup (PC): 16 where the grid is large; halved, down
+// to 4, while the grid has fewer than kIndexMinWorkgroups workgroups, so
+// that a few short chunks over long contexts still fill the GPU
+// (vllm-project/MSA PR 36, "Changes": the page chunk adapts to the batch).
+// Measured: 16 pages beat 8 and 4 on the 16K-token request (0.133 vs 0.158 /
+// 0.215 ms) and on 8 chunks of 64..512 tokens (0.128 vs 0.144 / 0.184 ms);
+// on two chunks of 64 and 40 tokens over 90K..120K contexts 4 pages win
+// (0.0285 vs 0.0328 ms).
+constexpr int kIndexPageChunks[] = {16, 8, 4};
+constexpr int64_t kIndexMinWorkgroups = 2048;  // two per resident slot (4 per CU, 256 CUs)
 constexpr int IPAGE = 128;  // tokens per page
 
 template <int D> struct IGeom {
@@ -71,7 +80,7 @@ __device__ __forceinline__ void store_kpage(uint8_t *sk, const u32x4 *r) {
   }
 }
 
-template <int D>
+template <int D, int IPC>
 __global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a) {
   using Gm = IGeom<D>;
   constexpr int IT = Gm::IT, ITQ = Gm::ITQ;
@@ -390,26 +399,46 @@ __global__ void k_index_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
 
-// Static LDS of k_index_scores<D> (its __shared__ arrays).
-template <int D> constexpr size_t index_scores_lds() {
+// Static LDS of k_index_scores<D, IPC> (its __shared__ arrays).
+template <int D, int IPC> constexpr size_t index_scores_lds() {
   using Gm = IGeom<D>;
   return 2 * (size_t)Gm::PAGE_BYTES + (size_t)Gm::ITQ * (IPC + 1) * 4 + 4 * (size_t)Gm::ITQ * 4 + 4 * 4;
 }
 
 size_t index_lds_bytes() {
-  return index_scores_lds<128>() > index_scores_lds<64>() ? index_scores_lds<128>() : index_scores_lds<64>();
+  // the largest page chunk holds the most scores
+  constexpr int pc = kIndexPageChunks[0];
+  return index_scores_lds<128, pc>() > index_scores_lds<64, pc>() ? index_scores_lds<128, pc>()
+                                                                   : index_scores_lds<64, pc>();
 }
+
+namespace {
+template <int D, int IPC>
+hipError_t launch_scores(const IndexArgs &a, int64_t tiles, hipStream_t s) {
+  dim3 grid((unsigned)tiles, (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
+  k_index_scores<D, IPC><<<grid, IGeom<D>::IT, 0, s>>>(a);
+  return hipGetLastError();
+}
+template <int D>
+hipError_t launch_scores_d(const IndexArgs &a, hipStream_t s) {
+  const int64_t tiles = (a.total_q + IGeom<D>::ITQ - 1) / IGeom<D>::ITQ;
+  int pc = kIndexPageChunks[0];
+  for (int c : kIndexPageChunks) {
+    pc = c;
+    if (tiles * a.H * ((a.max_pages + c - 1) / c) >= kIndexMinWorkgroups) break;
+  }
+  switch (pc) {
+    case 16: return launch_scores<D, 16>(a, tiles, s);
+    case 8: return launch_scores<D, 8>(a, tiles, s);
+    default: return launch_scores<D, 4>(a, tiles, s);
+  }
+}
+}  // namespace
 
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t s) {
   if (a.err_flags) k_index_zero<<<1, 1, 0, s>>>(a.err_flags);
   if (a.total_q == 0) return hipGetLastError();
-  const int itq = a.D == 64 ? IGeom<64>::ITQ : IGeom<128>::ITQ;
-  dim3 grid((unsigned)((a.total_q + itq - 1) / itq), (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
-  if (a.D == 64)
-    k_index_scores<64><<<grid, IGeom<64>::IT, 0, s>>>(a);
-  else
-    k_index_scores<128><<<grid, IGeom<128>::IT, 0, s>>>(a);
-  return hipGetLastError();
+  return a.D == 64 ? launch_scores_d<64>(a, s) : launch_scores_d<128>(a, s);
 }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {

@@ -386,6 +386,21 @@ def make_index_problem(seed: int = 2000) -> IndexProblem:
         description="1 x 16384 tokens, page 128, 2 indexer heads, d 128, E4M3 Q and cache, top 16 pages")
 
 
+def make_index_short_batch(seed: int = 2004) -> IndexProblem:
+    """The indexer on a batch of short chunks over long contexts (the shape
+    the adaptive page chunk is for): 8 requests, chunks in {64, 128, 256,
+    512}, cached contexts uniform in 16K..128K tokens, 2 heads of dim 128,
+    16 pages kept.  Request shapes come from a fixed shape seed."""
+    rng = np.random.default_rng(1104)
+    chunks = rng.choice([64, 128, 256, 512], size=8)
+    ctx = rng.integers(16384, 131072, size=8, endpoint=True)
+    return build_index_problem(
+        name="index_short_batch", seed=seed, ctx_lens=[int(c) for c in ctx],
+        chunk_lens=[int(c) for c in chunks], page_size=128, H=2, d=128, top_k=16, page_bias=1.0,
+        description="8 requests, chunks in {64..512}, context U[16K,128K], page 128, 2 indexer "
+                    "heads, d 128, E4M3 Q and cache, top 16 pages")
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------

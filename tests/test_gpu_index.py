@@ -214,6 +214,36 @@ def test_index_full_size_sampled():
     assert exact > len(toks)   # most rows are uniquely determined
 
 
+def _page_chunk(ip):
+    """The page chunk the library picks: 16 pages per workgroup, halved (to 4
+    at least) while the grid of (64-token tile, head, chunk) workgroups holds
+    fewer than 2048."""
+    tiles = -(-ip.total_q // 64)
+    for pc in (16, 8, 4):
+        if tiles * ip.H * -(-ip.max_pages // pc) >= 2048:
+            return pc
+    return 4
+
+
+@pytest.mark.parametrize("geo,pc", [
+    (dict(ctx_lens=[8192], chunk_lens=[8192]), 16),
+    (dict(ctx_lens=[12288], chunk_lens=[4096]), 8),
+    (dict(ctx_lens=[30000, 60000, 0], chunk_lens=[64, 100, 30]), 4),
+])
+def test_index_page_chunk_forms(geo, pc):
+    """Each page-chunk form of the scores kernel, on a workload that selects
+    it; sampled rows (the first and last tiles and a spread between)."""
+    ip = _small(47, H=2, d=128, top_k=16, pad_rows=3, **geo)
+    assert _page_chunk(ip) == pc
+    dev = DeviceIndexProblem(ip)
+    dev.run()
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([np.arange(0, min(80, ip.total_q)),
+                                     np.linspace(0, ip.total_q - 1, 120).astype(int),
+                                     np.arange(max(0, ip.total_q - 80), ip.total_q)]))
+    _check(ip, dev, toks)
+
+
 def test_indexer_selections_drive_the_attention():
     """End to end: the GPU indexer's selections are the attention's sel_idx /
     sel_mask (one indexer head per KV head); the attention on them matches
