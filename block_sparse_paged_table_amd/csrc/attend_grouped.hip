@@ -9,32 +9,37 @@
 // planner lists each split's units in ascending order, so the groups an XCD
 // runs together walk the K/V cache in step and mostly hit its L2.
 //
-// The workgroup first copies its split's unit list (8 bytes per unit: page,
-// unit in the page, mask) into LDS.  The units then stream through an LDS
-// ring of NST stages of 16 keys (4 units) each, loaded straight from the
-// cache into LDS (global_load_lds: no register staging, no LDS stores): wave
-// w loads unit w of a stage, its K rows then its V rows.  Loads run NST - 1
-// stages ahead of the stage being computed, and one barrier per stage both
+// The split's unit list (8 bytes per unit: page, unit in the page, mask)
+// streams into an LDS ring of two chunks of 256 entries (32 stages each), a
+// chunk loaded 32 stages before its first use.  The units stream through an
+// LDS ring of NST stages of 32 keys (8 units) each -- two 16-key tiles, A
+// and B -- loaded straight from the cache into LDS (global_load_lds: no
+// register staging, no LDS stores): wave w loads unit w of tile A and unit
+// w of tile B, each its K rows then its V rows.  Loads run NST - 1 stages
+// ahead of the stage being computed, and one barrier per stage both
 // publishes a landed stage and frees the slot the next loads reuse.  Inside
 // the loop the only memory accesses are these counted loads and LDS
 // traffic: a scalar or vector load there would make every later wait also
-// wait for the loads in flight.  K rows are stored as they are in the cache with a per-row XOR
-// swizzle of their 16-byte chunks (the 16 rows of one MFMA read fall in 16
-// different bank groups); V rows likewise, read back transposed.  Per stage
-// and active tile:
+// wait for the loads in flight.  At head_dim 256 two 32 KiB stages and the
+// 4 KiB list ring make 68 KiB of LDS (two workgroups per CU); against
+// 16-key stages with the same 32 keys in flight, a stage costs half the
+// barriers and softmax steps per key.  K rows are stored as they are in the
+// cache with a per-row XOR swizzle of their 16-byte chunks (the 16 rows of
+// one MFMA read fall in 16 different bank groups); V rows likewise, read
+// back transposed.  Per stage and active row tile:
 //
-//   S^T = K . Q^T      f16 MFMA 16x16x32, FP32 accumulate (K rows from LDS,
-//                      Q rows held in registers)
+//   S^T = K . Q^T      f16 MFMA 16x16x32 per 16-key tile, FP32 accumulate
+//                      (K rows from LDS, Q rows held in registers)
 //   mask               key i of unit b is visible to the row of token tau iff
 //                      bit 4*tau + i of the unit's mask word is set (the
 //                      planner folded the causal and tail rules into it)
-//   online softmax     running max / sums per row, rescaling O when the max
-//                      grows
-//   O^T += V^T . P^T   f16 MFMA 16x16x16: the V^T operand comes from the
-//                      untransposed V rows through the gfx950 transposing LDS
-//                      read (ds_read_b64_tr_b16), and the S^T accumulator of
-//                      a lane already holds its P^T operand (keys 4q..4q+3 of
-//                      its row)
+//   online softmax     running max / sums per row over the 32 keys,
+//                      rescaling O when the max grows
+//   O^T += V^T . P^T   f16 MFMA 16x16x32 over both tiles: the V^T operand
+//                      comes from the untransposed V rows through the gfx950
+//                      transposing LDS read (ds_read_b64_tr_b16), and the S^T
+//                      accumulators of a lane already hold its P^T operand
+//                      (keys 4q..4q+3 of each tile, of its row)
 //
 // A tile none of whose rows selected any unit of a stage skips it.  Each
 // split is an independent softmax: partial_o = O / l * v_scale and lse =
@@ -49,33 +54,37 @@ namespace {
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int GT = 256;             // threads per workgroup
-constexpr int SK = 16;              // keys per stage
-constexpr int UPS = SK / 4;         // units per stage = waves per workgroup
-static_assert(UPS * kWave == GT, "one unit per wave and stage");
+constexpr int SK = 32;              // keys per stage: two 16-key tiles A and B
+constexpr int UPS = SK / 4;         // units per stage: wave w loads units w (tile A) and w + 4 (tile B)
+static_assert(UPS == 2 * (GT / kWave), "two units per wave and stage");
 
 typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kListCap = kGroupTokens * 512;  // units a group's split may hold
+constexpr int kListChunk = 256;                // list entries per ring chunk
+constexpr int kChunkStages = kListChunk / UPS;  // stages one chunk covers
+constexpr int kListRing = 2 * kListChunk;       // entries the LDS ring holds
 
 template <int D> struct GGeom {
   static constexpr int RB = D * 2;                  // K / V row bytes (FP16)
   static constexpr int CPR = RB / 16;               // 16-byte chunks per row
   static constexpr int LANE_CH = CPR / 4;           // chunks of a Q/K row one lane holds
   static constexpr int K_BYTES = SK * RB;           // one stage's K rows
+  static constexpr int TILE_B = 16 * RB;            // tile B's rows follow tile A's (K and V)
   static constexpr int STAGE = 2 * K_BYTES;         // K rows, then V rows
-  static constexpr int NST = D == 256 ? 3 : 4;      // ring stages
+  static constexpr int NST = D == 256 ? 2 : 3;      // ring stages
   static constexpr int RING = NST * STAGE;
-  static constexpr int LDS = RING + kListCap * 8;   // ring + the split's unit list
+  static constexpr int LDS = RING + kListRing * 8;  // K/V ring + list ring
+  static constexpr int WGS = LDS <= 53 * 1024 ? 3 : 2;  // workgroups per CU
   static constexpr int ROWS_PER_LOAD = 1024 / RB;   // rows one 1 KiB wave load covers
   static constexpr int LPP = 4 / ROWS_PER_LOAD;     // wave loads per unit and part (K or V)
-  static constexpr int LOADS = 2 * LPP;             // wave loads per stage
+  static constexpr int ULOADS = 2 * LPP;            // wave loads per unit (K and V rows)
   static constexpr int MT = D / 16;
   static_assert(ROWS_PER_LOAD * RB == 1024 && LPP >= 1, "head_dim 128 or 256");
-  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
+  static_assert(WGS * LDS <= 160 * 1024, "workgroups per CU");
 };
 
-// Byte offset of 16-byte chunk c of K row r (r < 16) / V row r in a stage.
+// Byte offset of 16-byte chunk c of K row r (r < 32) / V row r in a stage.
 template <int D> __device__ __forceinline__ int gk_off(int r, int c) {
   return r * GGeom<D>::RB + ((c ^ (r & 15)) << 4);
 }
@@ -115,8 +124,8 @@ __device__ __forceinline__ void stage_barrier() {
 
 // Per-lane constants of the stage loop, computed once.
 template <int D> struct LaneOffsets {
-  uint32_t k[GGeom<D>::LANE_CH];  // K fragment c of row n (QK operand), from the slot
-  uint32_t v[8];                  // V^T fragment of dims tile mt (mt & 7; +256 B for mt >= 8)
+  uint32_t k[GGeom<D>::LANE_CH];  // K fragment c of row n of tile A (QK operand), from the slot
+  uint32_t v[8];                  // tile A's V^T fragment of dims tile mt (mt & 7; +256 B for mt >= 8)
   uint32_t dk[GGeom<D>::LPP];     // DMA source offsets in the unit, K rows
   uint32_t dv[GGeom<D>::LPP];     //   and V rows
 };
@@ -144,19 +153,20 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(const GroupArgs &a, int w
   return L;
 }
 
-// Issue this wave's part of one stage: the K and V rows of the unit at byte
-// offset `uoff` of the caches, straight into the stage's LDS slot.  A unit
-// past the end of the run is zero-filled instead (its mask is 0, so it adds
-// nothing; zeros keep the masked products finite).
+// Issue this wave's part of one stage: unit `ua` into tile A's rows 4w ..
+// 4w+3 and unit `ub` into tile B's (K rows, then V rows), straight into the
+// stage's LDS slot from their byte offsets in the caches.  A unit past the
+// end of the run is zero-filled instead (its mask is 0, so it adds nothing;
+// zeros keep the masked products finite) and issues no load.
 template <int D>
-__device__ __forceinline__ void issue_stage(const GroupArgs &a, uint8_t *slot, int w, int64_t uoff, bool real,
-                                            const LaneOffsets<D> &L) {
+__device__ __forceinline__ void issue_unit(const GroupArgs &a, uint8_t *slot, int row0, int64_t uoff, bool real,
+                                           const LaneOffsets<D> &L) {
   using Gm = GGeom<D>;
   const int lane = threadIdx.x & 63;
   if (!real) {
 #pragma unroll
     for (int h = 0; h < Gm::LPP; ++h) {
-      const int r0 = w * 4 + h * Gm::ROWS_PER_LOAD;
+      const int r0 = row0 + h * Gm::ROWS_PER_LOAD;
       *(u32x4 *)(slot + r0 * Gm::RB + lane * 16) = u32x4{0u, 0u, 0u, 0u};
       *(u32x4 *)(slot + Gm::K_BYTES + r0 * Gm::RB + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
@@ -167,10 +177,23 @@ __device__ __forceinline__ void issue_stage(const GroupArgs &a, uint8_t *slot, i
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t *)slot);
 #pragma unroll
   for (int h = 0; h < Gm::LPP; ++h)
-    lds_dma16(kb, L.dk[h], lds + (w * 4 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
+    lds_dma16(kb, L.dk[h], lds + (row0 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
 #pragma unroll
   for (int h = 0; h < Gm::LPP; ++h)
-    lds_dma16(vb, L.dv[h], lds + Gm::K_BYTES + (w * 4 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
+    lds_dma16(vb, L.dv[h], lds + Gm::K_BYTES + (row0 + h * Gm::ROWS_PER_LOAD) * Gm::RB);
+}
+
+// Chunk c of a list into LDS ring slot c % 2: entries 256 c .. 256 c + 255
+// from `list` (16-byte aligned), of which the first n are wanted.  Wave w
+// loads entries 64 w .. 64 w + 63 of the chunk, two per lane on lanes 0..31
+// (16 bytes each; lanes whose first entry is not wanted load nothing).
+// Counted with the stage loads of the wave (vmcnt).
+__device__ __forceinline__ void issue_list_chunk(const uint2 *list, int n, int c, int w, uint2 *sList) {
+  const int lane = threadIdx.x & 63;
+  const int e = c * kListChunk + w * 64 + 2 * lane;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(LDS_AS uint8_t *)(sList + (c & 1) * kListChunk + w * 64));
+  if (lane < 32 && e < n) lds_dma16((const uint8_t *)list, (uint32_t)e * 8u, lds);
 }
 
 // A row's running max may lag its true max by up to 2^kLag (log2 units)
@@ -181,12 +204,13 @@ constexpr float kLag = 8.0f;
 
 // PO: dtype of partial_o (MSA_F32, MSA_BF16 or MSA_F16).
 template <int D, int PO>
-__global__ void __launch_bounds__(GT, 2)
+__global__ void __launch_bounds__(GT, GGeom<D>::WGS)
     k_grouped_attend(const GroupArgs a, const uint2 *__restrict__ lists, const int *__restrict__ split_offs) {
   using Gm = GGeom<D>;
   constexpr int MT = Gm::MT, NST = Gm::NST;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Gm::RING];
-  __shared__ uint2 sList[kListCap];  // the split's units: {page << 5 | unit in page, mask32}
+  // ring of the split's units: {page << 5 | unit in page, mask32}; unit u at u % kListRing
+  __shared__ __attribute__((aligned(16))) uint2 sList[kListRing];
 
   // ---- work item; consecutive groups on one XCD (workgroups are dealt to
   // the 8 XCDs round-robin, and the grid's x size is a multiple of 8)
@@ -198,7 +222,12 @@ __global__ void __launch_bounds__(GT, 2)
   const int *soff = split_offs + li * (a.num_splits + 1) + split;
   const int first = soff[0];
   const int count = soff[1] - first;
-  const uint2 *list = lists + li * a.list_cap + first;
+  // the list from the even entry at or before `first` (16-byte pairs): unit
+  // u of the split is entry u + par of that run and sits at ring index
+  // (u + par) % kListRing
+  const int par = first & 1;
+  const uint2 *list = lists + li * a.list_cap + (first - par);
+  const int nlist = count + par;
   const int nst = (count + UPS - 1) / UPS;  // stages
 
   const int lane = threadIdx.x & 63;
@@ -231,27 +260,16 @@ __global__ void __launch_bounds__(GT, 2)
   // list entry, wave-uniform)
   const int64_t head_off = (int64_t)g * a.kv_stride_head;
   auto unit_off = [&](int u) {
-    const uint32_t e = __builtin_amdgcn_readfirstlane(sList[u].x);
+    const uint32_t e = __builtin_amdgcn_readfirstlane(sList[(u + par) % kListRing].x);
     return (int64_t)(e >> 5) * a.kv_stride_page + (int64_t)((e & 31u) * 4) * a.kv_stride_tok + head_off;
   };
 
-  // ---- prologue: the run's list into LDS, Q into registers, then the
-  // first NST - 1 stages in flight.  The loop below issues no memory access
-  // but the counted K/V loads, LDS traffic and its output stores.
-  {  // every load first, then the stores (one round trip, not one per entry)
-    constexpr int PER = kListCap / GT;
-    uint2 e[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = threadIdx.x + k * GT;
-      if (i < count) e[k] = list[i];
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = threadIdx.x + k * GT;
-      if (i < count) sList[i] = e[k];
-    }
-  }
+  // ---- prologue: the list's first two chunks into LDS, Q into registers,
+  // then the first NST - 1 stages in flight.  The loop below issues no memory
+  // access but the counted K/V and list loads, LDS traffic and its output
+  // stores.
+  issue_list_chunk(list, nlist, 0, wave, sList);
+  issue_list_chunk(list, nlist, 1, wave, sList);
   u32x4 qreg[Gm::LANE_CH];
   {
     const uint8_t *qp = (const uint8_t *)a.q +
@@ -264,67 +282,87 @@ __global__ void __launch_bounds__(GT, 2)
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f, lp = 0.0f;
   const float sc = a.scale_log2;
-  wait_vm_lgkm0<0>();  // Q and the list, read and stored
+  wait_vm_lgkm0<0>();  // Q and the list's first chunks landed
   stage_barrier();
+  // this wave's part of stage s: units UPS s + wave (tile A) and + 4 (tile B)
+  auto issue_stage = [&](uint8_t *slot, int s) {
+    const int ua = UPS * s + wave, ub = ua + 4;
+    issue_unit<D>(a, slot, wave * 4, ua < count ? unit_off(ua) : 0, ua < count, L);
+    issue_unit<D>(a, slot, 16 + wave * 4, ub < count ? unit_off(ub) : 0, ub < count, L);
+  };
+  // loads this wave issues for stage s (units past the run issue none)
+  auto loads_of = [&](int s) {
+    const int ua = UPS * s + wave;
+    return s < nst ? ((ua < count ? Gm::ULOADS : 0) + (ua + 4 < count ? Gm::ULOADS : 0)) : 0;
+  };
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) {
-    const int u = UPS * s + wave;
-    if (s < nst) issue_stage<D>(a, smem + s * Gm::STAGE, wave, u < count ? unit_off(u) : 0, u < count, L);
-  }
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nst) issue_stage(smem + s * Gm::STAGE, s);
 
   // One stage: J (compile time) is its ring slot.
   auto stage = [&](auto J_, const int beta) {
 #pragma clang fp contract(off)
     constexpr int J = decltype(J_)::value;
-    // loads this wave issued after stage beta's: stages beta+1 .. beta+NST-2
-    // that exist and hold a real unit of this wave (loads retire in order)
+    // loads this wave issued after stage beta's: those of stages beta+1 ..
+    // beta+NST-2 (loads retire in order)
     int newer = 0;
 #pragma unroll
-    for (int s = 1; s <= NST - 2; ++s)
-      newer += (beta + s < nst && UPS * (beta + s) + wave < count) ? Gm::LOADS : 0;
-    if (newer == 0) wait_vm_lgkm0<0>();
-    else if (newer == Gm::LOADS) wait_vm_lgkm0<Gm::LOADS>();
-    else wait_vm_lgkm0<2 * Gm::LOADS>();
+    for (int s = 1; s <= NST - 2; ++s) newer += loads_of(beta + s);
+    if constexpr (NST == 2) {
+      wait_vm_lgkm0<0>();
+    } else {
+      static_assert(NST == 3, "waits written for two and three stages");
+      if (newer == 0) wait_vm_lgkm0<0>();
+      else if (newer == Gm::ULOADS) wait_vm_lgkm0<Gm::ULOADS>();
+      else wait_vm_lgkm0<2 * Gm::ULOADS>();
+    }
     stage_barrier();  // stage beta landed for every wave; slot of beta - 1 free
-    {
-      const int s = beta + NST - 1, u = UPS * s + wave;
-      if (s < nst)
-        issue_stage<D>(a, smem + ((J + NST - 1) % NST) * Gm::STAGE, wave, u < count ? unit_off(u) : 0,
-                       u < count, L);
+    if (beta + NST - 1 < nst) issue_stage(smem + ((J + NST - 1) % NST) * Gm::STAGE, beta + NST - 1);
+    // List chunk c >= 2 goes into the slot chunk c - 2 held, free since this
+    // stage's barrier (chunk c - 2's last units are those of stage
+    // 64 (c - 1) - 1 at the latest); it is first read about 64 - NST stages
+    // later, long after the stage waits have covered it (loads retire in
+    // order, and it is older than the stage loads issued from the next stage
+    // on).  These loads are not in `newer`: a wait that leaves one of them out
+    // only waits for one load more than it needs.
+    if (beta >= kChunkStages + 1 && (beta - 1) % kChunkStages == 0) {
+      const int c = (beta - 1) / kChunkStages + 1;
+      if (c * kListChunk < nlist) issue_list_chunk(list, nlist, c, wave, sList);
     }
     const uint8_t *st = smem + J * Gm::STAGE;
-    // this lane group's unit of the stage, and whether any unit of the stage
-    // has a token of this wave's tile
-    const int ug = UPS * beta + gq;
-    const uint32_t mask = ug < count ? sList[ug].y : 0u;
-    if (!has_tile || !__any((mask & tilemask) != 0u)) return;
-    // ---- every LDS operand of the stage is requested up front: the K
-    // fragments of S^T = K Q^T and the V^T fragments of the PV product (lane n
-    // receives V rows 4gq .. 4gq+3 at dim 16 mt + n), so the PV products can
-    // start as soon as P is ready
-    u32x4 kf[Gm::LANE_CH];
+    // this lane group's units of the stage (gq of tile A, 4 + gq of tile B),
+    // and whether any unit of the stage has a token of this wave's tile
+    const int ua = UPS * beta + gq, ub = ua + 4;
+    const uint32_t mask_a = ua < count ? sList[(ua + par) % kListRing].y : 0u;
+    const uint32_t mask_b = ub < count ? sList[(ub + par) % kListRing].y : 0u;
+    if (!has_tile || !__any(((mask_a | mask_b) & tilemask) != 0u)) return;
+    // ---- S^T for the stage's 32 keys, tile A then tile B (lane: keys
+    // 4gq..4gq+3 of each tile, row n), each contraction over four
+    // accumulators; a tile's K fragments are all requested before its MFMAs
+    auto qk_tile = [&](const uint8_t *tb) {
+      u32x4 kf[Gm::LANE_CH];
 #pragma unroll
-    for (int c = 0; c < Gm::LANE_CH; ++c) kf[c] = *(const u32x4 *)(st + L.k[c]);
-    i16x4 vt[MT];
+      for (int c = 0; c < Gm::LANE_CH; ++c) kf[c] = *(const u32x4 *)(tb + L.k[c]);
+      __asm__ volatile("" ::: "memory");
+      f32x4 ac[4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      vt[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(st + L.v[mt & 7] + (mt & 8) * 32));
-    __asm__ volatile("" ::: "memory");
-    // ---- S^T for the stage's 16 keys (lane: keys 4gq..4gq+3 of row n), the
-    // contraction split over four accumulators to shorten the chain of
-    // dependent products
-    f32x4 ac[4];
+      for (int k = 0; k < 4; ++k) ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < Gm::LANE_CH; ++c) ac[c & 3] = mfma_f16(kf[c], qreg[c], ac[c & 3]);
+      return (ac[0] + ac[1]) + (ac[2] + ac[3]);
+    };
+    const f32x4 acc_a = qk_tile(st);
+    const f32x4 acc_b = qk_tile(st + Gm::TILE_B);
+    // ---- exact masks: key i of this lane group's unit in each tile
+    const uint32_t bits_a = active ? (mask_a >> mshift) & 0xfu : 0u;
+    const uint32_t bits_b = active ? (mask_b >> mshift) & 0xfu : 0u;
+    float x[8];
 #pragma unroll
-    for (int c = 0; c < Gm::LANE_CH; ++c) ac[c & 3] = mfma_f16(kf[c], qreg[c], ac[c & 3]);
-    const f32x4 acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
-    // ---- exact masks: key i of this lane group's unit gq
-    const uint32_t bits = active ? (mask >> mshift) & 0xfu : 0u;
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = ((bits >> i) & 1u) ? acc[i] * sc : -INFINITY;
-    float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    for (int i = 0; i < 4; ++i) {
+      x[i] = ((bits_a >> i) & 1u) ? acc_a[i] * sc : -INFINITY;
+      x[4 + i] = ((bits_b >> i) & 1u) ? acc_b[i] * sc : -INFINITY;
+    }
+    float mb = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mb = quarter_reduce<true>(mb);
     // ---- raise the running max only when a logit passes it by kLag
     const bool up = mb > m + kLag;  // also when m is still -inf and mb is not
@@ -337,30 +375,41 @@ __global__ void __launch_bounds__(GT, 2)
       m = up ? mb : m;
     }
     // ---- P = 2^(s - m) < 2^kLag (0 for masked keys and for rows with no
-    // key yet), sums, FP16 operand
+    // key yet), sums, FP16 operand: keys 4gq..4gq+3 of tile A, then of tile B
     const float ms = (m == -INFINITY) ? 0.0f : m;
-    float p[4];
+    float pv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(x[i] - ms);
-      l += p[i];
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - ms);
+      l += pv[i];
     }
-    const uint32_t pk0 = pack_f16x2(p[0], p[1]), pk1 = pack_f16x2(p[2], p[3]);
-    lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk0), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
-    lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk1), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
-    const f16x4v pf = __builtin_bit_cast(f16x4v, u32x2{pk0, pk1});
-    // ---- O^T += V^T P^T
+    // (each pair is cast from a scalar: a bit cast of a vector element,
+    // pf[j], was compiled as a cast of element 0)
+    u32x4 pf;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4v, vt[mt]), pf, o[mt], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pair = pack_f16x2(pv[2 * j], pv[2 * j + 1]);
+      pf[j] = pair;
+      lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
+    }
+    // ---- O^T += V^T P^T over the 32 keys (16x16x32: element j of the V^T
+    // operand and of the P^T operand name the same key): lane n receives V
+    // rows 4gq .. 4gq+3 of each tile at dim 16 mt + n
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t vo = L.v[mt & 7] + (mt & 8) * 32;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(st + vo));
+      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(st + Gm::TILE_B + vo));
+      const u32x2 wa = __builtin_bit_cast(u32x2, va), wb = __builtin_bit_cast(u32x2, vb);
+      o[mt] = mfma_f16(u32x4{wa[0], wa[1], wb[0], wb[1]}, pf, o[mt]);
+    }
   };
 
   for (int beta0 = 0; beta0 < nst; beta0 += NST) {
     stage(std::integral_constant<int, 0>{}, beta0);
     if (beta0 + 1 < nst) stage(std::integral_constant<int, 1>{}, beta0 + 1);
-    if (beta0 + 2 < nst) stage(std::integral_constant<int, 2 % NST>{}, beta0 + 2);
-    if constexpr (NST > 3) {
-      if (beta0 + 3 < nst) stage(std::integral_constant<int, 3 % NST>{}, beta0 + 3);
+    if constexpr (NST > 2) {
+      if (beta0 + 2 < nst) stage(std::integral_constant<int, 2 % NST>{}, beta0 + 2);
     }
   }
 
@@ -395,7 +444,8 @@ __global__ void __launch_bounds__(GT, 2)
 size_t grouped_attend_lds_bytes() {
   return (size_t)(GGeom<256>::LDS > GGeom<128>::LDS ? GGeom<256>::LDS : GGeom<128>::LDS);
 }
-static_assert(kListCap >= kGroupTokens * 512, "the list must hold 8 tokens x 512 slots");
+static_assert(kChunkStages > 2 * GGeom<256>::NST + 1 && kChunkStages > 2 * GGeom<128>::NST + 1,
+              "a list chunk is loaded NST stages before its first use");
 
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;

@@ -25,7 +25,9 @@ __host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, in
   L.meta = off;   off = align_up(off + 64 * 4, 256);
   L.split_off = off; off = align_up(off + (size_t)num_lists * (num_splits + 1) * 4, 256);
   L.stage = off;  off = align_up(off + (size_t)num_lists * list_cap * 16, 256);
-  L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 8, 256);
+  // (16 bytes of slack: the attention kernel loads entries in 16-byte pairs,
+  // so the last entry of a list may bring its successor along)
+  L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 8 + 16, 256);
   L.total = off;
   return L;
 }
