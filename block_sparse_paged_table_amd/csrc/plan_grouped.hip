@@ -15,7 +15,9 @@
 //        request:16 | unit:24 | token-in-group:3 | slot:10 | visible bits:4
 //      (bits 41.. | 17.. | 14.. | 4.. | 0..)
 //      (invalid selections sort to the end);
-//   2. bitonic sort of the keys in LDS;
+//   2. bitonic sort of the keys in LDS (or, for one request and one split,
+//      steps 2-4 through a bitmap of the request's units: see
+//      union_by_bitmap);
 //   3. duplicates of a (request, unit, token) beyond the first slot are
 //      dropped and flagged; the first slot of each (request, unit, token)
 //      names its split (slot / slots_per_split); each distinct (split,
@@ -34,6 +36,7 @@ namespace msa {
 namespace {
 
 constexpr uint64_t kInvalidKey = ~0ull;
+constexpr int kBitmapUnits = 65535;  // largest unit count the bitmap pass takes
 
 // Ascending bitonic sort of n = E * blockDim.x keys held in LDS.  Thread t
 // keeps the keys of sorted positions tE .. tE+E-1 in registers: compare-
@@ -189,6 +192,150 @@ __device__ __forceinline__ void bitonic_sort32(uint64_t *k, int n, Narrow narrow
   }
 }
 
+// Exclusive prefix of v over the workgroup's threads, and the total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int &total) {
+  __shared__ int wsum[NT / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();  // wsum free (an earlier scan may still read it)
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    before += k < w ? wsum[k] : 0;
+    total += wsum[k];
+  }
+  return before + x - v;
+}
+
+// The union of a group whose valid rows belong to one request, with one
+// split and units below 2^16 (contexts up to 256K tokens), without sorting: a bitmap of the request's
+// units marks the selected ones, so the union comes out in ascending unit
+// order (the order the sort gives) with a unit's rank = the set bits below
+// it; each (token, unit) ORs its visible bits into the unit's mask word.  A
+// per-token presence bitmap over the ranks catches a token that selected a
+// unit twice: then the kernel falls back to the sort, which applies the
+// first-slot rule (returns false).  Units no row sees (mask 0) are dropped,
+// as by the sort path; the list and split offsets it writes are the same.
+// LDS (the keys array, reused): bitmap and rank bases of ceil(nunits / 32)
+// words each, a mask word per union entry and 8 presence bits per entry.
+template <int NT, int JI>
+__device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64_t (&kr)[kGroupTokens][JI],
+                                                int b0, int nunits, uint2 *out, int *soff, uint32_t &err) {
+  extern __shared__ uint64_t keys[];
+  const int t = threadIdx.x;
+  const int nw = (nunits + 31) >> 5;   // <= 2048
+  const int cap = a.list_cap;          // bound on the union
+  const int pw = (cap + 31) >> 5;      // presence words per token
+  uint32_t *bm = (uint32_t *)keys;
+  uint32_t *pre = bm + nw;
+  uint32_t *msk = pre + nw;
+  uint32_t *pres = msk + cap;
+  for (int e = t; e < nw; e += NT) bm[e] = 0u;
+  for (int e = t; e < cap; e += NT) msk[e] = 0u;
+  for (int e = t; e < kGroupTokens * pw; e += NT) pres[e] = 0u;
+  __syncthreads();
+  // the selected units
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const uint64_t k = kr[tau][i];
+      if (k == kInvalidKey) continue;
+      const uint32_t u = (uint32_t)(k >> 17) & 0xffffffu;
+      atomicOr(&bm[u >> 5], 1u << (u & 31u));
+    }
+  __syncthreads();
+  // rank bases: thread t takes words [t * wpt, t * wpt + wpt)
+  const int wpt = (nw + NT - 1) / NT;
+  const int w0 = min(t * wpt, nw), w1 = min(w0 + wpt, nw);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  int nunion;
+  const int base = block_exclusive_scan<NT>(cnt, nunion);
+  {
+    int run = base;
+    for (int w = w0; w < w1; ++w) {
+      pre[w] = (uint32_t)run;
+      run += __popc(bm[w]);
+    }
+  }
+  __syncthreads();
+  // visible bits per (unit, token); a token meeting a unit twice is a duplicate
+  bool dup = false;
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const uint64_t k = kr[tau][i];
+      if (k == kInvalidKey) continue;
+      const uint32_t u = (uint32_t)(k >> 17) & 0xffffffu;
+      const uint32_t rank = pre[u >> 5] + (uint32_t)__popc(bm[u >> 5] & ((1u << (u & 31u)) - 1u));
+      const uint32_t bit = 1u << (rank & 31u);
+      if (atomicOr(&pres[tau * pw + (rank >> 5)], bit) & bit) dup = true;
+      const uint32_t vis = (uint32_t)k & 0xfu;
+      if (vis) atomicOr(&msk[rank], vis << (4 * tau));
+    }
+  if (__syncthreads_or(dup)) return false;
+  // entries with a visible key, in rank order: thread t's ranks are those of
+  // its words
+  int nz = 0;
+  for (int w = w0; w < w1; ++w) {
+    const int r0 = (int)pre[w], n = __popc(bm[w]);
+    for (int r = r0; r < r0 + n; ++r) nz += msk[r] != 0u;
+  }
+  int total;
+  int o = block_exclusive_scan<NT>(nz, total);
+  const int upp = a.page_size / a.unit_tokens;  // units per page
+  const int32_t *ptrow = a.page_table + (int64_t)max(b0, 0) * a.pt_stride;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bm[w];
+    int r = (int)pre[w];
+    while (bits) {
+      // up to 8 set units at a time: their page-table loads first, then the writes
+      int uu[8], phys[8];
+      uint32_t mm[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uu[q] = -1;
+        if (bits) {
+          const int j = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          uu[q] = w * 32 + j;
+          mm[q] = msk[r++];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) phys[q] = (uu[q] >= 0 && mm[q] != 0u) ? ptrow[uu[q] / upp] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (uu[q] < 0 || mm[q] == 0u) continue;
+        uint2 e;
+        if (phys[q] < 0 || phys[q] >= a.num_phys_pages) {
+          err |= MSA_ERRF_PHYS_RANGE;
+          e = make_uint2(0u, 0u);  // mask 0: contributes nothing
+        } else {
+          e = make_uint2(((uint32_t)phys[q] << 5) | (uint32_t)(uu[q] % upp), mm[q]);
+        }
+        out[o++] = e;
+      }
+    }
+  }
+  if (t == 0) {
+    soff[0] = 0;
+    soff[1] = total;
+  }
+  return true;
+}
+
 template <int NT>
 __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   extern __shared__ uint64_t keys[];  // npow2 + NT entries
@@ -226,14 +373,17 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     const int bc = min(max(b_t[tau], 0), a.num_seqs - 1);
     last_t[tau] = min(pos_t[tau], a.seq_lens[bc] - 1);
   }
-  for (int e = kGroupTokens * K + threadIdx.x; e < npow2; e += NT) keys[e] = kInvalidKey;
+  uint64_t kr[kGroupTokens][JI];  // this thread's keys (invalid past slot K)
 #pragma unroll
   for (int tau = 0; tau < kGroupTokens; ++tau)
 #pragma unroll
     for (int i = 0; i < JI; ++i) {
       const int j = threadIdx.x + i * NT;
-      if (j >= K) continue;
       uint64_t key = kInvalidKey;
+      if (j >= K) {
+        kr[tau][i] = key;
+        continue;
+      }
       if (pos_t[tau] >= 0 && mk[tau][i] != 0) {
         const int b = b_t[tau], u = ui[tau][i];
         if (b < 0 || b >= a.num_seqs) {
@@ -246,10 +396,9 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
           const uint32_t vis = mk[tau][i] & ((1u << nvis) - 1u) & 0xfu;
           key = ((uint64_t)b << 41) | ((uint64_t)u << 17) | ((uint64_t)tau << 14) |
                 ((uint64_t)j << 4) | vis;
-
         }
       }
-      keys[tau * K + j] = key;
+      kr[tau][i] = key;
     }
   // One request among the group's valid rows (every thread holds their
   // request ids) and units below 2^15 - 1 (valid units are below max_pages *
@@ -265,7 +414,30 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     if (b0 < 0) b0 = b;
     else if (b != b0) one_req = false;
   }
-  if (one_req && (int64_t)a.max_pages * a.page_size / a.unit_tokens <= 32767) {
+  const int64_t nunits = (int64_t)a.max_pages * a.page_size / a.unit_tokens;
+  const int64_t li = (int64_t)g * a.num_groups + grp;
+  const int64_t list_base = li * a.list_cap;
+  uint2 *out = (uint2 *)(a.ws + a.lay.lists) + list_base;
+  int *soff = (int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1);
+  if (one_req && a.num_splits == 1 && nunits <= kBitmapUnits) {
+    // one request, one split, units below 2^16: the union straight from a
+    // bitmap (done, unless some token selected a unit twice)
+    if (union_by_bitmap<NT>(a, kr, b0, (int)nunits, out, soff, err)) {
+      if (err) atomicOr(a.err_flags, err);
+      return;
+    }
+  }
+  // ---- 2. the keys to LDS, sorted
+  __syncthreads();  // the bitmap pass may have used the same LDS
+  for (int e = kGroupTokens * K + threadIdx.x; e < npow2; e += NT) keys[e] = kInvalidKey;
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const int j = threadIdx.x + i * NT;
+      if (j < K) keys[tau * K + j] = kr[tau][i];
+    }
+  if (one_req && nunits <= 32767) {
     const uint64_t hi = b0 < 0 ? 0ull : (uint64_t)b0 << 41;
     bitonic_sort32(keys, npow2, [](uint64_t x) { return (uint32_t)x; },
                    [hi](uint32_t x) { return hi | x; });
@@ -340,10 +512,7 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   // stage the distinct (split, unit)s: (unit id lo, hi, mask32, split), in
   // sorted order: round i's leaders follow every leader of the rounds before
   // it and, within the round, those of lower waves and lanes
-  const int64_t li = (int64_t)g * a.num_groups + grp;
-  const int64_t list_base = li * a.list_cap;
   uint4 *stage = (uint4 *)(a.ws + a.lay.stage) + list_base;
-  uint2 *out = (uint2 *)(a.ws + a.lay.lists) + list_base;
   int total = 0;
   for (int i = 0; i < per; ++i) {
     const Lead L = analyze(i * NT + threadIdx.x);
@@ -420,7 +589,6 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
     }
   }
   // split s owns sorted entries [first with split >= s, first with split >= s + 1)
-  int *soff = (int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1);
   for (int sp = threadIdx.x; sp <= a.num_splits; sp += NT) {
     int lo = 0, hi = total;
     while (lo < hi) {
@@ -437,18 +605,28 @@ __global__ void gplan_zero(uint32_t *err) { *err = 0u; }
 }  // namespace
 
 // Dynamic key array (sort size + one slot per thread) plus the static wave
-// counters, at the largest sort: 8 tokens x 512 slots.
+// counters and scan sums, at the largest sort: 8 tokens x 512 slots.  (The
+// bitmap pass needs at most 2 x 2048 + 4096 + 8 x 128 words, less.)
 size_t grouped_plan_lds_bytes() {
   size_t n = 1;
   while (n < (size_t)kGroupTokens * 512 || n < (size_t)kGPlanThreadsFew) n <<= 1;
-  return (n + kGPlanThreadsFew) * 8 + 16 * (kGPlanThreadsFew / 64) * 4;
+  const size_t sort = (n + kGPlanThreadsFew) * 8;
+  const size_t bitmap = (2 * (kBitmapUnits + 1) / 32 + (size_t)kGroupTokens * 512 + kGroupTokens * 128) * 4;
+  return (sort > bitmap ? sort : bitmap) + 16 * (kGPlanThreadsFew / 64) * 4 + (kGPlanThreadsFew / 64) * 4;
 }
 
 hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s) {
   gplan_zero<<<1, 1, 0, s>>>(a.err_flags);
   if (a.num_groups == 0) return hipGetLastError();
   dim3 grid((unsigned)a.num_groups, (unsigned)a.Hkv);
-  const size_t lds = ((size_t)a.sort_n + a.plan_threads) * 8;
+  // the sort's keys, or the bitmap pass's words if that is larger
+  size_t lds = ((size_t)a.sort_n + a.plan_threads) * 8;
+  const int64_t nunits = (int64_t)a.max_pages * a.page_size / a.unit_tokens;
+  if (a.num_splits == 1 && nunits <= kBitmapUnits) {
+    const size_t nw = (size_t)(nunits + 31) / 32, cap = (size_t)a.list_cap;
+    const size_t bm = (2 * nw + cap + kGroupTokens * ((cap + 31) / 32)) * 4;
+    lds = bm > lds ? bm : lds;
+  }
   if (a.plan_threads == kGPlanThreadsFew)
     gplan_kernel<kGPlanThreadsFew><<<grid, kGPlanThreadsFew, lds, s>>>(a);
   else

@@ -44,6 +44,13 @@ def test_grouped_small_all_rows(Hq, Hkv, d):
     _parity(_mb(31, Hq=Hq, Hkv=Hkv, d=d))
 
 
+@pytest.mark.parametrize("ctx_len", [100000, 150000])
+def test_grouped_long_context_one_split(ctx_len):
+    """One split over contexts of 25K and 37.5K four-token units (the
+    planner's bitmap pass, below and above 2^15 units), every row."""
+    _parity(_mb(41, ctx_len=ctx_len, chunk_len=37, num_slots=96))
+
+
 @pytest.mark.parametrize("pd", ["f16", "bf16"])
 def test_grouped_16bit_partials(pd):
     """16-bit partial storage on the grouped route: the rounding of the FP32
