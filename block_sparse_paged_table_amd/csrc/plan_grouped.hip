@@ -15,9 +15,9 @@
 //        request:16 | unit:24 | token-in-group:3 | slot:10 | visible bits:4
 //      (bits 41.. | 17.. | 14.. | 4.. | 0..)
 //      (invalid selections sort to the end);
-//   2. bitonic sort of the keys in LDS (or, for one request and one split,
-//      steps 2-4 through a bitmap of the request's units: see
-//      union_by_bitmap);
+//   2. bitonic sort of the keys in LDS (or, for one request, steps 2-4
+//      through bitmaps of the request's units and of the (split, unit)
+//      entries: see union_by_bitmap);
 //   3. duplicates of a (request, unit, token) beyond the first slot are
 //      dropped and flagged; the first slot of each (request, unit, token)
 //      names its split (slot / slots_per_split); each distinct (split,
@@ -36,7 +36,8 @@ namespace msa {
 namespace {
 
 constexpr uint64_t kInvalidKey = ~0ull;
-constexpr int kBitmapUnits = 65535;  // largest unit count the bitmap pass takes
+constexpr int kBitmapUnits = 65535;          // largest unit count the bitmap pass takes
+constexpr int64_t kBitmapPassWords = 15360;   // and its LDS budget (60 KiB)
 
 // Ascending bitonic sort of n = E * blockDim.x keys held in LDS.  Thread t
 // keeps the keys of sorted positions tE .. tE+E-1 in registers: compare-
@@ -216,8 +217,171 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int &total) {
   return before + x - v;
 }
 
-// The union of a group whose valid rows belong to one request, with one
-// split and units below 2^16 (contexts up to 256K tokens), without sorting: a bitmap of the request's
+// LDS words the bitmap pass needs (sizing on the host and checks here).
+__host__ __device__ inline int64_t bitmap_pass_words(int64_t nunits, int64_t cap, int64_t splits) {
+  const int64_t nw = (nunits + 31) / 32, pw = (cap + 31) / 32;
+  if (splits == 1) return 2 * nw + cap + kGroupTokens * pw;  // union_one_split_by_bitmap
+  return 2 * nw + (cap + 1) / 2 + 2 * splits * pw + cap + kGroupTokens * pw;
+}
+
+// The union of a group whose valid rows belong to one request, with units
+// below 2^16 (contexts up to 256K tokens), without sorting.  Two levels of
+// bitmaps: one over the request's units gives each selected unit its rank in
+// ascending unit order; one over (split, rank) pairs, split-major, gives each
+// list entry its place in (split, unit) order -- the order the sort gives.
+// Each (token, unit) ORs its visible bits into its entry's mask word.  A
+// per-token presence bitmap over the ranks catches a token that selected a
+// unit twice (in any splits): then the kernel falls back to the sort, which
+// applies the first-slot rule (returns false).  Entries no row sees (mask
+// 0) are dropped, as by the sort path; the list and split offsets it writes
+// are the same.  LDS (the keys array, reused): bitmap_pass_words words.
+template <int NT, int JI>
+__device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64_t (&kr)[kGroupTokens][JI],
+                                                int b0, int nunits, uint2 *out, int *soff, uint32_t &err) {
+  extern __shared__ uint64_t keys[];
+  const int t = threadIdx.x;
+  const int S = a.num_splits;
+  const int nw = (nunits + 31) >> 5;   // <= 2048
+  const int cap = a.list_cap;          // bound on the union and on the entries
+  const int pw = (cap + 31) >> 5;      // words of a rank bitmap
+  const int sw = S * pw;               // words of the (split, rank) bitmap
+  uint32_t *ubm = (uint32_t *)keys;    // units
+  uint32_t *upre = ubm + nw;           // ranks before each unit word
+  uint16_t *uor = (uint16_t *)(upre + nw);  // unit of each rank
+  uint32_t *ebm = upre + nw + (cap + 1) / 2;  // (split, rank) entries
+  uint32_t *epre = ebm + sw;           // entries before each entry word
+  uint32_t *msk = epre + sw;           // mask of each entry
+  uint32_t *pres = msk + cap;          // (token, rank) presence
+  const uint32_t split_mul = ((1u << 20) + (uint32_t)a.slots_per_split - 1u) / (uint32_t)a.slots_per_split;
+  auto split_of = [&](uint64_t k) { return (int)((((uint32_t)(k >> 4) & 0x3ffu) * split_mul) >> 20); };
+  auto below = [](uint32_t w, uint32_t bit) { return (uint32_t)__popc(w & ((1u << bit) - 1u)); };
+  for (int e = t; e < nw; e += NT) ubm[e] = 0u;
+  for (int e = t; e < sw; e += NT) ebm[e] = 0u;
+  for (int e = t; e < cap; e += NT) msk[e] = 0u;
+  for (int e = t; e < kGroupTokens * pw; e += NT) pres[e] = 0u;
+  __syncthreads();
+  // the selected units
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const uint64_t k = kr[tau][i];
+      if (k == kInvalidKey) continue;
+      const uint32_t u = (uint32_t)(k >> 17) & 0xffffu;
+      atomicOr(&ubm[u >> 5], 1u << (u & 31u));
+    }
+  __syncthreads();
+  // unit ranks: thread t takes words [t * wpt, t * wpt + wpt)
+  {
+    const int wpt = (nw + NT - 1) / NT;
+    const int w0 = min(t * wpt, nw), w1 = min(w0 + wpt, nw);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(ubm[w]);
+    int nunion;
+    int run = block_exclusive_scan<NT>(cnt, nunion);
+    for (int w = w0; w < w1; ++w) {
+      upre[w] = (uint32_t)run;
+      for (uint32_t bits = ubm[w]; bits; bits &= bits - 1u) uor[run++] = (uint16_t)(w * 32 + __builtin_ctz(bits));
+    }
+  }
+  __syncthreads();
+  // presence of (token, rank): a token meeting a unit twice is a duplicate;
+  // the (split, rank) entries
+  bool dup = false;
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const uint64_t k = kr[tau][i];
+      if (k == kInvalidKey) continue;
+      const uint32_t u = (uint32_t)(k >> 17) & 0xffffu;
+      const uint32_t r = upre[u >> 5] + below(ubm[u >> 5], u & 31u);
+      const uint32_t bit = 1u << (r & 31u);
+      if (atomicOr(&pres[tau * pw + (r >> 5)], bit) & bit) dup = true;
+      atomicOr(&ebm[split_of(k) * pw + (r >> 5)], bit);
+    }
+  if (__syncthreads_or(dup)) return false;
+  // entry positions
+  const int wpt = (sw + NT - 1) / NT;
+  const int w0 = min(t * wpt, sw), w1 = min(w0 + wpt, sw);
+  {
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(ebm[w]);
+    int nent;
+    int run = block_exclusive_scan<NT>(cnt, nent);
+    for (int w = w0; w < w1; ++w) {
+      epre[w] = (uint32_t)run;
+      run += __popc(ebm[w]);
+    }
+  }
+  __syncthreads();
+  // visible bits of each (token, unit) into its entry's mask
+#pragma unroll
+  for (int tau = 0; tau < kGroupTokens; ++tau)
+#pragma unroll
+    for (int i = 0; i < JI; ++i) {
+      const uint64_t k = kr[tau][i];
+      const uint32_t vis = (uint32_t)k & 0xfu;
+      if (k == kInvalidKey || vis == 0u) continue;
+      const uint32_t u = (uint32_t)(k >> 17) & 0xffffu;
+      const uint32_t r = upre[u >> 5] + below(ubm[u >> 5], u & 31u);
+      const int ew = split_of(k) * pw + (int)(r >> 5);
+      atomicOr(&msk[epre[ew] + below(ebm[ew], r & 31u)], vis << (4 * tau));
+    }
+  __syncthreads();
+  // entries with a visible key, in entry order; split s starts at entry word
+  // s * pw, and the thread holding that word records its output offset
+  int nz = 0;
+  for (int w = w0; w < w1; ++w) {
+    const int p0 = (int)epre[w], n = __popc(ebm[w]);
+    for (int q = p0; q < p0 + n; ++q) nz += msk[q] != 0u;
+  }
+  int total;
+  int o = block_exclusive_scan<NT>(nz, total);
+  const int upp = a.page_size / a.unit_tokens;  // units per page
+  const int32_t *ptrow = a.page_table + (int64_t)max(b0, 0) * a.pt_stride;
+  for (int w = w0; w < w1; ++w) {
+    if (w % pw == 0) soff[w / pw] = o;
+    uint32_t bits = ebm[w];
+    int q = (int)epre[w];
+    const int rbase = (w % pw) * 32;
+    while (bits) {
+      // up to 8 entries at a time: their page-table loads first, then the writes
+      int uu[8], phys[8];
+      uint32_t mm[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        uu[x] = -1;
+        mm[x] = 0u;
+        if (bits) {
+          const int r = rbase + __builtin_ctz(bits);
+          bits &= bits - 1u;
+          uu[x] = uor[r];
+          mm[x] = msk[q++];
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) phys[x] = (uu[x] >= 0 && mm[x] != 0u) ? ptrow[uu[x] / upp] : 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        if (uu[x] < 0 || mm[x] == 0u) continue;
+        uint2 e;
+        if (phys[x] < 0 || phys[x] >= a.num_phys_pages) {
+          err |= MSA_ERRF_PHYS_RANGE;
+          e = make_uint2(0u, 0u);  // mask 0: contributes nothing
+        } else {
+          e = make_uint2(((uint32_t)phys[x] << 5) | (uint32_t)(uu[x] % upp), mm[x]);
+        }
+        out[o++] = e;
+      }
+    }
+  }
+  if (t == 0) soff[S] = total;
+  return true;
+}
+
+// One split: the same in one level.  The union of a group whose valid rows
+// belong to one request, with units below 2^16, without sorting: a bitmap of the request's
 // units marks the selected ones, so the union comes out in ascending unit
 // order (the order the sort gives) with a unit's rank = the set bits below
 // it; each (token, unit) ORs its visible bits into the unit's mask word.  A
@@ -228,7 +392,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int &total) {
 // LDS (the keys array, reused): bitmap and rank bases of ceil(nunits / 32)
 // words each, a mask word per union entry and 8 presence bits per entry.
 template <int NT, int JI>
-__device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64_t (&kr)[kGroupTokens][JI],
+__device__ __forceinline__ bool union_one_split_by_bitmap(const GroupArgs &a, const uint64_t (&kr)[kGroupTokens][JI],
                                                 int b0, int nunits, uint2 *out, int *soff, uint32_t &err) {
   extern __shared__ uint64_t keys[];
   const int t = threadIdx.x;
@@ -419,10 +583,12 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   const int64_t list_base = li * a.list_cap;
   uint2 *out = (uint2 *)(a.ws + a.lay.lists) + list_base;
   int *soff = (int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1);
-  if (one_req && a.num_splits == 1 && nunits <= kBitmapUnits) {
-    // one request, one split, units below 2^16: the union straight from a
-    // bitmap (done, unless some token selected a unit twice)
-    if (union_by_bitmap<NT>(a, kr, b0, (int)nunits, out, soff, err)) {
+  if (one_req && nunits <= kBitmapUnits &&
+      bitmap_pass_words(nunits, a.list_cap, a.num_splits) <= kBitmapPassWords) {
+    // one request, units below 2^16: the union straight from bitmaps (done,
+    // unless some token selected a unit twice)
+    if (a.num_splits == 1 ? union_one_split_by_bitmap<NT>(a, kr, b0, (int)nunits, out, soff, err)
+                          : union_by_bitmap<NT>(a, kr, b0, (int)nunits, out, soff, err)) {
       if (err) atomicOr(a.err_flags, err);
       return;
     }
@@ -604,14 +770,13 @@ __global__ void gplan_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
 
-// Dynamic key array (sort size + one slot per thread) plus the static wave
-// counters and scan sums, at the largest sort: 8 tokens x 512 slots.  (The
-// bitmap pass needs at most 2 x 2048 + 4096 + 8 x 128 words, less.)
+// Dynamic LDS (the sort's keys, or the bitmap pass's words, at most
+// kBitmapPassWords) plus the static wave counters and scan sums.
 size_t grouped_plan_lds_bytes() {
   size_t n = 1;
   while (n < (size_t)kGroupTokens * 512 || n < (size_t)kGPlanThreadsFew) n <<= 1;
   const size_t sort = (n + kGPlanThreadsFew) * 8;
-  const size_t bitmap = (2 * (kBitmapUnits + 1) / 32 + (size_t)kGroupTokens * 512 + kGroupTokens * 128) * 4;
+  const size_t bitmap = (size_t)kBitmapPassWords * 4;
   return (sort > bitmap ? sort : bitmap) + 16 * (kGPlanThreadsFew / 64) * 4 + (kGPlanThreadsFew / 64) * 4;
 }
 
@@ -622,10 +787,10 @@ hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s) {
   // the sort's keys, or the bitmap pass's words if that is larger
   size_t lds = ((size_t)a.sort_n + a.plan_threads) * 8;
   const int64_t nunits = (int64_t)a.max_pages * a.page_size / a.unit_tokens;
-  if (a.num_splits == 1 && nunits <= kBitmapUnits) {
-    const size_t nw = (size_t)(nunits + 31) / 32, cap = (size_t)a.list_cap;
-    const size_t bm = (2 * nw + cap + kGroupTokens * ((cap + 31) / 32)) * 4;
-    lds = bm > lds ? bm : lds;
+  if (nunits <= kBitmapUnits) {
+    const int64_t words = bitmap_pass_words(nunits, a.list_cap, a.num_splits);
+    const size_t bm = (size_t)words * 4;
+    if (words <= kBitmapPassWords && bm > lds) lds = bm;
   }
   if (a.plan_threads == kGPlanThreadsFew)
     gplan_kernel<kGPlanThreadsFew><<<grid, kGPlanThreadsFew, lds, s>>>(a);
