@@ -92,6 +92,7 @@ def _calib_lib():
     lib.calib_read.argtypes = [P, I64, P, I32, I32, P]
     lib.calib_write.argtypes = [P, I64, I32, U32, I32, P]
     lib.calib_gather.argtypes = [P, I64, P, I64, P, I32, I32, P]
+    lib.calib_lds.argtypes = [P, I32, I32, I32, P]
     lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
     lib.calib_chunk_bytes.restype = I64
     return lib
@@ -164,6 +165,19 @@ def measure_ceilings(reps=5, buf_gib=4, pool_sweep=False):
     # and from a 2 MiB pool, which every XCD's 4 MB L2 holds: the rate of the
     # gathers that hit in L2
     out["gather_4k_l2_gbs"] = round(max(gather(2, (4, 8)).values()), 1)
+    # LDS reads of the grouped attention kernel's operands (bytes per clock and
+    # CU at the 2.4 GHz peak engine clock; each launch reads 16 KiB per wave
+    # and iteration, two 4-wave workgroups per CU)
+    lds_grid, lds_iters = 512, 2000
+    lds_sink = torch.zeros(lds_grid * 256, dtype=torch.int32, device="cuda")
+    lds_bytes = lds_grid * 4 * lds_iters * 16384
+    lds = {}
+    for mode, name in ((0, "k_frag_b128_bitrev"), (3, "k_frag_b128_rowidx"), (1, "v_frag_tr_b64"),
+                       (2, "consecutive_b128")):
+        fn = lambda: lib.calib_lds(lds_sink.data_ptr(), lds_grid, lds_iters, mode, sp)
+        timed(fn)
+        lds[name] = round(lds_bytes / (timed(fn) * 1e-3) / 256 / 2.4e9, 1)
+    out["lds_read_bytes_per_clk_cu"] = lds
     if pool_sweep:  # where the gather rate comes from: L2-, cache- or HBM-resident pools
         out["gather_4k_by_pool_mib"] = {m: round(max(gather(m, (4, 8)).values()), 1)
                                         for m in (2, 8, 32, 128, 1024)}
@@ -171,7 +185,8 @@ def measure_ceilings(reps=5, buf_gib=4, pool_sweep=False):
                      "read / write of %d GiB (grid-stride or one chunk per workgroup, %s "
                      "workgroups; writes non-temporal or write-back); 4 KiB-unit gather from a "
                      "32 MiB pool (and from a 2 MiB, L2-resident one), %d units, 2/4/8 units in "
-                     "flight per 256-thread workgroup, %d workgroups"
+                     "flight per 256-thread workgroup, %d workgroups; LDS operand reads of the "
+                     "grouped kernel, 2 x 4 waves per CU"
                      % (reps, buf_gib, "/".join(map(str, grids)), n_units, grid))
     return out
 

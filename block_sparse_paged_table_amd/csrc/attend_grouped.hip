@@ -24,8 +24,8 @@
 // 4 KiB list ring make 68 KiB of LDS (two workgroups per CU); against
 // 16-key stages with the same 32 keys in flight, a stage costs half the
 // barriers and softmax steps per key.  K rows are stored as they are in the
-// cache with a per-row XOR swizzle of their 16-byte chunks (the 16 rows of
-// one MFMA read fall in 16 different bank groups); V rows likewise, read
+// cache with a per-row XOR swizzle of their 16-byte chunks (so that the 16
+// rows of one MFMA read spread over the LDS banks); V rows likewise, read
 // back transposed.  Per stage and active row tile:
 //
 //   S^T = K . Q^T      f16 MFMA 16x16x32 per 16-key tile, FP32 accumulate
@@ -84,9 +84,17 @@ template <int D> struct GGeom {
   static_assert(WGS * LDS <= 160 * 1024, "workgroups per CU");
 };
 
+// XOR swizzle of the 16-byte chunks of K row r.  The 16 lanes of a quarter
+// wave read one chunk of each of rows 0..15; at head_dim 256 (512-byte rows)
+// the row index bit-reversed spreads those reads over the LDS banks of gfx950
+// (measured with ds_read_b128: 204 B per clock and CU against 116 for the
+// row index itself, which conflicts); at head_dim 128 the row index.
+template <int D> __device__ __forceinline__ int gk_swz(int r) {
+  return D == 256 ? (int)(__builtin_bitreverse32((uint32_t)(r & 15)) >> 28) : (r & 15);
+}
 // Byte offset of 16-byte chunk c of K row r (r < 32) / V row r in a stage.
 template <int D> __device__ __forceinline__ int gk_off(int r, int c) {
-  return r * GGeom<D>::RB + ((c ^ (r & 15)) << 4);
+  return r * GGeom<D>::RB + ((c ^ gk_swz<D>(r)) << 4);
 }
 template <int D> __device__ __forceinline__ int gv_off(int r, int c) {
   return GGeom<D>::K_BYTES + r * GGeom<D>::RB + ((c ^ ((r & 7) << 1)) << 4);
@@ -147,7 +155,7 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(const GroupArgs &a, int w
 #pragma unroll
   for (int h = 0; h < Gm::LPP; ++h) {
     const int r = w * 4 + h * Gm::ROWS_PER_LOAD + lane / Gm::CPR, pos = lane % Gm::CPR;
-    L.dk[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ (r & 15)) << 4);
+    L.dk[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ gk_swz<D>(r)) << 4);
     L.dv[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ ((r & 7) << 1)) << 4);
   }
   return L;
@@ -259,10 +267,18 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
   // byte offset in the K / V caches of unit u of the run (an LDS read of its
   // list entry, wave-uniform)
   const int64_t head_off = (int64_t)g * a.kv_stride_head;
-  auto unit_off = [&](int u) {
-    const uint32_t e = __builtin_amdgcn_readfirstlane(sList[(u + par) % kListRing].x);
+  auto entry_off = [&](uint32_t e) {
     return (int64_t)(e >> 5) * a.kv_stride_page + (int64_t)((e & 31u) * 4) * a.kv_stride_tok + head_off;
   };
+  auto unit_off = [&](int u) { return entry_off(__builtin_amdgcn_readfirstlane(sList[(u + par) % kListRing].x)); };
+  // List entries are read from LDS one stage before they are used, so that
+  // their latency hides behind a stage of compute instead of delaying the
+  // loads and the K reads after each barrier: `pe` holds the cache entries
+  // of the units the next stage issues (lane 0: tile A's, lane 1: tile B's),
+  // `pma` / `pmb` the masks of this lane group's units of the next stage.
+  // Entries past the run are read but not used.
+  auto fetch_issue = [&](int s) { return sList[(UPS * s + wave + (lane & 1) * 4 + par) & (kListRing - 1)].x; };
+  auto fetch_mask = [&](int u) { return sList[(u + par) & (kListRing - 1)].y; };
 
   // ---- prologue: the list's first two chunks into LDS, Q into registers,
   // then the first NST - 1 stages in flight.  The loop below issues no memory
@@ -298,6 +314,7 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < nst) issue_stage(smem + s * Gm::STAGE, s);
+  uint32_t pe = fetch_issue(NST - 1), pma = fetch_mask(gq), pmb = fetch_mask(gq + 4);
 
   // One stage: J (compile time) is its ring slot.
   auto stage = [&](auto J_, const int beta) {
@@ -317,14 +334,22 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
       else wait_vm_lgkm0<2 * Gm::ULOADS>();
     }
     stage_barrier();  // stage beta landed for every wave; slot of beta - 1 free
-    if (beta + NST - 1 < nst) issue_stage(smem + ((J + NST - 1) % NST) * Gm::STAGE, beta + NST - 1);
-    // List chunk c >= 2 goes into the slot chunk c - 2 held, free since this
-    // stage's barrier (chunk c - 2's last units are those of stage
-    // 64 (c - 1) - 1 at the latest); it is first read about 64 - NST stages
-    // later, long after the stage waits have covered it (loads retire in
-    // order, and it is older than the stage loads issued from the next stage
-    // on).  These loads are not in `newer`: a wait that leaves one of them out
-    // only waits for one load more than it needs.
+    if (beta + NST - 1 < nst) {
+      uint8_t *slot = smem + ((J + NST - 1) % NST) * Gm::STAGE;
+      const int ua = UPS * (beta + NST - 1) + wave, ub = ua + 4;
+      const uint32_t ea = __builtin_amdgcn_readlane(pe, 0), eb = __builtin_amdgcn_readlane(pe, 1);
+      issue_unit<D>(a, slot, wave * 4, ua < count ? entry_off(ea) : 0, ua < count, L);
+      issue_unit<D>(a, slot, 16 + wave * 4, ub < count ? entry_off(eb) : 0, ub < count, L);
+    }
+    // List chunk c >= 2 (list positions 256 c ..) goes into the slot chunk
+    // c - 2 held.  This is stage 32 c - 31; chunk c - 2 serves stages up to
+    // 32 c - 33, whose entries were read by stage 32 c - 34, before this
+    // stage's barrier.  Chunk c serves stages from 32 c - 1 on, whose entries
+    // are first read at stage 32 c - 1 - NST, 30 - NST stages from now: the
+    // stage waits cover it within NST stages (loads retire in order, and it
+    // is older than the stage loads issued from the next stage on), and a
+    // barrier then publishes it.  These loads are not in `newer`: a wait that
+    // leaves one of them out only waits for one load more than it needs.
     if (beta >= kChunkStages + 1 && (beta - 1) % kChunkStages == 0) {
       const int c = (beta - 1) / kChunkStages + 1;
       if (c * kListChunk < nlist) issue_list_chunk(list, nlist, c, wave, sList);
@@ -333,8 +358,11 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
     // this lane group's units of the stage (gq of tile A, 4 + gq of tile B),
     // and whether any unit of the stage has a token of this wave's tile
     const int ua = UPS * beta + gq, ub = ua + 4;
-    const uint32_t mask_a = ua < count ? sList[(ua + par) % kListRing].y : 0u;
-    const uint32_t mask_b = ub < count ? sList[(ub + par) % kListRing].y : 0u;
+    const uint32_t mask_a = ua < count ? pma : 0u;
+    const uint32_t mask_b = ub < count ? pmb : 0u;
+    pe = fetch_issue(beta + NST);
+    pma = fetch_mask(ua + UPS);
+    pmb = fetch_mask(ub + UPS);
     if (!has_tile || !__any(((mask_a | mask_b) & tilemask) != 0u)) return;
     // ---- S^T for the stage's 32 keys, tile A then tile B (lane: keys
     // 4gq..4gq+3 of each tile, row n), each contraction over four
@@ -444,8 +472,9 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
 size_t grouped_attend_lds_bytes() {
   return (size_t)(GGeom<256>::LDS > GGeom<128>::LDS ? GGeom<256>::LDS : GGeom<128>::LDS);
 }
-static_assert(kChunkStages > 2 * GGeom<256>::NST + 1 && kChunkStages > 2 * GGeom<128>::NST + 1,
-              "a list chunk is loaded NST stages before its first use");
+static_assert(kChunkStages - 2 - GGeom<256>::NST >= GGeom<256>::NST &&
+                  kChunkStages - 2 - GGeom<128>::NST >= GGeom<128>::NST,
+              "a list chunk has landed and is published before its entries are first read");
 
 hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
   if (a.num_groups == 0) return hipSuccess;

@@ -15,6 +15,16 @@
 //                 into a pool small enough to stay in the Infinity Cache:
 //                 the ceiling of the grouped microblock route's K/V gather.
 //                 Each workgroup keeps UPI units (UPI * 4 KiB) in flight.
+//   calib_lds     LDS read throughput of the grouped route's operand reads:
+//                 each wave reads one 16 KiB quarter of a 64 KiB buffer (two
+//                 16-row tiles of 512-byte rows) over and over, as K
+//                 fragments (ds_read_b128, lane (n, q) reads row n at chunk
+//                 (8 q + c) ^ s(n), with s(n) the 4-bit row index bit-reversed
+//                 as the head_dim 256 kernel stores K, or s(n) = n), as
+//                 transposed V fragments (ds_read_b64_tr_b16, row 4 q +
+//                 (lane / 4) % 4, chunk 2 (j ^ row % 8) + (lane % 4) / 2), or
+//                 as consecutive 16-byte reads.  Two workgroups of 4 waves
+//                 per CU, as the grouped attention kernel runs.
 //
 // All indexing is bounded by the sizes passed in; every kernel exits.
 #include <hip/hip_runtime.h>
@@ -128,9 +138,71 @@ __global__ void __launch_bounds__(kThreads) k_gather(const u32x4 *__restrict__ p
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int MODE>
+__global__ void __launch_bounds__(kThreads, 2) k_lds(uint32_t *__restrict__ sink, int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t s[65536];
+  const int t = threadIdx.x, lane = t & 63, n = lane & 15, q = lane >> 4;
+  for (int i = t; i < 65536 / 16; i += kThreads)
+    ((u32x4 *)s)[i] = u32x4{(uint32_t)i, (uint32_t)i * 2654435761u, ~(uint32_t)i, (uint32_t)i ^ 0x5bd1e995u};
+  __syncthreads();
+  uint32_t acc = 0;
+  uint32_t base = (uint32_t)(t >> 6) * 16384u;  // this wave's quarter: rows 0..31 of 512 bytes
+  const int vr = q * 4 + ((lane >> 2) & 3), vc = lane & 3;
+  for (int it = 0; it < iters; ++it) {
+    __asm__ volatile("" : "+v"(base));  // the reads are not hoisted out of the loop
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const uint32_t tb = base + tile * 8192u;
+      if constexpr (MODE == 0 || MODE == 3) {
+        const int sw = MODE == 0 ? (int)(__builtin_bitreverse32((uint32_t)n) >> 28) : n;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 v = *(const u32x4 *)(s + tb + n * 512 + (((8 * q + c) ^ sw) << 4));
+          acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+        }
+      } else if constexpr (MODE == 1) {
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt) {
+          const uint32_t o = tb + vr * 512 + (((((mt & 7) ^ (vr & 7)) << 1) + (vc >> 1)) << 4) + (vc & 1) * 8 +
+                             (mt & 8) * 32;
+          const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(s + o));
+          acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[1] << 16) ^ (uint32_t)(uint16_t)v[2] ^
+                 ((uint32_t)(uint16_t)v[3] << 16);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 v = *(const u32x4 *)(s + tb + c * 1024 + lane * 16);
+          acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+        }
+      }
+    }
+  }
+  sink[(int64_t)blockIdx.x * kThreads + t] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS probe: sink holds grid * 256 words; each wave reads 16 KiB per
+// iteration.  mode 0: K fragments, bit-reversed row swizzle; 1: transposed
+// V fragments; 2: consecutive 16-byte reads; 3: K fragments, row-index
+// swizzle.
+int calib_lds(uint32_t *sink, int grid, int iters, int mode, void *stream) {
+  if (!sink || grid < 1 || iters < 1 || mode < 0 || mode > 3) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (mode) {
+    case 0: k_lds<0><<<grid, kThreads, 0, s>>>(sink, iters); break;
+    case 1: k_lds<1><<<grid, kThreads, 0, s>>>(sink, iters); break;
+    case 2: k_lds<2><<<grid, kThreads, 0, s>>>(sink, iters); break;
+    default: k_lds<3><<<grid, kThreads, 0, s>>>(sink, iters); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // sink: one uint32 per wave (4 * grid words).  mode 0: grid-stride
 // addressing; mode 1: one contiguous chunk per workgroup (the chunked form

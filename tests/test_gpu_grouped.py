@@ -38,8 +38,11 @@ def _parity(p, out_dtype=None):
     return dp
 
 
+# head_dim 256 with 8 / 6 / 3 / 2 query heads per KV head: 4 / 3 / 2 / 1 row
+# tiles of a group, so every wave loads (4) or 1 / 2 / 3 tileless waves load
 @pytest.mark.parametrize("Hq,Hkv,d", [(6, 1, 256), (6, 1, 128), (1, 1, 128), (2, 1, 256),
-                                      (8, 1, 128), (12, 2, 256), (3, 3, 128)])
+                                      (8, 1, 128), (12, 2, 256), (3, 3, 128), (8, 1, 256),
+                                      (3, 1, 256)])
 def test_grouped_small_all_rows(Hq, Hkv, d):
     _parity(_mb(31, Hq=Hq, Hkv=Hkv, d=d))
 
