@@ -83,12 +83,27 @@ template <int ROUTE, int D> struct Geom {
   static constexpr int LDS = K_BYTES + V_BYTES + 64 + ENT_BYTES;
 };
 
-// Byte offset of 16-byte chunk c of K row `key`: XOR swizzle so that the 16
-// rows one MFMA reads land in distinct LDS banks.
+// XOR swizzle of the 16-byte chunks of K row `key`, a function of the
+// A-operand row r = row_of_key(key) the key feeds.  One ds_read_b128 has
+// each quarter wave read one chunk of rows r = 0..15; which swizzles keep
+// those reads apart on the LDS banks of gfx950 was measured (LDS probe,
+// bytes per clock and CU; the plain row index conflicts two-way, ~115-120):
+//   128-byte rows (FP8, d 128), keys of key_of:     (r ^ r >> 3) & 7   223
+//   256-byte rows (16-bit, d 128), keys of key_of:  (r & 3) << 2 | r >> 2   223
+//   256-byte rows (FP32, d 64), consecutive keys:   r bit-reversed   223
+// Other row widths keep r shifted down to the row's chunk count.
+template <int ROUTE, int D> __device__ __forceinline__ int k_swz(int key) {
+  using Gm = Geom<ROUTE, D>;
+  const int r = row_of_key<ROUTE>(key);
+  if constexpr (Gm::RB == 128 && ROUTE != kRouteF32) return (r ^ (r >> 3)) & 7;
+  else if constexpr (Gm::RB == 256 && ROUTE != kRouteF32) return ((r & 3) << 2) | (r >> 2);
+  else if constexpr (Gm::RB == 256) return (int)(__builtin_bitreverse32((uint32_t)r) >> 28);
+  else return r >> Gm::SWZ_SHIFT;
+}
+// Byte offset of 16-byte chunk c of K row `key`.
 template <int ROUTE, int D> __device__ __forceinline__ int k_off(int key, int c) {
   using Gm = Geom<ROUTE, D>;
-  const int sw = row_of_key<ROUTE>(key) >> Gm::SWZ_SHIFT;
-  return key * Gm::RB + ((c ^ sw) << 4);
+  return key * Gm::RB + ((c ^ k_swz<ROUTE, D>(key)) << 4);
 }
 // Byte offset of the 16-byte chunk holding keys [8c, 8c+8) of V^T row dv.
 __device__ __forceinline__ int vt_off(int dv, int c) { return dv * (PAGE * 2) + ((c ^ (dv & 15)) << 4); }

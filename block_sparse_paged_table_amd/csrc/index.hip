@@ -53,10 +53,14 @@ template <int D> struct IGeom {
 };
 
 // Byte offset of chunk c of K row `key` in LDS, XOR-swizzled so that the 16
-// rows an MFMA operand reads fall into different banks.
+// rows an MFMA operand reads (keys 16 t .. 16 t + 15) spread over the LDS
+// banks.  For 128-byte rows (d 128) the swizzle (key & 7) ^ 5 (key >> 3 & 1)
+// was measured on gfx950 at 221 B per clock and CU against 112 for key & 7,
+// which conflicts two-way; other row widths keep the key's low bits.
 template <int D> __device__ __forceinline__ int ik_off(int key, int c) {
   using Gm = IGeom<D>;
-  return key * Gm::RB + ((c ^ (key & (Gm::CPR - 1))) << 4);
+  const int sw = Gm::CPR == 8 ? (key & 7) ^ (((key >> 3) & 1) * 5) : (key & (Gm::CPR - 1));
+  return key * Gm::RB + ((c ^ sw) << 4);
 }
 
 template <int D>
