@@ -93,6 +93,7 @@ def _calib_lib():
     lib.calib_write.argtypes = [P, I64, I32, U32, I32, P]
     lib.calib_gather.argtypes = [P, I64, P, I64, P, I32, I32, P]
     lib.calib_lds.argtypes = [P, I32, I32, I32, P]
+    lib.calib_lds_pattern.argtypes = [P, I32, I32, P, I32, P]
     lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
     lib.calib_chunk_bytes.restype = I64
     return lib
@@ -191,6 +192,92 @@ def measure_ceilings(reps=5, buf_gib=4, pool_sweep=False):
     return out
 
 
+def lds_patterns(reps=5):
+    """LDS read throughput (bytes per clock and CU at 2.4 GHz, two 4-wave
+    workgroups per CU) of the kernels' MFMA operand reads, each K tile under
+    the XOR swizzle it uses and under the one it replaced (calib_lds_pattern;
+    the lane offsets follow the kernels' LDS layouts).  Lane l = n + 16 q
+    reads A-operand row n; a K row's 16-byte chunk c sits at c ^ swz(row)."""
+    import ctypes
+    import torch
+    lib = _calib_lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    grid, iters = 512, 2000
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    lanes = [(l & 15, l >> 4) for l in range(64)]
+    brev4 = lambda x: int("{:04b}".format(x & 15)[::-1], 2)
+    # page kernel, 16-bit and FP8 routes: key of A-operand row m in key tile t
+    key_of = lambda t, m: (t >> 1) * 32 + (m >> 2) * 8 + (t & 1) * 4 + (m & 3)
+
+    def grouped_k(sw):  # 512-byte rows, 32 per stage, chunk 8 q + c
+        return [[n * 512 + (((8 * q + c) ^ sw(n)) << 4) + tile * 8192 for n, q in lanes]
+                for tile in range(2) for c in range(8)]
+
+    def page_k(rb, sw):  # rows of rb bytes at key_of, chunk (rb / 64) q + c
+        lch = rb // 64
+        return [[key_of(t, n) * rb + (((lch * q + c) ^ sw(n)) << 4) for n, q in lanes]
+                for t in range(16 // lch) for c in range(lch)][:16]
+
+    def page_f32_k(sw):  # 256-byte rows (d 64), keys 16 t + n, chunk 4 q + c
+        return [[(t * 16 + n) * 256 + (((4 * q + c) ^ sw(n)) << 4) for n, q in lanes]
+                for t in range(4) for c in range(4)]
+
+    def index_k(sw):  # 128-byte rows, keys 16 t + n, chunk 2 q + c
+        return [[(t * 16 + n) * 128 + (((2 * q + c) ^ sw(t * 16 + n)) << 4) for n, q in lanes]
+                for t in range(8) for c in range(2)]
+
+    def page_vt():  # V^T rows of 256 bytes (128 keys), row 16 mt + n, chunk (4 kb + q) ^ (row & 15)
+        return [[(mt * 16 + n) * 256 + (((4 * kb + q) ^ n) << 4) for n, q in lanes]
+                for kb in range(2) for mt in range(8)]
+
+    def grouped_vtr():  # transposed reads of V rows (512 bytes), swizzle 2 (row & 7)
+        out = []
+        for tile in range(2):
+            for mt in range(8):
+                row = []
+                for l in range(64):
+                    vr, vc = (l >> 4) * 4 + ((l >> 2) & 3), l & 3
+                    row.append(tile * 8192 + vr * 512 + ((((mt ^ (vr & 7)) << 1) + (vc >> 1)) << 4) + (vc & 1) * 8)
+                out.append(row)
+        return out
+
+    pats = {
+        "consecutive_b128": (0, [[k * 1024 + l * 16 for l in range(64)] for k in range(16)]),
+        "grouped_k_d256_bitrev (used)": (0, grouped_k(brev4)),
+        "grouped_k_d256_rowidx": (0, grouped_k(lambda n: n)),
+        "page_k_fp8_d128 (r^r>>3)&7 (used)": (0, page_k(128, lambda r: (r ^ (r >> 3)) & 7)),
+        "page_k_fp8_d128 r>>1": (0, page_k(128, lambda r: r >> 1)),
+        "page_k_16bit_d128 (r&3)<<2|r>>2 (used)": (0, page_k(256, lambda r: ((r & 3) << 2) | (r >> 2))),
+        "page_k_16bit_d128 r": (0, page_k(256, lambda r: r)),
+        "page_k_f32_d64 bitrev (used)": (0, page_f32_k(brev4)),
+        "page_k_f32_d64 r": (0, page_f32_k(lambda r: r)),
+        "index_k_d128 (k&7)^5(k>>3&1) (used)": (0, index_k(lambda k: (k & 7) ^ (((k >> 3) & 1) * 5))),
+        "index_k_d128 k&7": (0, index_k(lambda k: k & 7)),
+        "page_vt_b128 (used)": (0, page_vt()),
+        "grouped_v_tr_b64 (used)": (1, grouped_vtr()),
+    }
+    res = {}
+    for name, (kind, tab) in pats.items():
+        t = np.asarray(tab, dtype=np.int64)
+        assert t.shape == (16, 64) and t.max() < 65536 and (t % (16 if kind == 0 else 8) == 0).all(), name
+        dev = torch.from_numpy(t.astype(np.int32)).cuda()
+        fn = lambda: lib.calib_lds_pattern(sink.data_ptr(), grid, iters, dev.data_ptr(), kind, sp)
+        for _ in range(2):
+            assert fn() == 0
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            assert fn() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        nbytes = grid * 4 * iters * 16 * (1024 if kind == 0 else 512)
+        res[name] = round(nbytes / (float(np.median(ts)) * 1e-3) / 256 / 2.4e9, 1)
+    return res
+
+
 def cpu_info():
     """Host the CPU baseline ran on: model, logical CPUs and affinity mask."""
     model = None
@@ -269,9 +356,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
+    ap.add_argument("--lds-patterns", action="store_true",
+                    help="measure the LDS read throughput of the kernels' operand read patterns "
+                         "under their K-tile swizzles and print it as JSON")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure the ceilings (HBM read, HBM write, cache-resident "
-                         "4 KiB gather) and print them as one JSON line")
+                         "4 KiB gather, LDS operand reads) and print them as one JSON line")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the live ceiling measurement of the normal run")
     args = ap.parse_args()
@@ -279,6 +369,11 @@ def main():
         import torch
         torch.cuda.set_device(0)
         print(json.dumps(measure_ceilings(pool_sweep=True)), flush=True)
+        return
+    if args.lds_patterns:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"lds_read_bytes_per_clk_cu": lds_patterns()}), flush=True)
         return
     if args.copy_calibration:
         import torch

@@ -25,6 +25,12 @@
 //                 (lane / 4) % 4, chunk 2 (j ^ row % 8) + (lane % 4) / 2), or
 //                 as consecutive 16-byte reads.  Two workgroups of 4 waves
 //                 per CU, as the grouped attention kernel runs.
+//   calib_lds_pattern  LDS read throughput of any one read pattern: 16
+//                 instructions of 64 lane offsets given by the caller
+//                 (ds_read_b128 or ds_read_b64_tr_b16), the same for every
+//                 wave, repeated; the offsets are masked into the 64 KiB
+//                 buffer.  It measures which XOR swizzle of a K tile keeps the
+//                 reads of an MFMA operand apart on the LDS banks.
 //
 // All indexing is bounded by the sizes passed in; every kernel exits.
 #include <hip/hip_runtime.h>
@@ -184,9 +190,49 @@ __global__ void __launch_bounds__(kThreads, 2) k_lds(uint32_t *__restrict__ sink
   sink[(int64_t)blockIdx.x * kThreads + t] = acc;
 }
 
+template <int KIND>  // 0: ds_read_b128, 1: ds_read_b64_tr_b16
+__global__ void __launch_bounds__(kThreads, 2) k_lds_pattern(uint32_t *__restrict__ sink, int iters,
+                                                            const uint32_t *__restrict__ tab) {
+  __shared__ __attribute__((aligned(16))) uint8_t s[65536];
+  const int t = threadIdx.x, lane = t & 63;
+  for (int i = t; i < 65536 / 16; i += kThreads)
+    ((u32x4 *)s)[i] = u32x4{(uint32_t)i, (uint32_t)i * 2654435761u, ~(uint32_t)i, (uint32_t)i ^ 0x5bd1e995u};
+  uint32_t off[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) off[k] = tab[k * 64 + lane] & (KIND == 0 ? 0xfff0u : 0xfff8u);
+  __syncthreads();
+  uint32_t acc = 0, z = 0;
+  for (int it = 0; it < iters; ++it) {
+    __asm__ volatile("" : "+v"(z));  // the reads are not hoisted out of the loop
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if constexpr (KIND == 0) {
+        const u32x4 v = *(const u32x4 *)(s + (off[k] | z));
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      } else {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(s + (off[k] | z)));
+        acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[1] << 16) ^ (uint32_t)(uint16_t)v[2] ^
+               ((uint32_t)(uint16_t)v[3] << 16);
+      }
+    }
+  }
+  sink[(int64_t)blockIdx.x * kThreads + t] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS pattern probe: tab holds 16 x 64 byte offsets (device memory), sink
+// grid * 256 words; kind 0: ds_read_b128 (16 KiB per wave and iteration),
+// kind 1: ds_read_b64_tr_b16 (8 KiB).
+int calib_lds_pattern(uint32_t *sink, int grid, int iters, const uint32_t *tab, int kind, void *stream) {
+  if (!sink || !tab || grid < 1 || iters < 1 || kind < 0 || kind > 1) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (kind == 0) k_lds_pattern<0><<<grid, kThreads, 0, s>>>(sink, iters, tab);
+  else k_lds_pattern<1><<<grid, kThreads, 0, s>>>(sink, iters, tab);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // LDS probe: sink holds grid * 256 words; each wave reads 16 KiB per
 // iteration.  mode 0: K fragments, bit-reversed row swizzle; 1: transposed

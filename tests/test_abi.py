@@ -308,7 +308,8 @@ def test_calibration_probes_load_and_validate():
     library) load, export their entry points and reject bad arguments on the
     host; calib_chunk_bytes is host arithmetic."""
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_paged_table_amd", "lib", "libmsa_calib.so"))
-    for name in ("calib_read", "calib_write", "calib_gather", "calib_lds", "calib_chunk_bytes"):
+    for name in ("calib_read", "calib_write", "calib_gather", "calib_lds", "calib_lds_pattern",
+                 "calib_chunk_bytes"):
         assert hasattr(lib, name), name
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.calib_lds.argtypes = [P, I32, I32, I32, P]
@@ -316,6 +317,9 @@ def test_calibration_probes_load_and_validate():
     assert lib.calib_lds(FAKE, 0, 10, 0, None) == 1     # empty grid
     assert lib.calib_lds(FAKE, 512, 0, 0, None) == 1    # no iterations
     assert lib.calib_lds(FAKE, 512, 10, 4, None) == 1   # unknown mode
+    lib.calib_lds_pattern.argtypes = [P, I32, I32, P, I32, P]
+    assert lib.calib_lds_pattern(FAKE, 512, 10, None, 0, None) == 1  # no offset table
+    assert lib.calib_lds_pattern(FAKE, 512, 10, FAKE, 2, None) == 1  # unknown read kind
     lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
     lib.calib_chunk_bytes.restype = I64
     assert lib.calib_chunk_bytes(4 << 30, 2048, 8) == 4 << 30
