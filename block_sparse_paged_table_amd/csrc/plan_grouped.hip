@@ -17,7 +17,7 @@
 //      (invalid selections sort to the end);
 //   2. bitonic sort of the keys in LDS (or, for one request, steps 2-4
 //      through bitmaps of the request's units and of the (split, unit)
-//      entries: see union_by_bitmap);
+//      entries: see union_one_split_by_bitmap and union_by_bitmap);
 //   3. duplicates of a (request, unit, token) beyond the first slot are
 //      dropped and flagged; the first slot of each (request, unit, token)
 //      names its split (slot / slots_per_split); each distinct (split,
