@@ -85,7 +85,7 @@ __device__ __forceinline__ void store_kpage(uint8_t *sk, const u32x4 *r) {
 }
 
 template <int D, int IPC>
-__global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a) {
+__global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArgs a) {
   using Gm = IGeom<D>;
   constexpr int IT = Gm::IT, ITQ = Gm::ITQ;
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][Gm::PAGE_BYTES];
@@ -222,11 +222,18 @@ __global__ void __launch_bounds__(IGeom<D>::IT) k_index_scores(const IndexArgs a
       const int jabs = j0 + jj;
       const int vis_to = (my_b == cb) ? my_last - jabs * IPAGE : -1;  // last visible in-page key
       float m = -INFINITY;
+      if (__all(vis_to >= IPAGE - 1)) {
+        // every row of the wave sees the whole page (all pages but a row's
+        // own): a plain max, no per-key test
 #pragma unroll
-      for (int t = 0; t < IPAGE / 16; ++t)
+        for (int t = 0; t < IPAGE / 16; ++t) m = fmaxf(m, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[t][i]);
+        for (int t = 0; t < IPAGE / 16; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[t][i]);
+      }
       m = quarter_reduce<true>(m);
       if (grp == 0 && my_b == cb) sScore[rho][jj] = m == -INFINITY ? m : m * a.scale;
     }
