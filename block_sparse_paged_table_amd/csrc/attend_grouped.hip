@@ -51,8 +51,6 @@
 namespace msa {
 namespace {
 
-#define LDS_AS __attribute__((address_space(3)))
-
 constexpr int GT = 256;             // threads per workgroup
 constexpr int SK = 32;              // keys per stage: two 16-key tiles A and B
 constexpr int UPS = SK / 4;         // units per stage: wave w loads units w (tile A) and w + 4 (tile B)
@@ -98,36 +96,6 @@ template <int D> __device__ __forceinline__ int gk_off(int r, int c) {
 }
 template <int D> __device__ __forceinline__ int gv_off(int r, int c) {
   return GGeom<D>::K_BYTES + r * GGeom<D>::RB + ((c ^ ((r & 7) << 1)) << 4);
-}
-
-// s_waitcnt with vmcnt(n) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
-// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
-template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// One 16-byte load per lane straight into LDS (global_load_lds_dwordx4):
-// lane i reads base + voff (base a wave-uniform 64-bit address, voff this
-// lane's 32-bit offset) and writes LDS bytes [lds + 16 i, lds + 16 i + 16);
-// M0 holds the LDS address, with the one wait state its write needs before
-// the load.  It is issued from asm so that the compiler, which cannot tell
-// which LDS bytes such a load writes, adds no wait for it before every later
-// LDS read: the kernel counts these loads itself (vmcnt) and publishes a
-// stage with a barrier.  No register is written: the data goes to LDS.
-__device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t voff, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(lds), "v"(voff), "s"(base)
-                   : "memory");
-}
-
-// Workgroup barrier that waits for nothing by itself (the waits are explicit)
-// and that the compiler may not move memory accesses across.
-__device__ __forceinline__ void stage_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
 }
 
 // Per-lane constants of the stage loop, computed once.

@@ -255,4 +255,37 @@ __device__ __forceinline__ float quarter_reduce(float x) {
   return MAX ? fmaxf(z0, z1) : z0 + z1;
 }
 
+#define LDS_AS __attribute__((address_space(3)))
+
+// s_waitcnt with vmcnt(n) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// One 16-byte load per lane straight into LDS (global_load_lds_dwordx4):
+// lane i reads base + voff (base a wave-uniform 64-bit address, voff this
+// lane's 32-bit offset) and writes LDS bytes [lds + 16 i, lds + 16 i + 16);
+// M0 holds the LDS address, with the one wait state its write needs before
+// the load.  It is issued from asm so that the compiler, which cannot tell
+// which LDS bytes such a load writes, adds no wait for it before every later
+// LDS read: the kernel counts these loads itself (vmcnt, which a
+// __syncthreads also drains) and publishes them with a barrier.  No register
+// is written: the data goes to LDS.
+__device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(lds), "v"(voff), "s"(base)
+                   : "memory");
+}
+
+// Workgroup barrier that waits for nothing by itself (the waits are explicit)
+// and that the compiler may not move memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 }  // namespace msa

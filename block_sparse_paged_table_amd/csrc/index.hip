@@ -57,31 +57,23 @@ template <int D> struct IGeom {
 // banks.  For 128-byte rows (d 128) the swizzle (key & 7) ^ 5 (key >> 3 & 1)
 // was measured on gfx950 at 221 B per clock and CU against 112 for key & 7,
 // which conflicts two-way; other row widths keep the key's low bits.
+template <int D> __device__ __forceinline__ int ik_swz(int key) {
+  using Gm = IGeom<D>;
+  return Gm::CPR == 8 ? (key & 7) ^ (((key >> 3) & 1) * 5) : (key & (Gm::CPR - 1));
+}
 template <int D> __device__ __forceinline__ int ik_off(int key, int c) {
-  using Gm = IGeom<D>;
-  const int sw = Gm::CPR == 8 ? (key & 7) ^ (((key >> 3) & 1) * 5) : (key & (Gm::CPR - 1));
-  return key * Gm::RB + ((c ^ sw) << 4);
+  return key * IGeom<D>::RB + ((c ^ ik_swz<D>(key)) << 4);
 }
 
-template <int D>
-__device__ __forceinline__ void load_kpage(const IndexArgs &a, int phys, int h, u32x4 *r) {
+// A K page goes straight from the cache into LDS (global_load_lds): load it
+// of wave w fills LDS chunks [q0, q0 + 64), q0 = it * IT + 64 w, each lane
+// one 16-byte chunk q0 + lane = row * CPR + physical chunk; this lane's
+// source offset in the page (the logical chunk is the physical one XOR the
+// row's swizzle) is dma_off(it).
+template <int D> __device__ __forceinline__ uint32_t kpage_src_off(const IndexArgs &a, int it) {
   using Gm = IGeom<D>;
-  const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)h * a.kv_stride_head;
-#pragma unroll
-  for (int it = 0; it < Gm::KCH; ++it) {
-    const int q = it * Gm::IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
-    r[it] = *(const u32x4 *)(kb + key * a.kv_stride_tok + c * 16);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_kpage(uint8_t *sk, const u32x4 *r) {
-  using Gm = IGeom<D>;
-#pragma unroll
-  for (int it = 0; it < Gm::KCH; ++it) {
-    const int q = it * Gm::IT + threadIdx.x, key = q / Gm::CPR, c = q % Gm::CPR;
-    *(u32x4 *)(sk + ik_off<D>(key, c)) = r[it];
-  }
+  const int q = it * Gm::IT + (int)threadIdx.x, key = q / Gm::CPR, pc = q % Gm::CPR;
+  return (uint32_t)(key * a.kv_stride_tok) + (uint32_t)((pc ^ ik_swz<D>(key)) << 4);
 }
 
 template <int D, int IPC>
@@ -167,6 +159,10 @@ __global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArg
     for (int c = 0; c < Gm::LANE_CH; ++c) qr[c] = *(const u32x4 *)(qp + c * 16);
   }
 
+  uint32_t dma_off[Gm::KCH];
+#pragma unroll
+  for (int it = 0; it < Gm::KCH; ++it) dma_off[it] = kpage_src_off<D>(a, it);
+
   const int nreq = sNreq;
   for (int ri = 0; ri < nreq; ++ri) {
     const int cb = sReq[ri];
@@ -174,22 +170,33 @@ __global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArg
     // pages of this chunk that some row of request cb can see
     const int jn = min(npg, lastmax / IPAGE - j0 + 1);
     if (jn <= 0) continue;
+    // the chunk's physical pages in one load (lane j: page j; -1 out of range)
     const int32_t *ptrow = a.page_table + (int64_t)cb * a.pt_stride + j0;
-    auto phys_of = [&](int jj) {
-      const int p = ptrow[jj];
-      return (p >= 0 && p < a.num_phys_pages) ? p : -1;
+    int pt = -1;
+    if (lane < jn) {
+      const int p = ptrow[lane];
+      pt = (p >= 0 && p < a.num_phys_pages) ? p : -1;
+    }
+    auto phys_of = [&](int jj) { return __builtin_amdgcn_readlane(pt, jj); };
+    // this wave's part of a page into buffer sk: KCH loads of 64 chunks
+    auto issue_page = [&](int phys, uint8_t *sk) {
+      const uint8_t *kb = a.k_cache + (int64_t)phys * a.kv_stride_page + (int64_t)h * a.kv_stride_head;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t *)sk);
+#pragma unroll
+      for (int it = 0; it < Gm::KCH; ++it) lds_dma16(kb, dma_off[it], lds + (it * IT + wave * 64) * 16);
     };
-    u32x4 kr[Gm::KCH];
     int phys_next = phys_of(0);
-    if (phys_next >= 0) load_kpage<D>(a, phys_next, h, kr);
+    if (phys_next >= 0) issue_page(phys_next, sK[0]);
     for (int jj = 0; jj < jn; ++jj) {
       const int phys = phys_next;
-      uint8_t *sk = sK[jj & 1];
-      if (phys >= 0) store_kpage<D>(sk, kr);
-      __syncthreads();
+      const uint8_t *sk = sK[jj & 1];
+      // page jj landed (each wave waits for its own loads; the barrier
+      // publishes them), and every wave is done with page jj - 1's buffer
+      wait_vm_lgkm0<0>();
+      stage_barrier();
       if (jj + 1 < jn) {
         phys_next = phys_of(jj + 1);
-        if (phys_next >= 0) load_kpage<D>(a, phys_next, h, kr);
+        if (phys_next >= 0) issue_page(phys_next, sK[(jj + 1) & 1]);
       }
       if (phys < 0) {
         if (a.err_flags && tid == 0) atomicOr(a.err_flags, MSA_ERRF_PHYS_RANGE);
