@@ -85,17 +85,17 @@ template <int D> struct GGeom {
 // XOR swizzle of the 16-byte chunks of K row r.  The 16 lanes of a quarter
 // wave read one chunk of each of rows 0..15; at head_dim 256 (512-byte rows)
 // the row index bit-reversed spreads those reads over the LDS banks of gfx950
-// (measured with ds_read_b128: 204 B per clock and CU against 116 for the
-// row index itself, which conflicts); at head_dim 128 the row index.
+// (measured with ds_read_b128: about 200 B per clock and CU against about 115
+// for the row index itself, which conflicts); at head_dim 128 the row index.
 template <int D> __device__ __forceinline__ int gk_swz(int r) {
   return D == 256 ? (int)(__builtin_bitreverse32((uint32_t)(r & 15)) >> 28) : (r & 15);
 }
-// Byte offset of 16-byte chunk c of K row r (r < 32) / V row r in a stage.
+// XOR swizzle of the chunks of V row r: an even value, so the two chunks of
+// one 16-dim block stay adjacent for the transposed reads.
+__device__ __forceinline__ int gv_swz(int r) { return (r & 7) << 1; }
+// Byte offset of 16-byte chunk c of K row r (r < 32) in a stage.
 template <int D> __device__ __forceinline__ int gk_off(int r, int c) {
   return r * GGeom<D>::RB + ((c ^ gk_swz<D>(r)) << 4);
-}
-template <int D> __device__ __forceinline__ int gv_off(int r, int c) {
-  return GGeom<D>::K_BYTES + r * GGeom<D>::RB + ((c ^ ((r & 7) << 1)) << 4);
 }
 
 // Per-lane constants of the stage loop, computed once.
@@ -114,17 +114,16 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(const GroupArgs &a, int w
 #pragma unroll
   for (int c = 0; c < Gm::LANE_CH; ++c) L.k[c] = gk_off<D>(n, gq * Gm::LANE_CH + c);
   // transposed V read: lane (gq, r, c) addresses row 4 gq + r at dims
-  // 16 mt + 4c .. +3, i.e. chunk 2 mt + c / 2, half c % 2; with the row's XOR
-  // swizzle 2 t (t = row & 7), chunk (2 mt + c/2) ^ 2t = 2 (mt ^ t) + c/2
+  // 16 mt + 4c .. +3, i.e. chunk 2 mt + c / 2, half c % 2, swizzled
   const int vr = gq * 4 + ((lane >> 2) & 3), vc = lane & 3;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    L.v[j] = Gm::K_BYTES + vr * Gm::RB + ((((j ^ (vr & 7)) << 1) + (vc >> 1)) << 4) + (vc & 1) * 8;
+    L.v[j] = Gm::K_BYTES + vr * Gm::RB + (((2 * j + (vc >> 1)) ^ gv_swz(vr)) << 4) + (vc & 1) * 8;
 #pragma unroll
   for (int h = 0; h < Gm::LPP; ++h) {
     const int r = w * 4 + h * Gm::ROWS_PER_LOAD + lane / Gm::CPR, pos = lane % Gm::CPR;
     L.dk[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ gk_swz<D>(r)) << 4);
-    L.dv[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ ((r & 7) << 1)) << 4);
+    L.dv[h] = (uint32_t)((r & 3) * a.kv_stride_tok) + ((pos ^ gv_swz(r)) << 4);
   }
   return L;
 }
