@@ -93,6 +93,7 @@ def _calib_lib():
     lib.calib_write.argtypes = [P, I64, I32, U32, I32, P]
     lib.calib_gather.argtypes = [P, I64, P, I64, P, I32, I32, P]
     lib.calib_lds.argtypes = [P, I32, I32, I32, P]
+    lib.calib_mixed.argtypes = [P, I64, P, I64, P, I32, I64, I32, P]
     lib.calib_lds_pattern.argtypes = [P, I32, I32, P, I32, P]
     lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
     lib.calib_chunk_bytes.restype = I64
@@ -144,6 +145,23 @@ def measure_ceilings(reps=5, buf_gib=4, pool_sweep=False):
     out["hbm_read_gbs"] = max(v for k, v in variants.items() if k.startswith("read"))
     out["variants"] = variants
     del buf
+    if pool_sweep:
+        # DRAM read and write streams at once, 1 : 6 (the page attention's
+        # L2-miss read : write bytes on the 16K Q8KV4 layer).  Not a ceiling of
+        # that kernel: its reads are mostly Infinity-Cache hits, and it moves
+        # more than this.
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(3 << 30, dtype=torch.uint8, device="cuda")
+        best = 0.0
+        for g in grids:
+            iters = src.numel() // (g * 8192)
+            fn = lambda: lib.calib_mixed(src.data_ptr(), src.numel(), dst.data_ptr(), dst.numel(),
+                                         sink.data_ptr(), g, iters, 6, sp)
+            timed(fn)
+            nb = g * iters * 8192 * 7
+            best = max(best, nb / (timed(fn) * 1e-3) / 1e9)
+        out["hbm_mixed_1r6w_gbs"] = round(best, 1)
+        del src, dst
     rng = np.random.default_rng(9)
     n_units = 1 << 20                           # 4 GiB of 4 KiB units
 
@@ -550,6 +568,7 @@ def main():
         if ceil:  # its bytes are almost all partial writes
             roof.update(ceiling=ceil["hbm_write_gbs"], ceiling_kind="measured HBM write",
                         frac_of_ceiling=round(attn_gbs / ceil["hbm_write_gbs"], 4))
+
     else:
         roof = dict(kernel="combine_kernel", bound="hbm", achieved=round(comb_gbs, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(comb_gbs / HBM_PEAK_GBS, 4),

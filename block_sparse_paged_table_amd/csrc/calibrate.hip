@@ -9,6 +9,10 @@
 //                 checksum per workgroup keeps the loads alive)
 //   calib_write   streaming write of a large buffer (16-byte non-temporal
 //                 stores)
+//   calib_mixed   streaming read and streaming write at once, WPR 4 KiB
+//                 blocks written per block read (16-byte non-temporal loads
+//                 and stores, each workgroup owning one chunk of each
+//                 array): what DRAM gives when both directions share it.
 //   calib_gather  gather of 4 KiB units -- two 2 KiB runs 8 KiB apart, the
 //                 K and V rows of one 4-token microblock in a K/V-interleaved
 //                 cache of 16-token blocks -- named by a list of unit ids
@@ -112,6 +116,29 @@ __global__ void __launch_bounds__(kThreads) k_write_chunk(u32x4 *__restrict__ ds
       else __builtin_nontemporal_store(v, dst + i + u * kThreads);
     }
   }
+}
+
+// Per iteration a workgroup reads 2 blocks of 4 KiB and writes 2 * WPR; it
+// owns `iters` iterations of each array (the caller sizes the arrays).
+template <int WPR>
+__global__ void __launch_bounds__(kThreads) k_mixed(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                    int64_t iters, uint32_t *__restrict__ sink) {
+  const int64_t lo_r = (int64_t)blockIdx.x * iters * 2 * kThreads;
+  const int64_t lo_w = (int64_t)blockIdx.x * iters * 2 * WPR * kThreads;
+  uint32_t acc = 0;
+  for (int64_t it = 0; it < iters; ++it) {
+    const u32x4 v0 = __builtin_nontemporal_load(src + lo_r + it * 2 * kThreads + threadIdx.x);
+    const u32x4 v1 = __builtin_nontemporal_load(src + lo_r + it * 2 * kThreads + kThreads + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < 2 * WPR; ++u) {
+      const uint32_t x = (uint32_t)(it * 2 * WPR + u) ^ threadIdx.x;
+      __builtin_nontemporal_store(u32x4{x, x + 1u, x + 2u, x + 3u},
+                                  dst + lo_w + (it * 2 * WPR + u) * kThreads + threadIdx.x);
+    }
+    acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
+  }
+  acc = wave_xor(acc);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
 }
 
 // Unit u of the pool: 16-byte chunks [u4 + c] for c < 128 (K half) and
@@ -277,6 +304,29 @@ int calib_write(void *dst, int64_t bytes, int grid, uint32_t seed, int mode, voi
 int64_t calib_chunk_bytes(int64_t bytes, int grid, int blocks_per_iter) {
   const int64_t it = (int64_t)blocks_per_iter * kThreads;
   return ((bytes / 16) / grid) / it * it * grid * 16;
+}
+
+// Mixed read + write: `iters` iterations per workgroup, each reading 8 KiB
+// and writing 8 KiB * wpr (wpr 1 .. 8); src must hold grid * iters * 8 KiB
+// and dst grid * iters * 8 KiB * wpr (checked against the sizes given).
+int calib_mixed(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes, uint32_t *sink, int grid,
+                int64_t iters, int wpr, void *stream) {
+  if (!src || !dst || !sink || grid < 1 || iters < 1 || wpr < 1 || wpr > 8) return 1;
+  if ((int64_t)grid * iters * 8192 > src_bytes || (int64_t)grid * iters * 8192 * wpr > dst_bytes) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  const u32x4 *r = (const u32x4 *)src;
+  u32x4 *w = (u32x4 *)dst;
+  switch (wpr) {
+    case 1: k_mixed<1><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 2: k_mixed<2><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 3: k_mixed<3><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 4: k_mixed<4><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 5: k_mixed<5><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 6: k_mixed<6><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    case 7: k_mixed<7><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+    default: k_mixed<8><<<grid, kThreads, 0, s>>>(r, w, iters, sink); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 // units_per_iter: 1, 2, 4 or 8 units in flight per workgroup.

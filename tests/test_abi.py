@@ -309,7 +309,7 @@ def test_calibration_probes_load_and_validate():
     host; calib_chunk_bytes is host arithmetic."""
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_paged_table_amd", "lib", "libmsa_calib.so"))
     for name in ("calib_read", "calib_write", "calib_gather", "calib_lds", "calib_lds_pattern",
-                 "calib_chunk_bytes"):
+                 "calib_mixed", "calib_chunk_bytes"):
         assert hasattr(lib, name), name
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.calib_lds.argtypes = [P, I32, I32, I32, P]
@@ -320,6 +320,10 @@ def test_calibration_probes_load_and_validate():
     lib.calib_lds_pattern.argtypes = [P, I32, I32, P, I32, P]
     assert lib.calib_lds_pattern(FAKE, 512, 10, None, 0, None) == 1  # no offset table
     assert lib.calib_lds_pattern(FAKE, 512, 10, FAKE, 2, None) == 1  # unknown read kind
+    lib.calib_mixed.argtypes = [P, I64, P, I64, P, I32, I64, I32, P]
+    assert lib.calib_mixed(FAKE, 8192, FAKE, 8192 * 6, FAKE, 1, 1, 9, None) == 1      # ratio out of range
+    assert lib.calib_mixed(FAKE, 8192, FAKE, 8192 * 5, FAKE, 1, 1, 6, None) == 1      # write array too small
+    assert lib.calib_mixed(FAKE, 8191, FAKE, 8192 * 6, FAKE, 1, 1, 6, None) == 1      # read array too small
     lib.calib_chunk_bytes.argtypes = [I64, I32, I32]
     lib.calib_chunk_bytes.restype = I64
     assert lib.calib_chunk_bytes(4 << 30, 2048, 8) == 4 << 30
