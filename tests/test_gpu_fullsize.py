@@ -102,3 +102,36 @@ def test_full_size_every_row(cfg):
         assert o_rel <= tol["rel_l2"] and v["o_max"] <= tol["max_abs"], v
     else:
         assert v["o_err"] ** 0.5 <= v["o_floor"] ** 0.5 + tol["rel_l2"] * v["o_ref"] ** 0.5, v
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_graph_replay_matches_eager(cfg):
+    """The step as the benchmark times it: plan, attention and combine
+    captured in one HIP graph and replayed.  Every replay rewrites the live
+    partials, the partial LSEs, the outputs and their LSEs bit for bit as the
+    eager launches wrote them (whose oracle parity the test above checks);
+    between replays the buffers are overwritten by eager work."""
+    p = synth.make_config(cfg)
+    dp = DeviceProblem(p, partial_layout="row")
+    dp.plan()
+    dp.attend()
+    dp.combine()
+    torch.cuda.synchronize()
+    live = torch.isfinite(dp.partial_lse)
+    ref = [dp.partial_o.clone(), dp.partial_lse.clone(), dp.out.clone(), dp.lse.clone()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dp.plan()
+        dp.attend()
+        dp.combine()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (dp.partial_o, dp.partial_lse, dp.out, dp.lse):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.partial_lse, ref[1]), i
+        assert torch.equal(dp.partial_o[live], ref[0][live]), i  # partial_o viewed [split][row][d]
+        assert torch.equal(dp.out, ref[2]) and torch.equal(dp.lse, ref[3]), i
+    print(f"\n{p.name}: 3 graph replays bitwise equal to the eager step", flush=True)
