@@ -37,7 +37,14 @@ namespace {
 
 constexpr uint64_t kInvalidKey = ~0ull;
 constexpr int kBitmapUnits = 65535;          // largest unit count the bitmap pass takes
-constexpr int64_t kBitmapPassWords = 15360;   // and its LDS budget (60 KiB)
+constexpr int64_t kBitmapPassWords = 15360;   // and its LDS budget (60 KiB) with many planner
+                                               // workgroups (256 threads)
+constexpr int64_t kBitmapPassWordsFew = 28672; // with at most 256 of them (1024 threads, a
+                                               // latency-bound grid): 112 KiB, room for
+                                               // 64 splits of 64 slots
+template <int NT> constexpr int64_t bitmap_budget() {
+  return NT == kGPlanThreadsFew ? kBitmapPassWordsFew : kBitmapPassWords;
+}
 
 // Ascending bitonic sort of n = E * blockDim.x keys held in LDS.  Thread t
 // keeps the keys of sorted positions tE .. tE+E-1 in registers: compare-
@@ -584,7 +591,7 @@ __global__ void __launch_bounds__(NT) gplan_kernel(const GroupArgs a) {
   uint2 *out = (uint2 *)(a.ws + a.lay.lists) + list_base;
   int *soff = (int *)(a.ws + a.lay.split_off) + li * (a.num_splits + 1);
   if (one_req && nunits <= kBitmapUnits &&
-      bitmap_pass_words(nunits, a.list_cap, a.num_splits) <= kBitmapPassWords) {
+      bitmap_pass_words(nunits, a.list_cap, a.num_splits) <= bitmap_budget<NT>()) {
     // one request, units below 2^16: the union straight from bitmaps (done,
     // unless some token selected a unit twice)
     if (a.num_splits == 1 ? union_one_split_by_bitmap<NT>(a, kr, b0, (int)nunits, out, soff, err)
@@ -771,12 +778,12 @@ __global__ void gplan_zero(uint32_t *err) { *err = 0u; }
 }  // namespace
 
 // Dynamic LDS (the sort's keys, or the bitmap pass's words, at most
-// kBitmapPassWords) plus the static wave counters and scan sums.
+// kBitmapPassWordsFew) plus the static wave counters and scan sums.
 size_t grouped_plan_lds_bytes() {
   size_t n = 1;
   while (n < (size_t)kGroupTokens * 512 || n < (size_t)kGPlanThreadsFew) n <<= 1;
   const size_t sort = (n + kGPlanThreadsFew) * 8;
-  const size_t bitmap = (size_t)kBitmapPassWords * 4;
+  const size_t bitmap = (size_t)kBitmapPassWordsFew * 4;
   return (sort > bitmap ? sort : bitmap) + 16 * (kGPlanThreadsFew / 64) * 4 + (kGPlanThreadsFew / 64) * 4;
 }
 
@@ -787,15 +794,24 @@ hipError_t launch_grouped_plan(const GroupArgs &a, hipStream_t s) {
   // the sort's keys, or the bitmap pass's words if that is larger
   size_t lds = ((size_t)a.sort_n + a.plan_threads) * 8;
   const int64_t nunits = (int64_t)a.max_pages * a.page_size / a.unit_tokens;
+  const bool few = a.plan_threads == kGPlanThreadsFew;
   if (nunits <= kBitmapUnits) {
     const int64_t words = bitmap_pass_words(nunits, a.list_cap, a.num_splits);
     const size_t bm = (size_t)words * 4;
-    if (words <= kBitmapPassWords && bm > lds) lds = bm;
+    if (words <= (few ? kBitmapPassWordsFew : kBitmapPassWords) && bm > lds) lds = bm;
   }
-  if (a.plan_threads == kGPlanThreadsFew)
+  if (few) {
+    if (lds > 64 * 1024) {
+      // allow the whole budget once (the function attribute, not a stream operation)
+      static const hipError_t attr =
+          hipFuncSetAttribute((const void *)gplan_kernel<kGPlanThreadsFew>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(kBitmapPassWordsFew * 4));
+      if (attr != hipSuccess) return attr;
+    }
     gplan_kernel<kGPlanThreadsFew><<<grid, kGPlanThreadsFew, lds, s>>>(a);
-  else
+  } else {
     gplan_kernel<kGPlanThreads><<<grid, kGPlanThreads, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -196,10 +196,13 @@ def test_grouped_splits_bitwise_repeatable():
         assert all(torch.equal(x, y) for x, y in zip(snaps[0], s))
 
 
-def test_page4_small_chunk_workload():
-    """The small-chunk workload at its full size (48 rows, 512 units per row,
-    16 splits), every row against the oracle."""
-    p = synth.make_page4_small_chunk(ctx_len=24240)
+@pytest.mark.parametrize("ctx_len,spp", [(24240, 32), (150288, 16), (150288, 8)])
+def test_page4_small_chunk_workload(ctx_len, spp):
+    """The small-chunk workload at its full size (48 rows, 512 units per row;
+    16, 32 and 64 splits), every row against the oracle.  Over 150K tokens of
+    context 32 and 64 splits take the planner's bitmap pass with more than
+    64 KiB of LDS (its latency-mode budget)."""
+    p = synth.make_page4_small_chunk(ctx_len=ctx_len, slots_per_split=spp)
     _parity(p)
 
 
