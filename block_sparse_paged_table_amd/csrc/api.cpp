@@ -46,6 +46,8 @@ int esize(int dt) {
 }
 
 constexpr int kPageRouteRowsPerUnit = 1024;  // (token, head) rows per work unit (at most)
+constexpr int kPageRouteMinRows = 64;         // rows per unit never cut below one 16-row tile per wave
+constexpr int64_t kPageRouteMinUnits = 512;   // two units per compute unit before units shrink
 constexpr int kMaxDevices = 64;               // devices the per-device caches cover
 
 // Route of a descriptor (page selections), or -1.
@@ -268,6 +270,15 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
   const int64_t L = (int64_t)d->num_seqs * d->max_pages * d->num_kv_heads;
   const int64_t NS = (int64_t)d->total_q * d->num_kv_heads * d->num_slots;
   if (L >= (1ll << 24)) return fail(MSA_ERR_UNSUPPORTED, "too many page lists");
+  // Small problems: with 1024-row units a few thousand selections make a
+  // handful of workgroups, each walking its rows one tile per wave at a time.
+  // Shrink the units toward two per compute unit (each still reads its page
+  // once); large problems keep the 1024-row units, which amortise the page
+  // load best.
+  if (NS < kPageRouteMinUnits * r.chunk) {
+    const int floor_e = std::min<int>(r.chunk, (kPageRouteMinRows + r.G - 1) / r.G);
+    r.chunk = (int32_t)std::max<int64_t>(floor_e, (NS + kPageRouteMinUnits - 1) / kPageRouteMinUnits);
+  }
   if (d->order_slice_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "order_slice_tokens < 0");
 
   // Ordering slices: the plan keeps one list per (slice, KV head, request,
