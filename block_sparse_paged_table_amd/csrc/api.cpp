@@ -279,6 +279,7 @@ msa_status check_desc(const msa_prefill_desc *d, PageArgs *a, GroupArgs *ga, boo
     const int floor_e = std::min<int>(r.chunk, (kPageRouteMinRows + r.G - 1) / r.G);
     r.chunk = (int32_t)std::max<int64_t>(floor_e, (NS + kPageRouteMinUnits - 1) / kPageRouteMinUnits);
   }
+  r.chunk_magic = ((1ull << 32) + (uint64_t)r.chunk - 1) / (uint64_t)r.chunk;
   if (d->order_slice_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "order_slice_tokens < 0");
 
   // Ordering slices: the plan keeps one list per (slice, KV head, request,

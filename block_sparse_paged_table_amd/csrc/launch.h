@@ -17,6 +17,7 @@ enum Route : int { kRouteF32 = 0, kRouteBF16 = 1, kRouteF16 = 2, kRouteQ8KV4 = 3
 struct PageArgs {
   int32_t num_seqs, total_q, Hq, Hkv, G, D, page_size, num_slots, max_pages, num_phys_pages;
   int32_t chunk;              // entries per work unit
+  uint64_t chunk_magic;       // ceil(2^32 / chunk): x / chunk = (x * chunk_magic) >> 32 for x < 2^24
   int32_t slice_rows;         // (token, KV head) rows per ordering slice, multiple of 256
   int32_t lists_per_slice;    // Hkv * num_seqs * max_pages (KV head outermost)
   int32_t route;

@@ -4,8 +4,8 @@
 // workgroup per (page, head, query split)).
 //
 //   plan_zero  : clear the per-list counters and the error word
-//   plan_count : per (token, KV head) -- validate every slot, write
-//                lse = -inf for each empty slot, and give every used slot its
+//   plan_count : per (token, KV head, slot), one lane each -- validate, write
+//                lse = -inf for an empty slot, and give a used slot its
 //                position inside its (slice, KV head, request, logical page)
 //                list.  Slices are runs of slice_rows (token, KV head) rows;
 //                listing them outermost makes the work units come out slice
@@ -29,8 +29,18 @@
 namespace msa {
 namespace {
 
-constexpr int kPlanThreads = 64;  // plan_fill: one (token, KV head) row per thread, many workgroups
-constexpr int kMaxLdsLists = 16384;  // lists an LDS histogram may hold (64 KiB)
+constexpr int kPlanThreads = 256;  // plan_fill workgroups
+
+// Marks v as produced here.  After a batch of loads, pinning each result
+// makes all of them complete before any is used (one wait for the batch):
+// without it the compiler turns a select on a uniform condition, such as
+// `j < K ? x[j] : 0`, into a branch and moves the load inside, which leaves
+// one load and one full wait per slot -- sixteen round trips where one does.
+template <class T>
+__device__ __forceinline__ void pin(T &v) {
+  __asm__ volatile("" : "+v"(v));
+}
+constexpr int kMaxLdsLists = 15360;  // lists an LDS histogram may hold (60 KiB, + 4 KiB of slot order)
 
 __global__ void plan_zero(int32_t *counts, int64_t n, uint32_t *err) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -58,47 +68,72 @@ __device__ __forceinline__ RowCtx row_ctx(const PageArgs &a, int r, uint32_t &er
   return c;
 }
 
-// Rows per plan_count workgroup (slice_rows is a multiple of both): 64 keeps
-// many workgroups in flight; 256 when a slice has many lists, since every
-// workgroup clears and claims all of its slice's lists.
-constexpr int kCountThreads = 64;
-constexpr int kCountThreadsWide = 256;
-constexpr int kCountWideLists = 2048;  // lists per slice from which the wide form is used
-constexpr int kRegSlots = 16;      // rows with at most this many slots keep them in registers
+// plan_count puts the K slots of a (token, KV head) row on K adjacent lanes
+// (K <= 64; rpw = the largest power of two <= 64 / K rows per wave, at most
+// 16), so that every load and store of the slot arrays is one contiguous run
+// per wave and each lane validates one slot; with K > 64 a row takes a whole
+// wave and each lane walks slots lane, lane + 64, ...  (One row per thread
+// walking its K slots had each wave serialise K rounds of branches and
+// scattered stores; a loop over several row groups per workgroup was slower
+// than more workgroups.)  A workgroup's 16 rpw rows, a power of two <= 256,
+// lie within one ordering slice (slice_rows is a multiple of 256).  The
+// workgroup takes its list positions in (slot, row) order; with 1024
+// threads (64 rows at K = 16) that order kept the attention kernel as fast
+// as before, where 256-thread workgroups (16 rows) cost it 4-5 % on the
+// 4 x 4096 BF16 workload -- the order in which a list's entries reach the
+// partial-output slabs matters to its write stream.
+constexpr int kCountThreads = 1024;
+constexpr int kClaimBatch = 8;           // list claims (returning atomics) in flight per thread
+
+// log2 of the rows per wave for K slots: the most rows of K lanes that fit
+// in 64, at most 16.
+__host__ __device__ inline int count_rpw_log2(int K) {
+  int l = 0;
+  while (l < 4 && K <= 32 >> l) ++l;
+  return l;
+}
 
 template <bool LDS_HIST, int NT>
 __global__ void __launch_bounds__(NT) plan_count(const PageArgs a) {
   extern __shared__ int32_t hist[];
   const int64_t L = a.lists_per_slice;
-  const int tid = threadIdx.x;
-  // slice_rows is a multiple of the block size: one slice per workgroup
-  const int64_t lbase = ((int64_t)blockIdx.x * NT) / a.slice_rows * L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.num_slots;
+  const int lpr = min(K, 64);  // lanes per row
+  const int rpw = 1 << count_rpw_log2(K);
+  const int64_t row0 = (int64_t)blockIdx.x * (NT / 64) * rpw;
+  const int64_t lbase = row0 / a.slice_rows * L;
+  const int64_t rows = (int64_t)a.total_q * a.Hkv;
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
+  int32_t *slot_list_all = (int32_t *)(a.ws + a.lay.slot_list);
+  int32_t *slot_pos_all = (int32_t *)(a.ws + a.lay.slot_pos);
+  // empty splits get lse = -inf for the G heads of the row, 16 bytes at a
+  // time where the layout allows
+  const bool lse4 = ((uintptr_t)a.partial_lse & 15) == 0 && (a.pl_split_stride & 3) == 0 &&
+                    (a.Hq & 3) == 0 && (a.G & 3) == 0;
   if constexpr (LDS_HIST) {
     for (int64_t i = tid; i < L; i += NT) hist[i] = 0;
     __syncthreads();
   }
-  const int64_t idx = (int64_t)blockIdx.x * NT + tid;
-  const bool live = idx < (int64_t)a.total_q * a.Hkv;
-  const int K = a.num_slots;
-  int32_t *slot_list = (int32_t *)(a.ws + a.lay.slot_list) + idx * K;
-  int32_t *slot_pos = (int32_t *)(a.ws + a.lay.slot_pos) + idx * K;
-  // rows of at most kRegSlots slots keep each slot's list (local index, -1:
-  // none) and its position in the workgroup's block in registers until the
-  // block offsets are known, and store the final position once
-  int lr[kRegSlots], pr[kRegSlots];
-#pragma unroll
-  for (int j = 0; j < kRegSlots; ++j) lr[j] = -1, pr[j] = 0;
-  if (live) {
-    const int r = (int)(idx / a.Hkv), g = (int)(idx - (int64_t)r * a.Hkv);
+  const int rr = lane / lpr, j0 = lane - rr * lpr;  // row in the wave, first slot
+  const int RW = (NT / 64) * rpw;                    // rows of the workgroup
+  __shared__ int32_t s_q[NT];  // K <= 64: (slot, row) -> list, then -> position (K RW <= NT)
+  int lr = -1, pr = 0;         // K <= 64: this lane's list (local, -1: none) and position
+  {
+    const int64_t idx = row0 + (int64_t)wave * rpw + rr;
+    const bool live = rr < rpw && idx < rows;
+    const int64_t ridx = live ? idx : 0;  // dead lanes read row 0 (rows >= 1 when launched)
+    const int r = (int)(ridx / a.Hkv), g = (int)(ridx - (int64_t)r * a.Hkv);
     const int32_t *sidx = a.sel_idx + r * a.sel_stride_tok + g * a.sel_stride_head;
     const uint8_t *smask = a.sel_mask + r * a.sel_stride_tok + g * a.sel_stride_head;
+    int32_t *slot_list = slot_list_all + ridx * K;
+    int32_t *slot_pos = slot_pos_all + ridx * K;
     uint32_t err = 0;
     const RowCtx c = row_ctx(a, r, err);
     const int bb = c.valid ? c.b : 0;  // an in-bounds table row for the loads below
-    // slot j: validate, find its list, claim a position (or mark the split
-    // empty); returns the list (-1: none) and, in `pos`, the position claimed
-    auto visit = [&](int j, uint32_t mk, int u, bool dup, int pp, int &pos, bool store_pos) -> int {
+    // slot j: validate, find its list (local index, -1: none) and record it
+    // -- or mark the split empty
+    auto visit = [&](int j, uint32_t mk, int u, bool dup, int pp) -> int {
       int list = -1;
       if (c.valid && mk) {
         if (u < 0 || u >= a.max_pages) {
@@ -113,70 +148,90 @@ __global__ void __launch_bounds__(NT) plan_count(const PageArgs a) {
         }
       }
       slot_list[j] = list >= 0 ? (int32_t)(lbase + list) : -1;
-      if (list >= 0) {
-        pos = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[lbase + list], 1);
-        if (store_pos) slot_pos[j] = pos;
-      } else {
+      if (list < 0) {
         float *pl = a.partial_lse + j * a.pl_split_stride + (int64_t)r * a.Hq + g * a.G;
-        for (int h = 0; h < a.G; ++h) pl[h] = -INFINITY;
+        if (lse4) {
+          for (int h = 0; h < a.G; h += 4) *(float4 *)(pl + h) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        } else {
+          for (int h = 0; h < a.G; ++h) pl[h] = -INFINITY;
+        }
       }
       return list;
     };
-    if (K <= kRegSlots) {
-      // every load of the row is issued before any is used; the duplicate
-      // test runs on registers
-      uint32_t mk[kRegSlots];
-      int uu[kRegSlots], pp[kRegSlots];
-#pragma unroll
-      for (int j = 0; j < kRegSlots; ++j) {
-        const int jc = j < K ? j : 0;
-        mk[j] = j < K ? (uint32_t)smask[jc] : 0u;
-        uu[j] = sidx[jc];
+    if (K <= 64) {
+      uint32_t mk = smask[j0];
+      int u = sidx[j0];
+      pin(mk);
+      pin(u);
+      const int uc = (u >= 0 && u < a.max_pages) ? u : 0;
+      const int pp = a.page_table[bb * a.pt_stride + uc];
+      // duplicate: an earlier slot of the row with a mask and the same page
+      // (all lanes shuffle; a row's lanes live or die together)
+      const int key = mk ? u : INT_MIN;
+      const int rb = rr * lpr;
+      bool dup = false;
+      for (int jj = 0; jj + 1 < lpr; ++jj) {
+        const int kj = __shfl(key, (rb + jj) & 63);
+        dup |= jj < j0 && kj == u;
       }
-#pragma unroll
-      for (int j = 0; j < kRegSlots; ++j) {
-        const int uc = (uu[j] >= 0 && uu[j] < a.max_pages) ? uu[j] : 0;
-        pp[j] = a.page_table[bb * a.pt_stride + uc];
-      }
-#pragma unroll
-      for (int j = 0; j < kRegSlots; ++j) {
-        if (j < K) {
-          bool dup = false;
-#pragma unroll
-          for (int jj = 0; jj < j; ++jj) dup |= (mk[jj] != 0u) && (uu[jj] == uu[j]);
-          lr[j] = visit(j, mk[j], uu[j], dup, pp[j], pr[j], !LDS_HIST);
-        }
-      }
-    } else {
-      for (int j = 0; j < K; ++j) {
+      if (live) lr = visit(j0, mk, u, dup, pp);
+      if (!LDS_HIST && lr >= 0) slot_pos[j0] = atomicAdd(&counts[lbase + lr], 1);
+      if (LDS_HIST && rr < rpw) s_q[j0 * RW + wave * rpw + rr] = lr;
+    } else if (live) {
+      // one row per wave (rr = 0); lane j0 takes slots j0, j0 + 64, ...
+      for (int j = j0; j < K; j += 64) {
         const uint32_t mk = smask[j];
         const int u = sidx[j];
         bool dup = false;
         for (int jj = 0; jj < j; ++jj) dup |= (smask[jj] != 0) && (sidx[jj] == u);
         const int uc = (u >= 0 && u < a.max_pages) ? u : 0;
-        int pos = 0;
-        visit(j, mk, u, dup, a.page_table[bb * a.pt_stride + uc], pos, true);
+        const int list = visit(j, mk, u, dup, a.page_table[bb * a.pt_stride + uc]);
+        if (list >= 0) slot_pos[j] = LDS_HIST ? atomicAdd(&hist[list], 1) : atomicAdd(&counts[lbase + list], 1);
       }
     }
-    if (err) atomicOr(a.err_flags, err);
+    if (live && err) atomicOr(a.err_flags, err);
   }
   if constexpr (LDS_HIST) {
-    __syncthreads();
-    for (int64_t i = tid; i < L; i += NT) {
-      const int32_t n = hist[i];
-      if (n) hist[i] = atomicAdd(&counts[lbase + i], n);  // this workgroup's block of list i
+    if (K <= 64) {
+      // positions in the workgroup's blocks, taken by one wave walking the
+      // slots in (slot, row) order: a list's entries then come slot by slot,
+      // rows ascending
+      __syncthreads();
+      if (wave == 0) {
+        for (int q = lane; q < K * RW; q += 64) {
+          const int l = s_q[q];
+          if (l >= 0) s_q[q] = atomicAdd(&hist[l], 1);
+        }
+      }
+      __syncthreads();
+      if (lr >= 0) pr = s_q[j0 * RW + wave * rpw + rr];
     }
     __syncthreads();
-    if (live) {
-      if (K <= kRegSlots) {
+    // this workgroup's block of each list it touches: the returning atomics
+    // go out kClaimBatch at a time, so their round trips overlap
+    for (int64_t i0 = tid; i0 < L; i0 += (int64_t)NT * kClaimBatch) {
+      int32_t n[kClaimBatch], o[kClaimBatch];
 #pragma unroll
-        for (int j = 0; j < kRegSlots; ++j)
-          if (lr[j] >= 0) slot_pos[j] = pr[j] + hist[lr[j]];
-      } else {
-        for (int j = 0; j < K; ++j) {
-          const int list = slot_list[j];
-          if (list >= 0) slot_pos[j] += hist[list - lbase];
-        }
+      for (int b = 0; b < kClaimBatch; ++b) {
+        const int64_t i = i0 + (int64_t)b * NT;
+        n[b] = i < L ? hist[i] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < kClaimBatch; ++b)
+        o[b] = n[b] ? atomicAdd(&counts[lbase + i0 + (int64_t)b * NT], n[b]) : 0;
+#pragma unroll
+      for (int b = 0; b < kClaimBatch; ++b)
+        if (n[b]) hist[i0 + (int64_t)b * NT] = o[b];
+    }
+    __syncthreads();
+    // positions within the workgroup's blocks -> within the lists
+    const int64_t idx = row0 + (int64_t)wave * rpw + rr;
+    if (K <= 64) {
+      if (lr >= 0) slot_pos_all[idx * K + j0] = pr + hist[lr];
+    } else if (rr < rpw && idx < rows) {
+      for (int j = j0; j < K; j += 64) {  // (the slot records this thread wrote, read back)
+        const int list = slot_list_all[idx * K + j];
+        if (list >= 0) slot_pos_all[idx * K + j] += hist[list - lbase];
       }
     }
   }
@@ -195,11 +250,21 @@ constexpr int kScanOneBlockMax = kScanThreads * 8;  // lists one workgroup scans
 // ceil(n / chunk) units of n / units entries each; its class is 0 for units
 // of at least chunk/2 entries, 1 for chunk/4, 2 for chunk/8, else 3.
 constexpr int kSizeClasses = 4;
-__device__ __forceinline__ int units_of(int32_t n, int chunk) { return (n + chunk - 1) / chunk; }
-__device__ __forceinline__ int size_class(const PageArgs &a, int32_t n) {
-  if (a.lay.num_lists != a.lists_per_slice) return 0;
-  const int32_t s = n / max(1, units_of(n, a.chunk));  // entries per unit (rounded down)
-  return 2 * s >= a.chunk ? 0 : (4 * s >= a.chunk ? 1 : (8 * s >= a.chunk ? 2 : 3));
+// ceil(n / chunk) by a multiply: a list holds at most total_q < 2^23 entries,
+// so x = n + chunk - 1 < 2^24, and x * ceil(2^32 / chunk) / 2^32 exceeds
+// x / chunk by less than x / 2^32 < 1 / chunk -- too little to reach the
+// next integer.
+__device__ __forceinline__ int units_of(const PageArgs &a, int32_t n) {
+  return (int)(((uint64_t)(uint32_t)(n + a.chunk - 1) * a.chunk_magic) >> 32);
+}
+__device__ __forceinline__ bool classed(const PageArgs &a) { return a.lay.num_lists == a.lists_per_slice; }
+// Class of a list of n entries in u units: s = floor(n / max(1, u)) entries
+// per unit against chunk/2, chunk/4, chunk/8.  For integer s and k,
+// k s >= chunk exactly when s >= ceil(chunk / k), i.e. n >= u ceil(chunk / k).
+__device__ __forceinline__ int size_class(const PageArgs &a, int32_t n, int32_t u) {
+  if (!classed(a)) return 0;
+  const int32_t v = max(1, u);
+  return n >= v * ((a.chunk + 1) >> 1) ? 0 : (n >= v * ((a.chunk + 3) >> 2) ? 1 : (n >= v * ((a.chunk + 7) >> 3) ? 2 : 3));
 }
 
 // Per-class unit counts of one thread's lists, and its running offsets.
@@ -211,31 +276,45 @@ struct ClassCounts {
 // thread -- inclusive scans within each wave by shuffles, the wave totals
 // through LDS behind a single barrier -- and writes the final offsets:
 // list_off (entries) in list order, unit_off (the list's first unit) in
-// (size class, list) order.
-template <int PER>
+// (size class, list) order.  Thread t scans lists [PER t, PER t + PER), but
+// global memory is read and written through an LDS transpose (element
+// k * threads + t by thread t): per-thread runs of PER words gave every load
+// and store instruction 64 scattered words, and the one workgroup's CU spent
+// most of the kernel issuing them.
+// NC = kSizeClasses with one ordering slice, else 1 (every unit in class 0:
+// the class sums then cost nothing).
+template <int PER, int NC>
 __global__ void __launch_bounds__(kScanThreads) plan_scan_one(const PageArgs a) {
   constexpr int NW = kScanThreads / 64;
-  constexpr int NC = kSizeClasses;
   __shared__ int32_t w_e[NW], w_u[NC][NW];
+  __shared__ int32_t s_x[kScanThreads * PER];  // the transpose buffer
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t L = a.lay.num_lists;
   const int32_t *counts = (const int32_t *)(a.ws + a.lay.counts);
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
-  const int64_t i0 = (int64_t)t * PER;
-  int32_t c[PER];
+  int32_t c[PER], cls[PER], nun[PER];
+  // unconditional loads (clamped index; L >= 1), all in flight at once;
+  // lists past L count 0
+#pragma unroll
+  for (int k = 0; k < PER; ++k) c[k] = counts[min((int64_t)k * kScanThreads + t, L - 1)];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    pin(c[k]);
+    s_x[k * kScanThreads + t] = (int64_t)k * kScanThreads + t < L ? c[k] : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k) c[k] = s_x[t * PER + k];
   int32_t se = 0;
   ClassCounts su = {};
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    // unconditional loads (clamped index; L >= 1), so that all of them are
-    // in flight at once instead of one branch and wait per list
-    const int32_t v = counts[min(i0 + k, L - 1)];
-    c[k] = i0 + k < L ? v : 0;
     se += c[k];
-    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+    nun[k] = units_of(a, c[k]);
+    cls[k] = NC == 1 ? 0 : size_class(a, c[k], nun[k]);
 #pragma unroll
-    for (int q = 0; q < NC; ++q) su.v[q] += q == cl ? u : 0;
+    for (int q = 0; q < NC; ++q) su.v[q] += q == cls[k] ? nun[k] : 0;
   }
   int32_t ie = se;  // inclusive scans over the wave's lanes
   ClassCounts iu = su;
@@ -275,20 +354,31 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_one(const PageArgs a) 
     bu.v[q] = base + ou.v[q] + iu.v[q] - su.v[q];
     base += tot.v[q];
   }
+  // unit offsets through the buffer (each thread rewrites only its own run,
+  // which only it has read), then the entry offsets
+  int32_t eo[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
     int32_t uo = bu.v[0];
 #pragma unroll
-    for (int q = 1; q < NC; ++q) uo = q == cl ? bu.v[q] : uo;
-    if (i0 + k < L) {
-      list_off[i0 + k] = be;
-      unit_off[i0 + k] = uo;
-    }
+    for (int q = 1; q < NC; ++q) uo = q == cls[k] ? bu.v[q] : uo;
+    s_x[t * PER + k] = uo;
+    eo[k] = be;
     be += c[k];
 #pragma unroll
-    for (int q = 0; q < NC; ++q) bu.v[q] += q == cl ? u : 0;
+    for (int q = 0; q < NC; ++q) bu.v[q] += q == cls[k] ? nun[k] : 0;
   }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if ((int64_t)k * kScanThreads + t < L) unit_off[k * kScanThreads + t] = s_x[k * kScanThreads + t];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k) s_x[t * PER + k] = eo[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if ((int64_t)k * kScanThreads + t < L) list_off[k * kScanThreads + t] = s_x[k * kScanThreads + t];
   if (t == kScanThreads - 1) {
     int32_t *meta = (int32_t *)(a.ws + a.lay.meta);
     list_off[L] = be;
@@ -314,17 +404,20 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
   int32_t *list_off = (int32_t *)(a.ws + a.lay.list_off);
   int32_t *unit_off = (int32_t *)(a.ws + a.lay.unit_off);
   const int64_t i0 = (int64_t)blockIdx.x * (kScanThreads * PER) + (int64_t)t * PER;
-  int32_t c[PER];
+  int32_t c[PER], cls[PER], nun[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) c[k] = counts[min(i0 + k, L - 1)];
   int32_t se = 0;
   ClassCounts su = {};
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int32_t v = counts[min(i0 + k, L - 1)];
-    c[k] = i0 + k < L ? v : 0;
+    pin(c[k]);
+    c[k] = i0 + k < L ? c[k] : 0;
     se += c[k];
-    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
+    nun[k] = units_of(a, c[k]);
+    cls[k] = NC == 1 ? 0 : size_class(a, c[k], nun[k]);
 #pragma unroll
-    for (int q = 0; q < NC; ++q) su.v[q] += q == cl ? u : 0;
+    for (int q = 0; q < NC; ++q) su.v[q] += q == cls[k] ? nun[k] : 0;
   }
   s_e[t] = se;
 #pragma unroll
@@ -347,17 +440,16 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_tiles(const PageArgs a
   for (int q = 0; q < NC; ++q) bu.v[q] = s_u[q][t] - su.v[q];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int cl = size_class(a, c[k]), u = units_of(c[k], a.chunk);
     int32_t uo = bu.v[0];
 #pragma unroll
-    for (int q = 1; q < NC; ++q) uo = q == cl ? bu.v[q] : uo;
+    for (int q = 1; q < NC; ++q) uo = q == cls[k] ? bu.v[q] : uo;
     if (i0 + k < L) {
       list_off[i0 + k] = be;
       unit_off[i0 + k] = uo;
     }
     be += c[k];
 #pragma unroll
-    for (int q = 0; q < NC; ++q) bu.v[q] += q == cl ? u : 0;
+    for (int q = 0; q < NC; ++q) bu.v[q] += q == cls[k] ? nun[k] : 0;
   }
   if (t == kScanThreads - 1) {  // this tile's totals, for plan_scan_top
     int32_t *tiles = (int32_t *)(a.ws + a.lay.tiles) + (int64_t)blockIdx.x * kTileWords;
@@ -444,7 +536,8 @@ __global__ void __launch_bounds__(kScanThreads) plan_scan_add(const PageArgs a) 
   const int64_t i0 = (int64_t)tile * kScanTile;
   for (int k = threadIdx.x; k < kScanTile; k += kScanThreads)
     if (i0 + k < L) {
-      const int cl = size_class(a, counts[i0 + k]);
+      const int32_t n = counts[i0 + k];
+      const int cl = size_class(a, n, units_of(a, n));
       int32_t o = ou.v[0];
 #pragma unroll
       for (int q = 1; q < kSizeClasses; ++q) o = q == cl ? ou.v[q] : o;
@@ -471,26 +564,32 @@ __device__ __forceinline__ void write_units(const PageArgs &a, int64_t l) {
   w.g = pl / (a.max_pages * a.num_seqs);
   w.phys = a.page_table[b * a.pt_stride + u];
   PageUnit *units = (PageUnit *)(a.ws + a.lay.units) + u0;
-  const int32_t nu = (n + a.chunk - 1) / a.chunk;  // the list's entries split evenly
+  // the list's entries split evenly: the first n % nu units take one more
+  const int32_t nu = units_of(a, n), q = n / nu, rem = n - q * nu;
+  int32_t b0 = lo;
   for (int32_t c = 0; c < nu; ++c) {
-    const int32_t b0 = (int32_t)((int64_t)c * n / nu), b1 = (int32_t)((int64_t)(c + 1) * n / nu);
-    w.e_begin = lo + b0;
-    w.e_count = b1 - b0;
+    w.e_begin = b0;
+    w.e_count = q + (c < rem ? 1 : 0);
+    b0 += w.e_count;
     units[c] = w;
   }
 }
 
-// Blocks [0, fill_blocks): one (token, KV head) row per thread, its entries
-// into the lists; the blocks after them: one list per thread, its units.
+// Blocks [0, fill_blocks): the rows' slots, one per lane as in plan_count
+// (K <= 64: K adjacent lanes per row; else a wave per row, each lane taking
+// every 64th slot); the blocks after them: one list per thread, its units.
 __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a, int fill_blocks) {
   if ((int)blockIdx.x >= fill_blocks) {
     write_units(a, (int64_t)(blockIdx.x - fill_blocks) * kPlanThreads + threadIdx.x);
     return;
   }
-  const int64_t idx = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
-  if (idx >= (int64_t)a.total_q * a.Hkv) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = a.num_slots, lpr = min(K, 64);
+  const int rpw = 1 << count_rpw_log2(K);
+  const int rr = lane / lpr, j0 = lane - rr * lpr;
+  const int64_t idx = ((int64_t)blockIdx.x * (kPlanThreads / 64) + wave) * rpw + rr;
+  if (rr >= rpw || idx >= (int64_t)a.total_q * a.Hkv) return;
   const int r = (int)(idx / a.Hkv), g = (int)(idx - (int64_t)r * a.Hkv);
-  const int K = a.num_slots;
   const int32_t *sidx = a.sel_idx + r * a.sel_stride_tok + g * a.sel_stride_head;
   const int32_t *slot_list = (const int32_t *)(a.ws + a.lay.slot_list) + idx * K;
   const int32_t *slot_pos = (const int32_t *)(a.ws + a.lay.slot_pos) + idx * K;
@@ -498,7 +597,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a, int 
   PlanEntry *entries = (PlanEntry *)(a.ws + a.lay.entries);
   uint32_t err = 0;
   const RowCtx c = row_ctx(a, r, err);
-  for (int j = 0; j < K; ++j) {
+  for (int j = j0; j < K; j += 64) {
     const int list = slot_list[j];
     if (list < 0) continue;
     PlanEntry e;
@@ -510,7 +609,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_fill(const PageArgs a, int 
 
 }  // namespace
 
-size_t page_plan_lds_bytes() { return (size_t)kMaxLdsLists * 4; }  // plan_count's histogram
+size_t page_plan_lds_bytes() { return (size_t)kMaxLdsLists * 4 + kCountThreads * 4; }  // plan_count
 
 hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   int32_t *counts = (int32_t *)(a.ws + a.lay.counts);
@@ -518,24 +617,23 @@ hipError_t launch_page_plan(const PageArgs &a, hipStream_t s) {
   const int64_t zero_blocks = (L + 255) / 256 > 0 ? (L + 255) / 256 : 1;
   plan_zero<<<(unsigned)zero_blocks, 256, 0, s>>>(counts, L, a.err_flags);
   const int64_t rows = (int64_t)a.total_q * a.Hkv;
-  const unsigned blocks = (unsigned)((rows + kPlanThreads - 1) / kPlanThreads);
+  auto row_blocks = [&](int64_t per) { return (unsigned)((rows + per - 1) / per); };
+  const unsigned blocks = row_blocks((int64_t)(kPlanThreads / 64) << count_rpw_log2(a.num_slots));
   if (rows > 0) {
     const size_t hist_bytes = (size_t)a.lists_per_slice * 4;
-    if (a.lists_per_slice > kMaxLdsLists) {
-      plan_count<false, kCountThreads><<<(unsigned)((rows + kCountThreads - 1) / kCountThreads),
-                                         kCountThreads, 0, s>>>(a);
-    } else if (a.lists_per_slice > kCountWideLists) {
-      plan_count<true, kCountThreadsWide><<<(unsigned)((rows + kCountThreadsWide - 1) / kCountThreadsWide),
-                                            kCountThreadsWide, hist_bytes, s>>>(a);
-    } else {
-      plan_count<true, kCountThreads><<<(unsigned)((rows + kCountThreads - 1) / kCountThreads),
-                                        kCountThreads, hist_bytes, s>>>(a);
-    }
+    const unsigned cblocks = row_blocks((kCountThreads / 64) << count_rpw_log2(a.num_slots));
+    if (a.lists_per_slice > kMaxLdsLists)
+      plan_count<false, kCountThreads><<<cblocks, kCountThreads, 0, s>>>(a);
+    else
+      plan_count<true, kCountThreads><<<cblocks, kCountThreads, hist_bytes, s>>>(a);
   }
+  const bool cl = L == a.lists_per_slice;  // one ordering slice: units by size class
   if (L <= kScanTile) {
-    plan_scan_one<kScanPer><<<1, kScanThreads, 0, s>>>(a);
+    if (cl) plan_scan_one<kScanPer, kSizeClasses><<<1, kScanThreads, 0, s>>>(a);
+    else plan_scan_one<kScanPer, 1><<<1, kScanThreads, 0, s>>>(a);
   } else if (L <= kScanOneBlockMax) {
-    plan_scan_one<kScanOneBlockMax / kScanThreads><<<1, kScanThreads, 0, s>>>(a);
+    if (cl) plan_scan_one<kScanOneBlockMax / kScanThreads, kSizeClasses><<<1, kScanThreads, 0, s>>>(a);
+    else plan_scan_one<kScanOneBlockMax / kScanThreads, 1><<<1, kScanThreads, 0, s>>>(a);
   } else {
     const int nt = (int)((L + kScanTile - 1) / kScanTile);
     plan_scan_tiles<<<nt, kScanThreads, 0, s>>>(a);
