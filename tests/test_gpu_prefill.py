@@ -193,6 +193,24 @@ def test_error_flags_and_invalid_rows():
     assert dp.err_flags() == 1 | 2 | 4 | 8
 
 
+@pytest.mark.parametrize("K", [1, 2, 3, 17, 33, 64, 65, 100])
+def test_slot_counts_and_duplicates(K):
+    """Slot counts around the plan's lane mapping (a row's K slots on K
+    adjacent lanes up to 64 -- 16, 16, 16, 2, 1 and 1 rows per wave here --
+    and a whole wave per row beyond), mostly empty slots (few pages exist),
+    and a duplicate selection at a late or an early slot."""
+    p = _small(40 + K, num_slots=K, Hq=8, Hkv=2, pad_rows=3)
+    if K > 1:
+        si, sm = p.sel_idx.numpy().copy(), p.sel_mask.numpy().copy()
+        t = 600
+        src = int(np.nonzero(sm[t, 1])[0][0])
+        dst = K - 1 if src != K - 1 else 0
+        si[t, 1, dst], sm[t, 1, dst] = si[t, 1, src], 1
+        p = dataclasses.replace(p, sel_idx=torch.from_numpy(si), sel_mask=torch.from_numpy(sm))
+    dp, _, _ = _full_parity(p)
+    assert dp.err_flags() == (8 if K > 1 else 0)
+
+
 def test_empty_and_all_padding_batches():
     """total_q = 0 launches nothing and touches nothing; a batch of padding rows
     only gives +0 outputs, lse = -inf and every split empty."""
