@@ -227,7 +227,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int &total) {
 // LDS words the bitmap pass needs (sizing on the host and checks here).
 __host__ __device__ inline int64_t bitmap_pass_words(int64_t nunits, int64_t cap, int64_t splits) {
   const int64_t nw = (nunits + 31) / 32, pw = (cap + 31) / 32;
-  if (splits == 1) return 2 * nw + cap + kGroupTokens * pw;  // union_one_split_by_bitmap
+  if (splits == 1) return 2 * nw + 2 * cap + kGroupTokens * pw;  // union_one_split_by_bitmap
   return 2 * nw + (cap + 1) / 2 + 2 * splits * pw + cap + kGroupTokens * pw;
 }
 
@@ -397,7 +397,8 @@ __device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64
 // first-slot rule (returns false).  Units no row sees (mask 0) are dropped,
 // as by the sort path; the list and split offsets it writes are the same.
 // LDS (the keys array, reused): bitmap and rank bases of ceil(nunits / 32)
-// words each, a mask word per union entry and 8 presence bits per entry.
+// words each, a mask word and a unit id per union entry and 8 presence bits
+// per entry.
 template <int NT, int JI>
 __device__ __forceinline__ bool union_one_split_by_bitmap(const GroupArgs &a, const uint64_t (&kr)[kGroupTokens][JI],
                                                 int b0, int nunits, uint2 *out, int *soff, uint32_t &err) {
@@ -410,6 +411,7 @@ __device__ __forceinline__ bool union_one_split_by_bitmap(const GroupArgs &a, co
   uint32_t *pre = bm + nw;
   uint32_t *msk = pre + nw;
   uint32_t *pres = msk + cap;
+  uint32_t *uor = pres + kGroupTokens * pw;  // unit of each rank
   for (int e = t; e < nw; e += NT) bm[e] = 0u;
   for (int e = t; e < cap; e += NT) msk[e] = 0u;
   for (int e = t; e < kGroupTokens * pw; e += NT) pres[e] = 0u;
@@ -436,7 +438,7 @@ __device__ __forceinline__ bool union_one_split_by_bitmap(const GroupArgs &a, co
     int run = base;
     for (int w = w0; w < w1; ++w) {
       pre[w] = (uint32_t)run;
-      run += __popc(bm[w]);
+      for (uint32_t bits = bm[w]; bits; bits &= bits - 1u) uor[run++] = (uint32_t)(w * 32 + __builtin_ctz(bits));
     }
   }
   __syncthreads();
@@ -467,6 +469,40 @@ __device__ __forceinline__ bool union_one_split_by_bitmap(const GroupArgs &a, co
   int o = block_exclusive_scan<NT>(nz, total);
   const int upp = a.page_size / a.unit_tokens;  // units per page
   const int32_t *ptrow = a.page_table + (int64_t)max(b0, 0) * a.pt_stride;
+  if (total == nunion) {
+    // (the usual case) every unit of the union is seen by some row: entry r
+    // is rank r, written by thread r mod NT -- four page-table loads in
+    // flight per thread, and each wave's stores one contiguous run
+    for (int r0 = t; r0 < total; r0 += 4 * NT) {
+      int uu[4], phys[4];
+      uint32_t mm[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rc = min(r0 + q * NT, total - 1);
+        uu[q] = (int)uor[rc];
+        mm[q] = msk[rc];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) phys[q] = ptrow[uu[q] / upp];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (r0 + q * NT >= total) continue;
+        uint2 e;
+        if (phys[q] < 0 || phys[q] >= a.num_phys_pages) {
+          err |= MSA_ERRF_PHYS_RANGE;
+          e = make_uint2(0u, 0u);  // mask 0: contributes nothing
+        } else {
+          e = make_uint2(((uint32_t)phys[q] << 5) | (uint32_t)(uu[q] % upp), mm[q]);
+        }
+        out[r0 + q * NT] = e;
+      }
+    }
+    if (t == 0) {
+      soff[0] = 0;
+      soff[1] = total;
+    }
+    return true;
+  }
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = bm[w];
     int r = (int)pre[w];
