@@ -228,7 +228,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int &total) {
 __host__ __device__ inline int64_t bitmap_pass_words(int64_t nunits, int64_t cap, int64_t splits) {
   const int64_t nw = (nunits + 31) / 32, pw = (cap + 31) / 32;
   if (splits == 1) return 2 * nw + 2 * cap + kGroupTokens * pw;  // union_one_split_by_bitmap
-  return 2 * nw + (cap + 1) / 2 + 2 * splits * pw + cap + kGroupTokens * pw;
+  return 2 * nw + 2 * ((cap + 1) / 2) + 2 * splits * pw + cap + kGroupTokens * pw;
 }
 
 // The union of a group whose valid rows belong to one request, with units
@@ -259,6 +259,7 @@ __device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64
   uint32_t *epre = ebm + sw;           // entries before each entry word
   uint32_t *msk = epre + sw;           // mask of each entry
   uint32_t *pres = msk + cap;          // (token, rank) presence
+  uint16_t *erank = (uint16_t *)(pres + kGroupTokens * pw);  // rank of each entry
   const uint32_t split_mul = ((1u << 20) + (uint32_t)a.slots_per_split - 1u) / (uint32_t)a.slots_per_split;
   auto split_of = [&](uint64_t k) { return (int)((((uint32_t)(k >> 4) & 0x3ffu) * split_mul) >> 20); };
   auto below = [](uint32_t w, uint32_t bit) { return (uint32_t)__popc(w & ((1u << bit) - 1u)); };
@@ -318,7 +319,8 @@ __device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64
     int run = block_exclusive_scan<NT>(cnt, nent);
     for (int w = w0; w < w1; ++w) {
       epre[w] = (uint32_t)run;
-      run += __popc(ebm[w]);
+      for (uint32_t bits = ebm[w]; bits; bits &= bits - 1u)
+        erank[run++] = (uint16_t)((w % pw) * 32 + __builtin_ctz(bits));
     }
   }
   __syncthreads();
@@ -347,6 +349,38 @@ __device__ __forceinline__ bool union_by_bitmap(const GroupArgs &a, const uint64
   int o = block_exclusive_scan<NT>(nz, total);
   const int upp = a.page_size / a.unit_tokens;  // units per page
   const int32_t *ptrow = a.page_table + (int64_t)max(b0, 0) * a.pt_stride;
+  if (total == (int)epre[sw - 1] + __popc(ebm[sw - 1])) {
+    // (the usual case) no entry drops out: output e is entry e, written by
+    // thread e mod NT -- four page-table loads in flight per thread, and
+    // each wave's stores one contiguous run
+    for (int e0 = t; e0 < total; e0 += 4 * NT) {
+      int uu[4], phys[4];
+      uint32_t mm[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int ec = min(e0 + x * NT, total - 1);
+        uu[x] = uor[erank[ec]];
+        mm[x] = msk[ec];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) phys[x] = ptrow[uu[x] / upp];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (e0 + x * NT >= total) continue;
+        uint2 e;
+        if (phys[x] < 0 || phys[x] >= a.num_phys_pages) {
+          err |= MSA_ERRF_PHYS_RANGE;
+          e = make_uint2(0u, 0u);  // mask 0: contributes nothing
+        } else {
+          e = make_uint2(((uint32_t)phys[x] << 5) | (uint32_t)(uu[x] % upp), mm[x]);
+        }
+        out[e0 + x * NT] = e;
+      }
+    }
+    for (int sp = t; sp < S; sp += NT) soff[sp] = (int)epre[sp * pw];
+    if (t == 0) soff[S] = total;
+    return true;
+  }
   for (int w = w0; w < w1; ++w) {
     if (w % pw == 0) soff[w / pw] = o;
     uint32_t bits = ebm[w];
