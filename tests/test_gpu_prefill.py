@@ -211,6 +211,18 @@ def test_slot_counts_and_duplicates(K):
     assert dp.err_flags() == (8 if K > 1 else 0)
 
 
+@pytest.mark.parametrize("K", [8, 65])
+def test_many_lists_global_count_path(K):
+    """More (request, page) lists per ordering slice than the planner's LDS
+    histogram holds (130 requests x a 121-page table row = 15730 > 15360):
+    the count takes its positions with one global atomic per selection."""
+    ctx = [15360] + [0] * 129
+    chunk = [64] + [32] * 129
+    p = _small(61 + K, num_slots=K, Hq=4, Hkv=1, d=64, ctx_lens=ctx, chunk_lens=chunk, pad_rows=2)
+    assert p.num_seqs * p.max_pages * p.Hkv > 15360
+    _full_parity(p)
+
+
 def test_empty_and_all_padding_batches():
     """total_q = 0 launches nothing and touches nothing; a batch of padding rows
     only gives +0 outputs, lse = -inf and every split empty."""
