@@ -60,6 +60,20 @@ int page_route(const msa_prefill_desc *d) {
   return -1;
 }
 
+constexpr int kMaxSubSplits = 4;             // runs per split of the grouped route (at most)
+constexpr int64_t kSubSplitMaxItems = 512;   // work items up to which runs are added
+
+// Workspace layout of a resolved grouped problem, and the strides of its
+// runs' partials when sub_splits > 1 ([split][row][run][d], [run][split][row]).
+void set_grouped_layout(GroupArgs *a) {
+  const int H = a->sub_splits;
+  const int64_t rows_all = (int64_t)a->total_q * a->Hq;
+  const int64_t sub_rows = H > 1 ? (int64_t)a->num_splits * H * rows_all : 0;
+  a->lay = group_layout((int64_t)a->num_groups * a->Hkv, a->list_cap, a->num_splits, sub_rows, a->D);
+  a->po_sub_stride = H > 1 ? a->D : 0;
+  a->pl_sub_stride = H > 1 ? (int64_t)a->num_splits * rows_all : 0;
+}
+
 // Grouped microblock route (4-token units with per-row bit masks).  With
 // slots_per_split < num_slots it is the split-k form: every (group, KV head,
 // split) is a work item of its own and writes that split's partials.
@@ -135,7 +149,19 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   r.po_row_stride = d->po_row_stride;
   r.partial_lse = d->partial_lse;
   r.pl_split_stride = d->pl_split_stride;
-  r.lay = group_layout((int64_t)r.num_groups * r.Hkv, r.list_cap, r.num_splits);
+  // Sub-splits: a grid of few (group, KV head, split) work items leaves most
+  // CUs idle (two attention workgroups fit one).  Each split's list is then
+  // cut into H runs, each its own workgroup writing FP32 partials of its run
+  // into the workspace, and a combine merges a split's runs into the split's
+  // partials (the split-k small chunk: 128 work items, attention 42 -> 27 us
+  // with 2 runs per split).  The runs' partials stay below 24 MiB.
+  const int64_t items = (int64_t)(r.num_groups + 7) / 8 * 8 * r.Hkv * r.num_splits;
+  const int64_t rows_all = (int64_t)r.total_q * r.Hq;
+  r.sub_splits = 1;
+  while (r.sub_splits < kMaxSubSplits && items * r.sub_splits * 2 <= kSubSplitMaxItems &&
+         (int64_t)r.num_splits * r.sub_splits * 2 * rows_all * (r.D + 1) * 4 <= (24ll << 20))
+    r.sub_splits *= 2;
+  set_grouped_layout(&r);
   return MSA_OK;
 }
 
@@ -505,6 +531,10 @@ msa_status msa_sparse_prefill_noalloc(const msa_prefill_desc *d, void *stream) {
   Resolved r;
   msa_status s = resolve(d, &r);
   if (s != MSA_OK) return s;
+  if (r.grouped && r.ga.sub_splits > 1 && r.ws_bytes() > kNoAllocScratchBytes) {
+    r.ga.sub_splits = 1;  // the fixed scratch holds the problem without runs' partials
+    set_grouped_layout(&r.ga);
+  }
   const size_t need = r.ws_bytes();
   if (need > kNoAllocScratchBytes)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL,

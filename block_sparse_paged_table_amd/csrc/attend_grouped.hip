@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "grouped.h"
+#include "launch.h"
 
 namespace msa {
 namespace {
@@ -192,11 +193,19 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
   const int per_xcd = (a.num_groups + 7) >> 3;
   const int grp = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (grp >= a.num_groups) return;  // the whole workgroup, before any barrier
-  const int g = blockIdx.y, split = blockIdx.z;
+  const int g = blockIdx.y;
+  const int split = blockIdx.z / a.sub_splits, run = blockIdx.z - split * a.sub_splits;
   const int64_t li = (int64_t)g * a.num_groups + grp;
   const int *soff = split_offs + li * (a.num_splits + 1) + split;
-  const int first = soff[0];
-  const int count = soff[1] - first;
+  // run `run` of the split's list: whole stages of UPS units, evenly
+  int first, count;
+  {
+    const int f0 = soff[0], n0 = soff[1] - f0;
+    const int per = ((n0 + a.sub_splits - 1) / a.sub_splits + UPS - 1) / UPS * UPS;
+    const int lo = min(run * per, n0);
+    first = f0 + lo;
+    count = min(lo + per, n0) - lo;
+  }
   // the list from the even entry at or before `first` (16-byte pairs): unit
   // u of the split is entry u + par of that run and sits at ring index
   // (u + par) % kListRing
@@ -416,8 +425,8 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
   l = quarter_reduce<false>(l);
   lp = quarter_reduce<false>(lp);
   const int64_t row = (int64_t)tok * a.Hq + h;
-  const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + gq * 4;
-  float *lse_dst = a.partial_lse + (int64_t)split * a.pl_split_stride + row;
+  const int64_t off = (int64_t)split * a.po_split_stride + row * a.po_row_stride + run * a.po_sub_stride + gq * 4;
+  float *lse_dst = a.partial_lse + (int64_t)split * a.pl_split_stride + run * a.pl_sub_stride + row;
   if (l > 0.0f) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -443,9 +452,23 @@ static_assert(kChunkStages - 2 - GGeom<256>::NST >= GGeom<256>::NST &&
                   kChunkStages - 2 - GGeom<128>::NST >= GGeom<128>::NST,
               "a list chunk has landed and is published before its entries are first read");
 
-hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
-  if (a.num_groups == 0) return hipSuccess;
-  dim3 grid((unsigned)((a.num_groups + 7) / 8 * 8), (unsigned)a.Hkv, (unsigned)a.num_splits);
+hipError_t launch_grouped_attend(const GroupArgs &ga, hipStream_t s) {
+  if (ga.num_groups == 0) return hipSuccess;
+  const int H = ga.sub_splits;
+  // With runs (H > 1) the kernel writes FP32 partials of each run into the
+  // workspace, [split][row][run][d] and [run][split][row]; a combine then
+  // merges each split's runs into the caller's partials.
+  GroupArgs a = ga;
+  const int64_t rows_all = (int64_t)ga.total_q * ga.Hq;
+  if (H > 1) {
+    a.partial_o = ga.ws + ga.lay.sub_po;
+    a.po_dtype = MSA_F32;
+    a.po_split_stride = rows_all * H * ga.D;
+    a.po_row_stride = (int64_t)H * ga.D;
+    a.partial_lse = (float *)(ga.ws + ga.lay.sub_pl);
+    a.pl_split_stride = rows_all;
+  }
+  dim3 grid((unsigned)((a.num_groups + 7) / 8 * 8), (unsigned)a.Hkv, (unsigned)(a.num_splits * H));
   const uint2 *lists = (const uint2 *)(a.ws + a.lay.lists);
   const int *soffs = (const int *)(a.ws + a.lay.split_off);
   switch ((a.D == 256 ? 8 : 0) + a.po_dtype) {
@@ -456,7 +479,12 @@ hipError_t launch_grouped_attend(const GroupArgs &a, hipStream_t s) {
     case MSA_F16: k_grouped_attend<128, MSA_F16><<<grid, GT, 0, s>>>(a, lists, soffs); break;
     default: k_grouped_attend<128, MSA_F32><<<grid, GT, 0, s>>>(a, lists, soffs); break;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || H == 1) return e;
+  // merge: the flat list of (split, row) rows, H runs each, into the split slabs
+  return launch_combine(a.partial_o, MSA_F32, ga.D, (int64_t)H * ga.D, a.partial_lse, a.pl_split_stride * ga.num_splits,
+                        H, (int64_t)ga.num_splits * rows_all, ga.D, ga.partial_o, ga.po_dtype, ga.po_row_stride,
+                        ga.partial_lse, s, OutMap{rows_all, ga.po_split_stride, ga.pl_split_stride});
 }
 
 }  // namespace msa

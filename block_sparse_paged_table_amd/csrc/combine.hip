@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(512) combine_kernel(const void *__restrict__ p
                                                       int64_t po_row, const float *__restrict__ pl,
                                                       int64_t pl_split, int S, int64_t rows, int dv,
                                                       void *__restrict__ out, int64_t out_row,
-                                                      float *__restrict__ lse_out) {
+                                                      float *__restrict__ lse_out, const OutMap om) {
   constexpr int NV = CPT / 4;                   // 16-byte vectors per split and thread
   const int tpr = dv / CPT;                     // threads per row
   const int rows_per_block = blockDim.x / tpr;  // host guarantees tpr <= 256 (blocks of 512)
@@ -142,10 +142,16 @@ __global__ void __launch_bounds__(512) combine_kernel(const void *__restrict__ p
     for (int k = 0; k < NV; ++k) acc[k] = acc[k] * inv;
   }
   if (!live) return;
+  int64_t orow = row * out_row, lrow = row;
+  if (om.rows_per_split > 0) {  // placed into split slabs
+    const int64_t sp = row / om.rows_per_split, rs = row - sp * om.rows_per_split;
+    orow = sp * om.split + rs * out_row;
+    lrow = sp * om.lse_split + rs;
+  }
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const f32x4 a = acc[k];
-    const int64_t o = row * out_row + cc * CPT + 4 * k;
+    const int64_t o = orow + cc * CPT + 4 * k;
     if constexpr (OUT == MSA_F32) {
       *(f32x4 *)((float *)out + o) = a;
     } else if constexpr (OUT == MSA_BF16) {
@@ -157,26 +163,26 @@ __global__ void __launch_bounds__(512) combine_kernel(const void *__restrict__ p
     }
   }
   if (lse_out && cc == 0)
-    lse_out[row] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(W) * 0.69314718055994530942f;
+    lse_out[lrow] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(W) * 0.69314718055994530942f;
 }
 
 template <int CPT, int B, int IN>
 hipError_t launch_cb(const void *po, int64_t po_split, int64_t po_row, const float *pl,
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
-                     int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+                     int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s, const OutMap &om) {
   const int tpr = dv / CPT;  // <= 256 (head_dim_v <= 1024)
   const int rpb = 512 / tpr;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   if (blocks == 0) return hipSuccess;
   switch (out_dtype) {
     case MSA_F32:
-      combine_kernel<CPT, B, MSA_F32, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F32, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse, om);
       break;
     case MSA_BF16:
-      combine_kernel<CPT, B, MSA_BF16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_BF16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse, om);
       break;
     default:
-      combine_kernel<CPT, B, MSA_F16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse);
+      combine_kernel<CPT, B, MSA_F16, IN><<<(unsigned)blocks, 512, 0, s>>>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_row, lse, om);
       break;
   }
   return hipGetLastError();
@@ -185,30 +191,31 @@ hipError_t launch_cb(const void *po, int64_t po_split, int64_t po_row, const flo
 template <int IN>
 hipError_t launch_in(const void *po, int64_t po_split, int64_t po_row, const float *pl,
                      int64_t pl_split, int32_t S, int64_t rows, int32_t dv, void *out,
-                     int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+                     int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s, const OutMap &om) {
   if constexpr (IN != MSA_F32) {  // 8 columns per thread: one 16-byte load per split
     // (only where every row of every split starts 16-byte aligned; rows
     // padded to a multiple of 4 elements only take the 8-byte path below)
     if (dv % 8 == 0 && (po_row | po_split) % 8 == 0) {
-      if (S <= 4) return launch_cb<8, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-      if (S <= 8) return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-      return launch_cb<8, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+      if (S <= 4) return launch_cb<8, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+      if (S <= 8) return launch_cb<8, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+      return launch_cb<8, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
     }
   }
-  if (S <= 4) return launch_cb<4, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-  if (S <= 8) return launch_cb<4, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-  return launch_cb<4, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+  if (S <= 4) return launch_cb<4, 4, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+  if (S <= 8) return launch_cb<4, 8, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+  return launch_cb<4, 16, IN>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
                           const float *pl, int64_t pl_split, int32_t S, int64_t rows, int32_t dv,
-                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s) {
+                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s,
+                          const OutMap &om) {
   switch (po_dtype) {
-    case MSA_BF16: return launch_in<MSA_BF16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-    case MSA_F16: return launch_in<MSA_F16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
-    default: return launch_in<MSA_F32>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s);
+    case MSA_BF16: return launch_in<MSA_BF16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+    case MSA_F16: return launch_in<MSA_F16>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
+    default: return launch_in<MSA_F32>(po, po_split, po_row, pl, pl_split, S, rows, dv, out, out_dtype, out_row, lse, s, om);
   }
 }
 

@@ -15,11 +15,15 @@ constexpr int kGPlanThreadsFew = 1024;  // planner workgroup when groups are few
 // and, within a split, by unit; and the num_splits + 1 offsets of the
 // splits' runs in it (split s owns entries [split_off[s], split_off[s + 1])).
 // `stage` is the planner's own scratch (16 bytes per candidate unit).
+// With H > 1 sub-splits, `sub_po` / `sub_pl` hold the FP32 partials and LSEs
+// of the runs of each split ([split][row][run][d] and [run][split][row]),
+// which a combine then merges into the split's partials.
 struct GroupLayout {
-  size_t meta, split_off, stage, lists, total;
+  size_t meta, split_off, stage, lists, sub_po, sub_pl, total;
 };
 
-__host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, int64_t num_splits) {
+__host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, int64_t num_splits,
+                                         int64_t sub_rows = 0, int64_t sub_dv = 0) {
   GroupLayout L;
   size_t off = 0;
   L.meta = off;   off = align_up(off + 64 * 4, 256);
@@ -28,6 +32,9 @@ __host__ inline GroupLayout group_layout(int64_t num_lists, int64_t list_cap, in
   // (16 bytes of slack: the attention kernel loads entries in 16-byte pairs,
   // so the last entry of a list may bring its successor along)
   L.lists = off;  off = align_up(off + (size_t)num_lists * list_cap * 8 + 16, 256);
+  // sub_rows = splits x H x rows partial rows of sub_dv FP32 values each
+  L.sub_po = off; off = align_up(off + (size_t)sub_rows * sub_dv * 4, 256);
+  L.sub_pl = off; off = align_up(off + (size_t)sub_rows * 4, 256);
   L.total = off;
   return L;
 }
@@ -41,6 +48,7 @@ struct GroupArgs {
   int32_t sort_n;      // power of two >= kGroupTokens * num_slots and >= plan_threads
   int32_t list_cap;    // kGroupTokens * num_slots
   int32_t num_splits, slots_per_split;  // split s merges slots [s * spp, (s + 1) * spp)
+  int32_t sub_splits;  // H: runs each split's list is cut into (1: none)
   float scale_log2, v_scale;
   const void *q;
   int64_t q_stride_tok, q_stride_head;
@@ -57,6 +65,7 @@ struct GroupArgs {
   int64_t po_split_stride, po_row_stride;  // elements
   float *partial_lse;
   int64_t pl_split_stride;
+  int64_t po_sub_stride, pl_sub_stride;  // run hh of a split: + hh times these (H > 1)
   uint32_t *err_flags;
   uint8_t *ws;
   GroupLayout lay;

@@ -50,9 +50,17 @@ struct PageArgs {
 hipError_t launch_page_plan(const PageArgs &a, hipStream_t s);
 hipError_t launch_page_attend(const PageArgs &a, hipStream_t s);
 
+// Output placement of a combine: row i of the flat row list goes to
+// out[i * out_row] and lse[i] (rows_per_split 0), or, with rows_per_split
+// R > 0, to out[(i / R) * split + (i % R) * out_row] and
+// lse[(i / R) * lse_split + i % R] -- the split slabs of a partial buffer.
+struct OutMap {
+  int64_t rows_per_split, split, lse_split;
+};
 hipError_t launch_combine(const void *po, int32_t po_dtype, int64_t po_split, int64_t po_row,
                           const float *pl, int64_t pl_split, int32_t S, int64_t rows, int32_t dv,
-                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s);
+                          void *out, int32_t out_dtype, int64_t out_row, float *lse, hipStream_t s,
+                          const OutMap &om = OutMap{0, 0, 0});
 
 // Largest LDS (static + dynamic) one workgroup of each kernel family needs.
 size_t page_plan_lds_bytes();

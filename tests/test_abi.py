@@ -68,11 +68,25 @@ _MICROBLOCK = dict(page_size=16, unit_tokens=4, q_dtype=msa.MSA_F16, kv_dtype=ms
 @pytest.mark.parametrize("spp", [8, 4, 2, 1])
 def test_microblock_route_takes_any_split_count(spp):
     """Microblock selections may be cut into num_slots / slots_per_split splits
-    (the split-k form of the grouped route); the workspace grows with them."""
-    n = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=spp, **_MICROBLOCK))
-    assert n > 0
+    (the split-k form of the grouped route); on a grid large enough that no
+    split is cut into runs (8192 tokens: 1024 groups), the workspace grows
+    with the splits (their offsets)."""
+    assert msa.msa_prefill_workspace_bytes(_desc(slots_per_split=spp, **_MICROBLOCK)) > 0
+    big = dict(_MICROBLOCK, total_q=8192)
+    n = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=spp, **big))
     if spp < 8:
-        assert n > msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **_MICROBLOCK))
+        assert n > msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **big))
+
+
+def test_microblock_small_grid_runs_workspace():
+    """A small grid cuts each split's list into runs whose FP32 partials live
+    in the workspace: 128 groups x 1 split gets 4 runs, (4 x 1024 x 6 rows) x
+    (128 + 1) x 4 bytes more than the same problem on a grid too large for
+    runs would need per row."""
+    small = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **_MICROBLOCK))
+    sub = 4 * 1024 * 6 * 128 * 4 + 4 * 1024 * 6 * 4
+    big = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **dict(_MICROBLOCK, total_q=8192)))
+    assert small >= sub and small < big + sub
 
 
 def test_microblock_route_rejects_uneven_splits():
