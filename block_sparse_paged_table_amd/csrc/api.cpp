@@ -60,8 +60,9 @@ int page_route(const msa_prefill_desc *d) {
   return -1;
 }
 
-constexpr int kMaxSubSplits = 4;             // runs per split of the grouped route (at most)
-constexpr int64_t kSubSplitMaxItems = 512;   // work items up to which runs are added
+constexpr int kMaxSubSplits = 16;            // runs per split of the grouped route (at most)
+constexpr int64_t kSubSplitMaxItems = 512;   // workgroups the runs may fill (two per CU)
+constexpr int kMinRunSlots = 8;              // slots of a split per run (at least)
 
 // Workspace layout of a resolved grouped problem, and the strides of its
 // runs' partials when sub_splits > 1 ([split][row][run][d], [run][split][row]).
@@ -149,18 +150,24 @@ msa_status resolve_grouped(const msa_prefill_desc *d, GroupArgs *a) {
   r.po_row_stride = d->po_row_stride;
   r.partial_lse = d->partial_lse;
   r.pl_split_stride = d->pl_split_stride;
-  // Sub-splits: a grid of few (group, KV head, split) work items leaves most
-  // CUs idle (two attention workgroups fit one).  Each split's list is then
-  // cut into H runs, each its own workgroup writing FP32 partials of its run
-  // into the workspace, and a combine merges a split's runs into the split's
-  // partials (the split-k small chunk: 128 work items, attention 42 -> 27 us
-  // with 2 runs per split).  The runs' partials stay below 24 MiB.
+  // Runs: a grid of few (group, KV head, split) work items leaves most CUs
+  // idle (two attention workgroups fit one).  Each split's list is then cut
+  // into H runs, each its own workgroup writing FP32 partials of its run into
+  // the workspace, and a combine merges a split's runs into the split's
+  // partials.  H doubles while the grid stays within 512 workgroups and a run
+  // keeps at least 8 slots' worth of the split; the runs' partials stay below
+  // 24 MiB.  (Split-k small chunk, 16 splits of 32 slots: attention plus
+  // merge 42 -> 32 us with 2 runs, 28 us with 4, 36 us with 8; with 32
+  // splits of 16 slots 2 runs cost 3 us more than they gained.)
   const int64_t items = (int64_t)(r.num_groups + 7) / 8 * 8 * r.Hkv * r.num_splits;
   const int64_t rows_all = (int64_t)r.total_q * r.Hq;
   r.sub_splits = 1;
-  while (r.sub_splits < kMaxSubSplits && items * r.sub_splits * 2 <= kSubSplitMaxItems &&
-         (int64_t)r.num_splits * r.sub_splits * 2 * rows_all * (r.D + 1) * 4 <= (24ll << 20))
-    r.sub_splits *= 2;
+  if (items * 4 <= kSubSplitMaxItems) {
+    while (r.sub_splits < kMaxSubSplits && items * r.sub_splits * 2 <= kSubSplitMaxItems &&
+           r.slots_per_split / (r.sub_splits * 2) >= kMinRunSlots &&
+           (int64_t)r.num_splits * r.sub_splits * 2 * rows_all * (r.D + 1) * 4 <= (24ll << 20))
+      r.sub_splits *= 2;
+  }
   set_grouped_layout(&r);
   return MSA_OK;
 }

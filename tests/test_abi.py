@@ -80,13 +80,17 @@ def test_microblock_route_takes_any_split_count(spp):
 
 def test_microblock_small_grid_runs_workspace():
     """A small grid cuts each split's list into runs whose FP32 partials live
-    in the workspace: 128 groups x 1 split gets 4 runs, (4 x 1024 x 6 rows) x
-    (128 + 1) x 4 bytes more than the same problem on a grid too large for
-    runs would need per row."""
-    small = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **_MICROBLOCK))
+    in the workspace: 128 groups x 1 split of 64 slots gets 4 runs (4 x 128
+    work items fill the 512 the runs may use, 16 slots per run), i.e.
+    4 x (1024 x 6 rows) x (128 + 1) x 4 bytes; with 8 slots a run would hold
+    fewer than 8 slots, so there are none."""
+    wide = dict(_MICROBLOCK, num_slots=64, sel_stride_tok=64, sel_stride_head=64)
+    runs = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=64, **wide))
     sub = 4 * 1024 * 6 * 128 * 4 + 4 * 1024 * 6 * 4
-    big = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **dict(_MICROBLOCK, total_q=8192)))
-    assert small >= sub and small < big + sub
+    lists = 128 * (8 * 64) * (16 + 8)  # planner stage + lists
+    assert sub + lists <= runs <= sub + lists + (1 << 20)
+    few = msa.msa_prefill_workspace_bytes(_desc(slots_per_split=8, **_MICROBLOCK))
+    assert few < sub
 
 
 def test_microblock_route_rejects_uneven_splits():

@@ -104,14 +104,15 @@ def test_full_size_every_row(cfg):
         assert v["o_err"] ** 0.5 <= v["o_floor"] ** 0.5 + tol["rel_l2"] * v["o_ref"] ** 0.5, v
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, "page4_small_chunk"])
 def test_full_size_graph_replay_matches_eager(cfg):
     """The step as the benchmark times it: plan, attention and combine
     captured in one HIP graph and replayed.  Every replay rewrites the live
     partials, the partial LSEs, the outputs and their LSEs bit for bit as the
     eager launches wrote them (whose oracle parity the test above checks);
-    between replays the buffers are overwritten by eager work."""
-    p = synth.make_config(cfg)
+    between replays the buffers are overwritten by eager work.  The split-k
+    small chunk runs its splits in runs merged by an extra combine."""
+    p = synth.make_page4_small_chunk() if cfg == "page4_small_chunk" else synth.make_config(cfg)
     dp = DeviceProblem(p, partial_layout="row")
     dp.plan()
     dp.attend()
