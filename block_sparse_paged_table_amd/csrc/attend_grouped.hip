@@ -44,6 +44,12 @@
 // A tile none of whose rows selected any unit of a stage skips it.  Each
 // split is an independent softmax: partial_o = O / l * v_scale and lse =
 // m + ln l (or -inf with zeros for a row that sees nothing in the split).
+//
+// Runs: when the (group, KV head, split) grid is small, the host cuts each
+// split's list into sub_splits runs of whole stages; one workgroup per run
+// writes the run's FP32 partials and LSE into the workspace, and a combine
+// (LSE merge over the runs) writes the split's partials.  A small grid
+// otherwise leaves most CUs idle while each workgroup walks a long list.
 #include <type_traits>
 
 #include "grouped.h"
