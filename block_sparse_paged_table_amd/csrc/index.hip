@@ -43,7 +43,6 @@ template <int D> struct IGeom {
   // waves per workgroup: each thread copies at least one 16-byte chunk of a page
   static constexpr int WAVES = ITQ_WAVES * 64 > IPAGE * D / 16 ? IPAGE * D / 16 / 64 : ITQ_WAVES;
   static constexpr int IT = 64 * WAVES;    // threads per workgroup
-  static constexpr int ITQ = 16 * WAVES;   // query tokens per workgroup
   static constexpr int RB = D;              // bytes per K row (E4M3)
   static constexpr int CPR = RB / 16;       // 16-byte chunks per row
   static constexpr int LANE_CH = CPR / 4;   // chunks of a row one lane holds
@@ -76,10 +75,17 @@ template <int D> __device__ __forceinline__ uint32_t kpage_src_off(const IndexAr
   return (uint32_t)(key * a.kv_stride_tok) + (uint32_t)((pc ^ ik_swz<D>(key)) << 4);
 }
 
-template <int D, int IPC>
-__global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArgs a) {
+// RPW: 16-row tiles per wave.  With 2 every K fragment read from LDS feeds
+// two MFMAs (half the LDS reads per row) and a page load serves twice the
+// rows: 0.091 -> 0.083 ms on the 16K-token request; on short chunks the
+// 128-token tiles straddle requests and idle rows, so those keep 1 (there 2
+// took 0.103 -> 0.174 ms, and 0.024 -> 0.056 ms on two chunks of 64 and 40).
+template <int D, int RPW> constexpr int index_tile_tokens() { return 16 * IGeom<D>::WAVES * RPW; }
+
+template <int D, int IPC, int RPW>
+__global__ void __launch_bounds__(IGeom<D>::IT, RPW == 2 ? 3 : 4) k_index_scores(const IndexArgs a) {
   using Gm = IGeom<D>;
-  constexpr int IT = Gm::IT, ITQ = Gm::ITQ;
+  constexpr int IT = Gm::IT, ITQ = index_tile_tokens<D, RPW>();
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][Gm::PAGE_BYTES];
   __shared__ float sScore[ITQ][IPC + 1];
   __shared__ int sRowB[ITQ], sRowLast[ITQ];
@@ -148,15 +154,18 @@ __global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArg
   }
   __syncthreads();
 
-  // ---- this lane's Q row (row wave*16 + n of the tile), its quarter of d
-  const int rho = wave * 16 + n;
-  const int my_b = sRowB[rho], my_last = sRowLast[rho];
-  u32x4 qr[Gm::LANE_CH];
-  {
-    const int tok = my_b >= 0 ? tok0 + rho : 0;  // rows that see nothing read token 0
+  // ---- this lane's Q rows (row wave*16*RPW + 16p + n of the tile), its quarter of d
+  int rho[RPW], my_b[RPW], my_last[RPW];
+  u32x4 qr[RPW][Gm::LANE_CH];
+#pragma unroll
+  for (int p = 0; p < RPW; ++p) {
+    rho[p] = wave * 16 * RPW + 16 * p + n;
+    my_b[p] = sRowB[rho[p]];
+    my_last[p] = sRowLast[rho[p]];
+    const int tok = my_b[p] >= 0 ? tok0 + rho[p] : 0;  // rows that see nothing read token 0
     const uint8_t *qp = a.q + (int64_t)tok * a.q_stride_tok + (int64_t)h * a.q_stride_head + grp * (Gm::RB / 4);
 #pragma unroll
-    for (int c = 0; c < Gm::LANE_CH; ++c) qr[c] = *(const u32x4 *)(qp + c * 16);
+    for (int c = 0; c < Gm::LANE_CH; ++c) qr[p][c] = *(const u32x4 *)(qp + c * 16);
   }
 
   uint32_t dma_off[Gm::KCH];
@@ -202,18 +211,21 @@ __global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArg
         if (a.err_flags && tid == 0) atomicOr(a.err_flags, MSA_ERRF_PHYS_RANGE);
         continue;  // scores stay -inf
       }
-      // ---- S^T = K Q^T: lane holds keys 16t + 4grp + i of row n
-      f32x4 acc[IPAGE / 16];
+      // ---- S^T = K Q^T: lane holds keys 16t + 4grp + i of row n (of each tile)
+      f32x4 acc[RPW][IPAGE / 16];
 #pragma unroll
-      for (int t = 0; t < IPAGE / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < RPW; ++p)
+#pragma unroll
+        for (int t = 0; t < IPAGE / 16; ++t) acc[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (Gm::LANE_CH == 2) {
         // d = 128: the lane's 32 bytes of a K row against its 32 bytes of the
-        // Q row, one K = 128 MFMA per key tile
+        // Q row, one K = 128 MFMA per key tile and row tile
 #pragma unroll
         for (int t = 0; t < IPAGE / 16; ++t) {
           const u32x4 k0 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * 2));
           const u32x4 k1 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * 2 + 1));
-          acc[t] = mfma_fp8_k128(k0, k1, qr[0], qr[1], acc[t]);
+#pragma unroll
+          for (int p = 0; p < RPW; ++p) acc[p][t] = mfma_fp8_k128(k0, k1, qr[p][0], qr[p][1], acc[p][t]);
         }
       } else {
 #pragma unroll
@@ -221,28 +233,35 @@ __global__ void __launch_bounds__(IGeom<D>::IT, 4) k_index_scores(const IndexArg
 #pragma unroll
           for (int t = 0; t < IPAGE / 16; ++t) {
             const u32x4 k4 = *(const u32x4 *)(sk + ik_off<D>(t * 16 + n, grp * Gm::LANE_CH + c));
-            acc[t] = mfma_fp8(u32x2{k4[0], k4[1]}, u32x2{qr[c][0], qr[c][1]}, acc[t]);
-            acc[t] = mfma_fp8(u32x2{k4[2], k4[3]}, u32x2{qr[c][2], qr[c][3]}, acc[t]);
+#pragma unroll
+            for (int p = 0; p < RPW; ++p) {
+              acc[p][t] = mfma_fp8(u32x2{k4[0], k4[1]}, u32x2{qr[p][c][0], qr[p][c][1]}, acc[p][t]);
+              acc[p][t] = mfma_fp8(u32x2{k4[2], k4[3]}, u32x2{qr[p][c][2], qr[p][c][3]}, acc[p][t]);
+            }
           }
       }
-      // ---- max over the keys this row sees
+      // ---- max over the keys each row sees
       const int jabs = j0 + jj;
-      const int vis_to = (my_b == cb) ? my_last - jabs * IPAGE : -1;  // last visible in-page key
-      float m = -INFINITY;
-      if (__all(vis_to >= IPAGE - 1)) {
-        // every row of the wave sees the whole page (all pages but a row's
-        // own): a plain max, no per-key test
 #pragma unroll
-        for (int t = 0; t < IPAGE / 16; ++t) m = fmaxf(m, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
-      } else {
+      for (int p = 0; p < RPW; ++p) {
+        const int vis_to = (my_b[p] == cb) ? my_last[p] - jabs * IPAGE : -1;  // last visible in-page key
+        float m = -INFINITY;
+        if (__all(vis_to >= IPAGE - 1)) {
+          // every row of the tile sees the whole page (all pages but a row's
+          // own): a plain max, no per-key test
 #pragma unroll
-        for (int t = 0; t < IPAGE / 16; ++t)
+          for (int t = 0; t < IPAGE / 16; ++t)
+            m = fmaxf(m, fmaxf(fmaxf(acc[p][t][0], acc[p][t][1]), fmaxf(acc[p][t][2], acc[p][t][3])));
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[t][i]);
+          for (int t = 0; t < IPAGE / 16; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t * 16 + 4 * grp + i <= vis_to) m = fmaxf(m, acc[p][t][i]);
+        }
+        m = quarter_reduce<true>(m);
+        if (grp == 0 && my_b[p] == cb) sScore[rho[p]][jj] = m == -INFINITY ? m : m * a.scale;
       }
-      m = quarter_reduce<true>(m);
-      if (grp == 0 && my_b == cb) sScore[rho][jj] = m == -INFINITY ? m : m * a.scale;
     }
     __syncthreads();  // the last page's buffer is reused by the next request
   }
@@ -417,39 +436,54 @@ __global__ void k_index_zero(uint32_t *err) { *err = 0u; }
 
 }  // namespace
 
-// Static LDS of k_index_scores<D, IPC> (its __shared__ arrays).
-template <int D, int IPC> constexpr size_t index_scores_lds() {
+// Static LDS of k_index_scores<D, IPC, RPW> (its __shared__ arrays).
+template <int D, int IPC, int RPW> constexpr size_t index_scores_lds() {
   using Gm = IGeom<D>;
-  return 2 * (size_t)Gm::PAGE_BYTES + (size_t)Gm::ITQ * (IPC + 1) * 4 + 4 * (size_t)Gm::ITQ * 4 + 4 * 4;
+  constexpr size_t itq = index_tile_tokens<D, RPW>();
+  return 2 * (size_t)Gm::PAGE_BYTES + itq * (IPC + 1) * 4 + 4 * itq * 4 + 4 * 4;
 }
 
 size_t index_lds_bytes() {
-  // the largest page chunk holds the most scores
+  // the largest page chunk and tile hold the most scores
   constexpr int pc = kIndexPageChunks[0];
-  return index_scores_lds<128, pc>() > index_scores_lds<64, pc>() ? index_scores_lds<128, pc>()
-                                                                   : index_scores_lds<64, pc>();
+  return index_scores_lds<128, pc, 2>() > index_scores_lds<64, pc, 1>() ? index_scores_lds<128, pc, 2>()
+                                                                         : index_scores_lds<64, pc, 1>();
 }
 
 namespace {
-template <int D, int IPC>
+template <int D, int IPC, int RPW>
 hipError_t launch_scores(const IndexArgs &a, int64_t tiles, hipStream_t s) {
   dim3 grid((unsigned)tiles, (unsigned)a.H, (unsigned)((a.max_pages + IPC - 1) / IPC));
-  k_index_scores<D, IPC><<<grid, IGeom<D>::IT, 0, s>>>(a);
+  k_index_scores<D, IPC, RPW><<<grid, IGeom<D>::IT, 0, s>>>(a);
   return hipGetLastError();
 }
-template <int D>
-hipError_t launch_scores_d(const IndexArgs &a, hipStream_t s) {
-  const int64_t tiles = (a.total_q + IGeom<D>::ITQ - 1) / IGeom<D>::ITQ;
+template <int D, int RPW>
+hipError_t launch_scores_r(const IndexArgs &a, hipStream_t s) {
+  constexpr int itq = index_tile_tokens<D, RPW>();
+  const int64_t tiles = (a.total_q + itq - 1) / itq;
   int pc = kIndexPageChunks[0];
   for (int c : kIndexPageChunks) {
     pc = c;
     if (tiles * a.H * ((a.max_pages + c - 1) / c) >= kIndexMinWorkgroups) break;
   }
   switch (pc) {
-    case 16: return launch_scores<D, 16>(a, tiles, s);
-    case 8: return launch_scores<D, 8>(a, tiles, s);
-    default: return launch_scores<D, 4>(a, tiles, s);
+    case 16: return launch_scores<D, 16, RPW>(a, tiles, s);
+    case 8: return launch_scores<D, 8, RPW>(a, tiles, s);
+    default: return launch_scores<D, 4, RPW>(a, tiles, s);
   }
+}
+template <int D>
+hipError_t launch_scores_d(const IndexArgs &a, hipStream_t s) {
+  // two row tiles per wave for long chunks (1024 tokens or more per
+  // request on average) on a grid that still fills the GPU
+  if constexpr (D == 128) {
+    constexpr int itq2 = index_tile_tokens<D, 2>();
+    const int64_t tiles2 = (a.total_q + itq2 - 1) / itq2;
+    if ((int64_t)a.total_q >= 1024ll * a.num_seqs &&
+        tiles2 * a.H * ((a.max_pages + kIndexPageChunks[0] - 1) / kIndexPageChunks[0]) >= kIndexMinWorkgroups)
+      return launch_scores_r<D, 2>(a, s);
+  }
+  return launch_scores_r<D, 1>(a, s);
 }
 }  // namespace
 
