@@ -400,9 +400,10 @@ msa_status resolve_index(const msa_index_desc *d, bool need_topk, IndexArgs *r) 
   if (d->page_table_stride < d->max_pages) return fail(MSA_ERR_INVALID_ARG, "page_table_stride < max_pages");
   if (!(d->q_scale > 0.0f) || !std::isfinite(d->q_scale) || !(d->k_scale > 0.0f) || !std::isfinite(d->k_scale))
     return fail(MSA_ERR_INVALID_ARG, "q_scale and k_scale must be finite and > 0");
-  if (!d->scores || d->score_stride < d->max_pages || !aligned(d->scores, 4))
+  const bool rows = d->total_q > 0;  // an empty batch reads and writes nothing: NULL buffers pass
+  if ((rows && !d->scores) || d->score_stride < d->max_pages || !aligned(d->scores, 4))
     return fail(MSA_ERR_INVALID_ARG, "scores must be a 4-byte aligned buffer with score_stride >= max_pages");
-  {  // inputs (checked for every call: one descriptor serves all three)
+  if (rows) {  // inputs (checked for every call: one descriptor serves all three)
     const void *need[] = {d->q, d->q_seq, d->q_pos, d->seq_lens, d->k_cache, d->page_table};
     for (const void *p : need)
       if (!p) return fail(MSA_ERR_INVALID_ARG, "NULL input pointer");
@@ -415,7 +416,7 @@ msa_status resolve_index(const msa_index_desc *d, bool need_topk, IndexArgs *r) 
   }
   if (need_topk) {
     if (d->top_k < 1 || d->top_k > 255) return fail(MSA_ERR_INVALID_ARG, "top_k must be in [1, 255]");
-    if (!d->sel_idx || !d->sel_mask) return fail(MSA_ERR_INVALID_ARG, "selection outputs are NULL");
+    if (rows && (!d->sel_idx || !d->sel_mask)) return fail(MSA_ERR_INVALID_ARG, "selection outputs are NULL");
     if (!aligned(d->sel_idx, 4) || d->sel_stride_tok < 0 || d->sel_stride_head < 0 ||
         (d->num_heads > 1 && d->sel_stride_head < d->top_k) ||
         d->sel_stride_tok < (int64_t)d->top_k + (int64_t)(d->num_heads - 1) * d->sel_stride_head)

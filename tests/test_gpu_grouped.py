@@ -135,6 +135,22 @@ def test_grouped_all_invalid_group_bitwise_zero():
     assert torch.all(torch.isneginf(dp.lse[: 8 * p.Hq]))
 
 
+@pytest.mark.parametrize("spp", [None, 12])
+def test_grouped_empty_batch(spp):
+    """total_q = 0 on the microblock route (one split, and its split-k form)
+    launches nothing past clearing the error word; its buffers are NULL."""
+    p = _mb(37, num_slots=48)
+    if spp is not None:
+        p = dataclasses.replace(p, slots_per_split=spp)
+    empty = dataclasses.replace(p, q=p.q[:0], q_seq=p.q_seq[:0], q_pos=p.q_pos[:0],
+                                sel_idx=p.sel_idx[:0], sel_mask=p.sel_mask[:0])
+    dp = DeviceProblem(empty)
+    dp.err.fill_(7)
+    dp.run()
+    torch.cuda.synchronize()
+    assert dp.err_flags() == 0
+
+
 def test_grouped_full_size_config_sampled():
     p = synth.make_config(3)
     dp = DeviceProblem(p)

@@ -188,6 +188,19 @@ def test_index_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_index_empty_batch():
+    """total_q = 0: the indexer accepts NULL query, score and selection buffers
+    and only clears the error word."""
+    ip = _small(71)
+    empty = dataclasses.replace(ip, q=ip.q[:0], q_seq=ip.q_seq[:0], q_pos=ip.q_pos[:0])
+    dev = DeviceIndexProblem(empty)
+    assert dev.scores.numel() == 0 and dev.sel_idx.numel() == 0
+    dev.err.fill_(7)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.err_flags() == 0
+
+
 def test_index_error_rows():
     ip = _small(45)
     q_seq = ip.q_seq.numpy().copy()
