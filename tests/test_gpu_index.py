@@ -143,6 +143,20 @@ def test_index_topk_wide_rows(ctx, chunk, top_k):
     assert err == 0 and exact > 0
 
 
+def test_index_max_pages():
+    """A request of exactly the 2048 pages a top-k row can hold (64 lanes x 32
+    pages) with the largest top_k, on sampled tokens: the last register slot of
+    the last lane holds a live page."""
+    ctx, chunk = 2048 * 128 - 130, 130
+    ip = _small(48, ctx_lens=[ctx], chunk_lens=[chunk], top_k=255, H=1, pad_rows=2)
+    assert ip.max_pages == 2048
+    dev = DeviceIndexProblem(ip)
+    dev.run()
+    torch.cuda.synchronize()
+    err, exact = _check(ip, dev, tokens=[0, 77, chunk - 1, chunk])
+    assert err == 0 and exact > 0
+
+
 def test_index_deterministic():
     ip = _small(44)
     dev = DeviceIndexProblem(ip)
