@@ -363,6 +363,10 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
     };
     const f32x4 acc_a = qk_tile(st);
     const f32x4 acc_b = qk_tile(st + Gm::TILE_B);
+    // ---- masks and softmax at raised wave priority (back to 0 before PV):
+    // this VALU stretch of one wave gets the issue slots first while the
+    // other wave of the SIMD keeps the matrix cores busy
+    __builtin_amdgcn_s_setprio(1);
     // ---- exact masks: key i of this lane group's unit in each tile
     const uint32_t bits_a = active ? (mask_a >> mshift) & 0xfu : 0u;
     const uint32_t bits_b = active ? (mask_b >> mshift) & 0xfu : 0u;
@@ -402,6 +406,7 @@ __global__ void __launch_bounds__(GT, GGeom<D>::WGS)
       pf[j] = pair;
       lp = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), f16x2{(_Float16)1.0f, (_Float16)1.0f}, lp, false);
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- O^T += V^T P^T over the 32 keys (16x16x32: element j of the V^T
     // operand and of the P^T operand name the same key): lane n receives V
     // rows 4gq .. 4gq+3 of each tile at dim 16 mt + n
